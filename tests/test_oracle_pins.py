@@ -1,0 +1,492 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks an oracle function against something other than itself: a
+value printed on the pages (fixtures under tests/golden/), a closed form, an
+invariant, a special case that reduces to a textbook quantity, or brute force
+on tiny inputs.  None of these needs a GPU.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _fp16_values(a):
+    return np.asarray(a, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+# ---------------------------------------------------------------- transform
+def test_equivalent_transform_exact_in_fp64():
+    """W' x' = W x in full precision ("AWQ Math", "The equivalent transform")."""
+    g = _rng(1)
+    for N, K in [(7, 256), (64, 512), (3, 128)]:
+        W = g.standard_normal((N, K))
+        x = g.standard_normal(K) * np.where(g.random(K) < 0.05, 20.0, 1.0)
+        s = np.exp(g.uniform(-3, 3, K))
+        y = W @ x
+        y2 = O.scale_columns(W, s) @ O.unscale_activation(x, s)
+        assert np.max(np.abs(y2 - y)) / np.max(np.abs(y)) <= 1e-12
+
+
+def test_transform_direction_on_grid_weights():
+    """Weights that sit on the 16-level grid after W diag(s) quantize without
+    loss, so the search loss is zero: pins that s multiplies W's columns before
+    quantizing and divides them after.  With s = 2^e the products are exact."""
+    g = _rng(2)
+    N, K = 4, 256
+    e = g.integers(-3, 4, K)
+    s = np.ldexp(np.float32(1), e).astype(np.float32)
+    D = np.float32(2.0 ** -6)
+    q = g.integers(0, 16, (N, K))
+    q[:, ::128] = 0
+    q[:, 1::128] = 15
+    z = 7
+    Wp = (D * (q - z)).astype(np.float32)            # on the grid, 0 at code 7
+    W = (Wp / s[None, :]).astype(np.float32)
+    r = O.quantize_layer(W, s)
+    assert np.array_equal(r["q"], q.astype(np.uint8))
+    assert np.all(r["z"] == z)
+    X = g.standard_normal((5, K)).astype(np.float32)
+    L = O.search_losses(W, X, s[None, :])
+    assert L[0] == 0.0
+    # the opposite direction (dividing the columns first) is not lossless
+    L_wrong = O.search_losses(W, X, (1.0 / s)[None, :].astype(np.float32))
+    assert L_wrong[0] > 0.0
+
+
+# ---------------------------------------------------------------- quantizer
+def _bound_ok(wp, D, q, z):
+    err = np.abs(wp.astype(np.float64) - D.astype(np.float64)[..., None]
+                 * (q.astype(np.float64) - z.astype(np.float64)[..., None]))
+    return np.all(err <= D.astype(np.float64)[..., None] * (0.5 + 2.0 ** -18)), err
+
+
+@pytest.mark.parametrize("kind", ["normal", "uniform", "outlier", "positive", "negative",
+                                  "constant", "zeros", "tiny", "ties"])
+def test_rounding_error_at_most_half_step(kind):
+    """Per-weight error <= step/2 ("AWQ Math", "Weight-only quantization and
+    where it breaks"); the fp32 division adds at most 15 * 2^-24 steps."""
+    g = _rng(3)
+    G = 2000
+    if kind == "normal":
+        w = g.standard_normal((G, 128)) * 0.02
+    elif kind == "uniform":
+        w = g.uniform(-1, 1, (G, 128))
+    elif kind == "outlier":
+        w = g.standard_normal((G, 128)) * 0.02
+        w[:, 5] *= 40
+    elif kind == "positive":
+        w = np.abs(g.standard_normal((G, 128))) + 0.5
+    elif kind == "negative":
+        w = -np.abs(g.standard_normal((G, 128))) - 0.5
+    elif kind == "constant":
+        w = np.repeat(g.standard_normal((G, 1)), 128, axis=1)
+    elif kind == "zeros":
+        w = np.zeros((G, 128))
+    elif kind == "tiny":
+        w = g.standard_normal((G, 128)) * 1e-7
+    else:  # values on half-steps of a power-of-two grid
+        w = (g.integers(-30, 31, (G, 128)) + 0.5) * 2.0 ** -8
+        w[:, 0] = -7.5 * 2.0 ** -6
+        w[:, 1] = 7.5 * 2.0 ** -6
+    wp = _fp16_values(w)
+    D, step, z, d = O.group_quant_params(wp)
+    q = O.quantize_codes(wp, D, z)
+    ok, err = _bound_ok(wp, D, q, z)
+    assert ok, float(np.max(err / D[..., None]))
+    assert np.all(D >= d) and np.all(D >= 2.0 ** -24)
+
+
+def test_round_to_nearest_step_would_break_the_bound():
+    """The reading that rounds the stored step up is needed: rounding it to
+    nearest instead lets the top of some ranges need code 16, which exceeds the
+    half-step bound.  Pins that the oracle really rounds up."""
+    g = _rng(4)
+    wp = _fp16_values(g.standard_normal((20000, 128)) * 0.02)
+    lo = np.minimum(wp.min(-1), 0)
+    hi = np.maximum(wp.max(-1), 0)
+    d = (hi - lo) / np.float32(15)
+    D_rne = d.astype(np.float16).astype(np.float32)
+    z = np.clip(np.rint(-lo / D_rne), 0, 15)
+    q = np.clip(np.rint(wp / D_rne[:, None]) + z[:, None], 0, 15)
+    err = np.abs(wp - D_rne[:, None] * (q - z[:, None])) / D_rne[:, None]
+    assert err.max() > 0.5 + 1e-3
+    D, _, zz, _ = O.group_quant_params(wp)
+    ok, _ = _bound_ok(wp, D, O.quantize_codes(wp, D, zz), zz)
+    assert ok
+
+
+def test_fp16_round_up_brute_force():
+    """Smallest float16 >= d, checked against the sorted list of every finite
+    positive float16."""
+    allh = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)
+    g = _rng(5)
+    d = np.concatenate([
+        g.uniform(0, 1, 20000).astype(np.float32) * np.float32(2.0) ** g.integers(-26, 15, 20000),
+        allh[g.integers(0, allh.size, 2000)],          # exact fp16 values map to themselves
+        np.float32([2.0 ** -25, 2.0 ** -24, 65504.0, 1.0, 3.0e-8]),
+    ]).astype(np.float32)
+    got = O.fp16_round_up(d).astype(np.float32)
+    idx = np.searchsorted(allh, d, side="left")
+    assert np.array_equal(got, allh[idx])
+
+
+def test_exactly_sixteen_levels_and_full_code_range():
+    """N = 4 bits give 2^N = 16 levels; a dense sweep over a group's range hits
+    every code; the group minimum maps to code 0 when the range is negative."""
+    g = _rng(6)
+    for _ in range(50):
+        lo, hi = -g.uniform(0.1, 3), g.uniform(0.1, 3)
+        wp = _fp16_values(np.linspace(lo, hi, 128))[None, :]
+        D, _, z, _ = O.group_quant_params(wp)
+        q = O.quantize_codes(wp, D, z)
+        assert q.min() == 0 and q.max() <= 15 and q[0, np.argmin(wp)] == 0
+        levels = np.unique(O.dequantize(np.arange(16, dtype=np.uint8)[None, :], D, z))
+        assert levels.size == 16
+        assert set(np.unique(q).tolist()) >= set(range(1, 15))
+
+
+def test_codes_are_nearest_level_brute_force():
+    """Every code is the level nearest to fp32(w'/D) - by exhaustive search over
+    the 16 codes in exact rational arithmetic, ties to the even quotient."""
+    g = _rng(7)
+    wp = _fp16_values(g.standard_normal((40, 128)) * g.uniform(0.001, 2, (40, 1)))
+    D, _, z, _ = O.group_quant_params(wp)
+    q = O.quantize_codes(wp, D, z)
+    for gi in range(wp.shape[0]):
+        zz = int(z[gi])
+        for k in range(0, 128, 3):
+            quo = Fraction(float(np.float32(wp[gi, k]) / np.float32(D[gi])))
+            best = None
+            for c in range(16):
+                dist = abs(quo - (c - zz))
+                key = (dist, (c - zz) % 2)   # ties: even integer (c - z)
+                if best is None or key < best[0]:
+                    best = (key, c)
+            assert q[gi, k] == best[1]
+
+
+def test_zero_is_exact_and_zero_point_in_range():
+    g = _rng(8)
+    wp = _fp16_values(g.standard_normal((500, 128)))
+    wp[:, 17] = 0.0
+    D, _, z, _ = O.group_quant_params(wp)
+    q = O.quantize_codes(wp, D, z)
+    assert np.all(z <= 15) and np.all(z >= 0)
+    assert np.all(q[:, 17] == z)
+
+
+def test_mean_round_fraction_is_quarter():
+    """E[RoundErr] ~ 0.25 with RoundErr in [0, 0.5] ("AWQ Math", "Why scaling
+    shrinks the error that matters"; fixture worked_example.json)."""
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    g = _rng(9)
+    wp = g.uniform(-1, 1, (8000, 128)).astype(np.float32)
+    D, _, z, _ = O.group_quant_params(wp)
+    q = O.quantize_codes(wp, D, z)
+    frac = np.abs(wp / D[:, None] - (q.astype(np.float32) - z[:, None]))
+    assert frac.max() <= ex["round_fraction_range"][1] + 1e-5
+    # the two extremes of each group set the grid (for symmetric data they sit
+    # near half-steps); the statistic is about the weights inside the range
+    inner = np.ones_like(frac, dtype=bool)
+    inner[np.arange(wp.shape[0]), np.argmin(wp, 1)] = False
+    inner[np.arange(wp.shape[0]), np.argmax(wp, 1)] = False
+    assert abs(frac[inner].mean() - ex["mean_round_fraction"]) < 0.002
+
+
+def test_worked_example():
+    """The pages' worked example: 4 bits, group max 1.0 -> step 1/8; a salient
+    weight 0.1 with |x| = 10 has expected output error 0.3125; scaling the
+    channel by 2 (group max unchanged) gives 0.15625.  Expectations are over
+    the rounding fraction, so they are checked by Monte Carlo with the pages'
+    symmetric quantizer and with the oracle's code/dequantize steps at the same
+    step (zero point 8)."""
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    step = ex["group_max_abs"] / 2 ** (ex["bits"] - 1)
+    assert step == ex["step"]
+    assert math.isclose(step * ex["mean_round_fraction"] * ex["mean_abs_activation"], ex["err_before"])
+    g = _rng(10)
+    w = g.uniform(-0.25, 0.25, 2_000_000)          # weights spread over several steps
+    x = ex["mean_abs_activation"]
+    s = ex["scale"]
+    e1 = np.mean(np.abs(O.symmetric_rtn(w, step) - w)) * x
+    e2 = np.mean(np.abs(O.symmetric_rtn(w * s, step) - w * s)) * x / s
+    assert abs(e1 - ex["err_before"]) / ex["err_before"] < 0.01
+    assert abs(e2 - ex["err_after"]) / ex["err_after"] < 0.01
+    # same expectation through the oracle's asymmetric code path at step 1/8
+    D = np.full(1, step, dtype=np.float32)
+    z = np.full(1, 8, dtype=np.float32)
+    for sc, want in [(1.0, ex["err_before"]), (s, ex["err_after"])]:
+        wp = (w * sc).astype(np.float32)[None, :]
+        q = O.quantize_codes(wp, D, z)
+        e = np.mean(np.abs(O.dequantize(q, D, z)[0] - wp[0])) * x / sc
+        assert abs(e - want) / want < 0.01
+
+
+def test_idempotent_on_dequantized_weights():
+    """Re-quantizing D (q - z) returns the same step, zero point and codes when
+    both end codes occur in the group."""
+    g = _rng(11)
+    wp = _fp16_values(g.standard_normal((3000, 128)) * 0.05)
+    D, step, z, _ = O.group_quant_params(wp)
+    q = O.quantize_codes(wp, D, z)
+    full = (q.min(-1) == 0) & (q.max(-1) == 15)
+    assert full.mean() > 0.5
+    back = O.dequantize(q, D, z).astype(np.float32)
+    D2, step2, z2, _ = O.group_quant_params(back)
+    q2 = O.quantize_codes(back, D2, z2)
+    assert np.array_equal(step2[full], step[full])
+    assert np.array_equal(z2[full], z[full])
+    assert np.array_equal(q2[full], q[full])
+
+
+def test_power_of_two_scale_invariance():
+    """s -> 2^k s leaves codes and zero points unchanged, multiplies the step by
+    2^k and leaves the dequantized weights and the loss unchanged (the
+    transform is exact for powers of two and the step has no over/underflow)."""
+    g = _rng(12)
+    N, K, T = 6, 384, 9
+    W = _fp16_values(g.standard_normal((N, K)) * 0.02)
+    X = _fp16_values(g.standard_normal((T, K)))
+    s = np.exp(g.uniform(-1, 1, K)).astype(np.float32)
+    base = O.quantize_layer(W, s)
+    L0 = O.search_losses(W, X, s[None, :])[0]
+    for k in (-3, 3):
+        s2 = (s * np.float32(2.0 ** k)).astype(np.float32)
+        r = O.quantize_layer(W, s2)
+        assert np.array_equal(r["q"], base["q"]) and np.array_equal(r["z"], base["z"])
+        assert np.array_equal(r["D"], base["D"] * np.float32(2.0 ** k))
+        assert O.search_losses(W, X, s2[None, :])[0] == L0
+
+
+# ---------------------------------------------------------------- packing
+def test_pack_layout_and_round_trip():
+    q = np.array([[0, 1, 2, 3, 4, 5, 6, 7], [15] * 8], dtype=np.uint8)
+    w = O.pack_codes(q)
+    assert w.dtype == np.int32
+    assert int(w[0, 0]) == 0x76543210
+    assert int(w[1, 0]) == -1
+    g = _rng(13)
+    q = g.integers(0, 16, (37, 256)).astype(np.uint8)
+    assert np.array_equal(O.unpack_codes(O.pack_codes(q)), q)
+
+
+def test_storage_size_matches_pages():
+    """~4x smaller than FP16 with one scale and one zero point per 128 weights
+    ("AWQ > Benefits and Practical Considerations"; storage_figures.json)."""
+    fx = json.load(open(os.path.join(GOLDEN, "storage_figures.json")))
+    N, K = 256, 1024
+    r = O.quantize_layer(np.zeros((N, K), np.float32))
+    nbytes = O.pack_codes(r["q"]).nbytes + r["step"].nbytes + r["z"].nbytes
+    assert nbytes == N * K // 2 + 3 * N * K // fx["group"]
+    ratio = (2 * N * K) / nbytes
+    assert abs(ratio - 16 / 4.1875) < 1e-12 and abs(ratio - fx["approx_reduction"]) < 0.25
+    # 70B-shaped stack: 80 x (q, k, v, o, gate, up, down) of the workload
+    per_layer = 8192 * 8192 * 2 + 1024 * 8192 * 2 + 28672 * 8192 * 3
+    packed_gb = 80 * per_layer * (0.5 + 3 / 128) / 1e9
+    assert abs(packed_gb - 35.83) < 0.01
+    lo, hi = fx["models_gb"]["70B"]
+    assert packed_gb < hi and 80 * per_layer * 2 / 1e9 < lo * 1.0
+
+
+# ---------------------------------------------------------------- statistics
+def test_mean_abs_closed_forms():
+    g = _rng(14)
+    T, K = 300, 40
+    X = np.zeros((T, K), np.float32)
+    X[:, 0] = -3.25                                  # constant column
+    X[:, 1] = g.integers(-50, 51, T)                 # integer-valued column
+    X[:, 2:] = _fp16_values(g.standard_normal((T, K - 2)) * 5)
+    m = O.act_mean_abs(X)
+    assert m[0] == np.float32(3.25)
+    assert m[1] == np.float32(np.abs(X[:, 1]).astype(np.int64).sum() / T)
+    for j in range(K):   # every column equals the correctly rounded sum / T
+        want = np.float32(math.fsum(np.abs(X[:, j].astype(np.float64))) / T)
+        assert m[j] == want
+
+
+def test_mean_abs_bf16_truncation_only_below_2_pow_minus_17():
+    # bf16-valued data whose magnitudes are >= 2^-17 are multiples of 2^-24: exact
+    g = _rng(15)
+    v = (g.standard_normal((64, 16)) * 4).astype(np.float32)
+    v = (v.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)   # bf16 values
+    v[np.abs(v) < 2.0 ** -17] = 0
+    m = O.act_mean_abs(v)
+    for j in range(16):
+        assert m[j] == np.float32(math.fsum(np.abs(v[:, j].astype(np.float64))) / 64)
+    tiny = np.full((4, 1), 2.0 ** -30, np.float32)
+    assert O.act_mean_abs(tiny)[0] == 0.0
+    # below 2^-24 the fixed point truncates (toward zero), it does not round
+    frac = np.full((8, 1), 1.5 * 2.0 ** -25, np.float32)      # 0.75 LSB
+    assert O.act_mean_abs(frac)[0] == 0.0
+    assert O.act_fixed_point_sums(np.full((8, 1), 1.75 * 2.0 ** -24, np.float32))[0] == 8
+
+
+# ---------------------------------------------------------------- scales
+def test_candidate_scale_special_cases():
+    """alpha = 0 gives s = 1 (plain quantization); alpha = 1 gives s = s_X
+    ("AWQ Math", "Searching the scale")."""
+    g = _rng(16)
+    m = np.abs(g.standard_normal(300)).astype(np.float32)
+    m[:3] = [0.0, 1e-9, 2.0 ** -14]
+    S = O.candidate_scales(m, np.array([0.0, 1.0, 0.5]))
+    assert np.all(S[0] == 1.0)
+    assert np.array_equal(S[1], np.maximum(m, np.float32(2.0 ** -14)))
+    assert np.array_equal(S[2], np.sqrt(np.maximum(m, 2.0 ** -14).astype(np.float64)).astype(np.float32))
+    r1 = O.quantize_layer(_fp16_values(g.standard_normal((4, 256))), S[0, :256])
+    r0 = O.quantize_layer(_fp16_values(g.standard_normal((4, 256))) * 0 + r1["wp"], None)
+    assert np.array_equal(r0["q"], r1["q"])
+
+
+# ---------------------------------------------------------------- loss + search
+def _loss_by_loops(W, X, s):
+    """Independent tiny-size loss: for each token, the layer output W x and the
+    quantized layer's output computed as Q(W diag(s)) (diag(s)^-1 x), each
+    with explicit Python loops over the unpacked codes; squared difference
+    averaged over tokens and outputs."""
+    N, K = W.shape
+    r = O.quantize_layer(W, s)
+    q, D, z = r["q"], r["D"], r["z"]
+    tot = 0.0
+    for t in range(X.shape[0]):
+        xs = [float(X[t, k]) / float(s[k]) for k in range(K)]
+        for n in range(N):
+            y = math.fsum(float(W[n, k]) * float(X[t, k]) for k in range(K))
+            yq = math.fsum(float(D[n, k // 128]) * (int(q[n, k]) - int(z[n, k // 128])) * xs[k]
+                           for k in range(K))
+            tot += (y - yq) ** 2
+    return tot / (X.shape[0] * N)
+
+
+def test_search_loss_against_loops_and_gram_form():
+    g = _rng(17)
+    N, K, T = 3, 256, 6
+    W = _fp16_values(g.standard_normal((N, K)) * 0.02)
+    X = _fp16_values(g.standard_normal((T, K)) * np.where(np.arange(K) % 50 == 3, 20, 1))
+    m = O.act_mean_abs(X)
+    alphas = np.arange(20) / 19.0
+    S = O.candidate_scales(m, alphas)
+    L = O.search_losses(W, X, S)
+    for i in (0, 7, 19):
+        ref = _loss_by_loops(W, X, S[i])
+        assert abs(L[i] - ref) <= 1e-9 * ref
+    # Gram form: sum_n e_n^T (X^T X) e_n -- the same sum regrouped
+    for i in (3, 11):
+        r = O.quantize_layer(W, S[i])
+        grid = r["D"].astype(np.float64).repeat(128, 1) * (r["q"].astype(np.float64)
+                                                            - r["z"].astype(np.float64).repeat(128, 1))
+        E = W.astype(np.float64) - grid / S[i].astype(np.float64)
+        Gm = X.astype(np.float64).T @ X.astype(np.float64)
+        ref = np.einsum("nk,kl,nl->", E, Gm, E) / (T * N)
+        assert abs(L[i] - ref) <= 1e-10 * ref
+
+
+def test_search_loss_identity_calibration_is_frobenius():
+    """With X = I (each token activates one channel) the loss is ||E||_F^2 / (T N)."""
+    g = _rng(18)
+    N, K = 5, 128
+    W = _fp16_values(g.standard_normal((N, K)) * 0.1)
+    X = np.eye(K, dtype=np.float32)
+    r = O.quantize_layer(W, None)
+    E = W.astype(np.float64) - O.dequantize(r["q"].reshape(N, 1, K), r["D"],
+                                            r["z"].astype(np.float32)).reshape(N, K)
+    L = O.search_losses(W, X, np.ones((1, K), np.float32))
+    assert abs(L[0] - np.sum(E * E) / (K * N)) <= 1e-14
+
+
+def test_search_tiny_layers_brute_force():
+    """Search on tiny layers: the chosen index is the minimum of the loss vector
+    (lowest index on ties), never worse than alpha = 0 (plain round-to-nearest),
+    and a brute-force per-channel scale over the boosted channels can only do
+    as well or better than the one-knob family."""
+    for seed in range(4):
+        g = _rng(100 + seed)
+        K = 128 * (1 + seed % 2)
+        N, T = 2 + seed % 3, 8 + 4 * seed
+        b = np.ones(K, np.float32)
+        boosted = g.choice(K, 2, replace=False)
+        b[boosted] = 20.0
+        W = _fp16_values(g.standard_normal((N, K)) * 0.02)
+        X = _fp16_values(g.standard_normal((T, K)) * b)
+        m = O.act_mean_abs(X)
+        alphas = np.arange(20) / 19.0
+        i, s, inv, L = O.search_scales(W, X, m, alphas)
+        assert L[i] == np.min(L) and np.all(L[:i] > L[i])
+        assert L[i] <= L[0]
+        assert np.array_equal(s, O.candidate_scales(m, alphas)[i])
+        assert np.array_equal(inv, (np.float32(1) / s).astype(np.float32))
+        cands = []
+        for a in (1, 2, 4, 8):
+            for c in (1, 2, 4, 8):
+                v = np.ones(K, np.float32)
+                v[boosted[0]], v[boosted[1]] = a, c
+                cands.append(v)
+        Lb = O.search_losses(W, X, np.array(cands))
+        assert np.min(Lb) <= L[0]          # s = 1 is in the brute-force set
+
+
+def test_argmin_ties_and_nan():
+    assert O.choose_candidate(np.array([3.0, 1.0, 1.0, 2.0])) == 1
+    assert O.choose_candidate(np.array([np.nan, 5.0, np.nan, 4.0])) == 3
+    with pytest.raises(ValueError):
+        O.choose_candidate(np.array([np.nan, np.nan]))
+
+
+# ---------------------------------------------------------------- W4A16 product
+def test_w4a16_special_cases():
+    g = _rng(19)
+    N, K = 9, 384
+    q = g.integers(0, 16, (N, K)).astype(np.uint8)
+    step = _fp16_values(g.uniform(1e-3, 1e-1, (N, K // 128))).astype(np.float16)
+    z = g.integers(0, 16, (N, K // 128)).astype(np.uint8)
+    words = O.pack_codes(q)
+    # q == z everywhere -> y == 0 exactly
+    qz = np.repeat(z, 128, axis=1)
+    x = _fp16_values(g.standard_normal((3, K)))
+    assert np.all(O.w4a16_matmul(x, O.pack_codes(qz), step, z) == 0.0)
+    # one-hot x picks one dequantized column exactly
+    for k in (0, 129, 383):
+        e = np.zeros((1, K), np.float32)
+        e[0, k] = 1.0
+        y = O.w4a16_matmul(e, words, step, z)[0]
+        want = step[:, k // 128].astype(np.float64) * (q[:, k].astype(np.float64) - z[:, k // 128])
+        assert np.array_equal(y, want)
+
+
+def test_w4a16_equals_quantized_layer_times_scaled_input():
+    """The fused product over the packed format equals the quantized layer
+    Q(W diag(s)) applied to diag(s)^-1 x, rebuilt from the unpacked codes."""
+    g = _rng(20)
+    N, K, M = 12, 512, 4
+    W = _fp16_values(g.standard_normal((N, K)) * 0.02)
+    s = np.exp(g.uniform(-2, 2, K)).astype(np.float32)
+    r = O.quantize_layer(W, s)
+    words = O.pack_codes(r["q"])
+    x = _fp16_values(g.standard_normal((M, K)))
+    inv = (np.float32(1) / s).astype(np.float32)
+    y = O.w4a16_matmul(x, words, r["step"], r["z"], inv)
+    Wq = np.zeros((N, K))
+    for n in range(N):
+        for k in range(K):
+            Wq[n, k] = float(r["step"][n, k // 128]) * (int(r["q"][n, k]) - int(r["z"][n, k // 128]))
+    ref = (x.astype(np.float64) * inv.astype(np.float64)) @ Wq.T
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+    rows = np.array([0, 5, 11])
+    assert np.allclose(O.w4a16_matmul_rows(x, words, r["step"], r["z"], rows, inv), y[:, rows],
+                       rtol=0, atol=1e-15)
+    # with s = 1 it approximates the unquantized layer W x within the 4-bit error
+    r1 = O.quantize_layer(W, None)
+    y1 = O.w4a16_matmul(x, O.pack_codes(r1["q"]), r1["step"], r1["z"])
+    yw = x.astype(np.float64) @ W.astype(np.float64).T
+    assert np.max(np.abs(y1 - yw)) < 0.25 * np.max(np.abs(yw))
