@@ -223,6 +223,64 @@ def search_losses(W: np.ndarray, X: np.ndarray, S: np.ndarray, group: int = GROU
     return out
 
 
+def _pow2_row_exponent(a: np.ndarray) -> np.ndarray:
+    """Per row, p such that max|a_row| * 2^p < 2^14 (p = 14 - e with
+    max = f 2^e, f in [0.5, 1)); 0 for an all-zero row."""
+    mx = np.max(np.abs(a), axis=1).astype(np.float32)
+    _, e = np.frexp(mx)
+    return np.where(mx > 0, 14 - e.astype(np.int64), 0)
+
+
+def _round_rows_fp16(a32: np.ndarray):
+    """(fp16(a * 2^p_row) as float64, p_row): the exact power-of-two row scale
+    keeps each row inside float16's normal range before rounding."""
+    p = _pow2_row_exponent(a32)
+    scaled = np.ldexp(a32, p[:, None].astype(np.int32)).astype(np.float32)
+    return scaled.astype(np.float16).astype(np.float64), p
+
+
+def search_losses_operand_model(W: np.ndarray, X: np.ndarray, S: np.ndarray,
+                                x_is_fp16: bool = True, group: int = GROUP,
+                                t_chunk: int = 4096) -> np.ndarray:
+    """The same losses as ``search_losses``, scored in the precision of a
+    matrix-core evaluation, so that the chosen index -- an integer decided by
+    floating point -- is taken in the precision that evaluation uses.
+
+    READING (the pages fix no precision for the search): the error of each
+    weight is formed in float32 as E = W - fp32(fp32(D (q - z)) / s); each row
+    of E is scaled by an exact power of two 2^p (row max below 2^14) and
+    rounded to float16; calibration tokens that are not float16 already
+    (bfloat16 input) get the same treatment per token; the products and sums
+    are then exact (float64 here), and the scales are undone exactly.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    X = np.asarray(X, dtype=np.float32)
+    N, K = W.shape
+    T = X.shape[0]
+    if x_is_fp16:
+        Xh = X.astype(np.float64)
+        assert np.array_equal(X.astype(np.float16).astype(np.float32), X)
+        px = np.zeros(T, dtype=np.int64)
+    else:
+        Xh, px = _round_rows_fp16(X)
+    out = np.empty(S.shape[0], dtype=np.float64)
+    for i in range(S.shape[0]):
+        s = np.asarray(S[i], dtype=np.float32)
+        r = quantize_layer(W, s, group)
+        Dk = np.repeat(r["D"], group, axis=1)                       # float32 [N, K]
+        zk = np.repeat(r["z"].astype(np.float32), group, axis=1)
+        grid = Dk * (r["q"].astype(np.float32) - zk)                # exact in float32
+        E32 = W - grid / s[None, :]                                 # float32 division, subtraction
+        Eh, pe = _round_rows_fp16(E32)
+        acc = 0.0
+        for t0 in range(0, T, t_chunk):
+            P = Xh[t0:t0 + t_chunk] @ Eh.T                          # [t, N], scaled by 2^(px + pe)
+            P = np.ldexp(P, -(px[t0:t0 + t_chunk, None] + pe[None, :]).astype(np.int32))
+            acc += float(np.sum(P * P))
+        out[i] = acc / (float(T) * float(N))
+    return out
+
+
 def choose_candidate(losses: np.ndarray) -> int:
     """Lowest index among the minimal finite losses; NaN is never chosen
     (READING); all-NaN is an error."""
@@ -235,11 +293,17 @@ def choose_candidate(losses: np.ndarray) -> int:
 
 
 def search_scales(W: np.ndarray, X: np.ndarray, m: np.ndarray, alphas: np.ndarray,
-                  group: int = GROUP):
+                  group: int = GROUP, operand_model: str | None = None):
     """Full search: candidate scales, losses, argmin.  Returns
-    (best index, s* float32 [K], 1/s* float32 [K], losses float64 [n])."""
+    (best index, s* float32 [K], 1/s* float32 [K], losses float64 [n]).
+    operand_model: None scores exactly (float64); "fp16" / "fp16-scaled-x"
+    score with ``search_losses_operand_model`` (calibration tokens already
+    float16, or rounded to float16 per token)."""
     S = candidate_scales(m, alphas)
-    L = search_losses(W, X, S, group)
+    if operand_model is None:
+        L = search_losses(W, X, S, group)
+    else:
+        L = search_losses_operand_model(W, X, S, operand_model == "fp16", group)
     i = choose_candidate(L)
     s = S[i]
     return i, s, (np.float32(1.0) / s).astype(np.float32), L

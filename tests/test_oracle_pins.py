@@ -490,3 +490,71 @@ def test_w4a16_equals_quantized_layer_times_scaled_input():
     y1 = O.w4a16_matmul(x, O.pack_codes(r1["q"]), r1["step"], r1["z"])
     yw = x.astype(np.float64) @ W.astype(np.float64).T
     assert np.max(np.abs(y1 - yw)) < 0.25 * np.max(np.abs(yw))
+
+
+# ---------------------------------------------------------------- scoring precision model
+def test_operand_model_within_rounding_bound_of_exact():
+    """Scoring with fp16-rounded errors stays within the rounding bound of the
+    exact loss (fp16 unit roundoff 2^-11 on E, plus the float32 formation of
+    E), on tiny layers with outlier channels."""
+    g = _rng(30)
+    for seed in range(3):
+        N, K, T = 3 + seed, 256, 9 + seed
+        W = _fp16_values(g.standard_normal((N, K)) * 0.02)
+        X = _fp16_values(g.standard_normal((T, K)) * np.where(np.arange(K) % 37 == 1, 20, 1))
+        S = O.candidate_scales(O.act_mean_abs(X), np.arange(20) / 19.0)
+        Lm = O.search_losses_operand_model(W, X, S)
+        Le = O.search_losses(W, X, S)
+        for i in range(20):
+            r = O.quantize_layer(W, S[i])
+            grid = O.dequantize(r["q"].reshape(N, 2, 128), r["D"], r["z"].astype(np.float32)).reshape(N, K)
+            Wh = O.unscale_activation(grid, S[i])
+            E = W.astype(np.float64) - Wh
+            A = np.abs(E) @ np.abs(X.astype(np.float64)).T
+            C = (np.abs(W) + np.abs(Wh)) @ np.abs(X.astype(np.float64)).T
+            B = 2.0 ** -11 * A + 2.0 ** -22 * C
+            P = E @ X.astype(np.float64).T
+            bound = np.sum(2 * np.abs(P) * B + B * B) / (T * N)
+            assert abs(Lm[i] - Le[i]) <= bound
+
+
+def test_operand_model_exact_when_errors_are_representable():
+    """With s = 1 and weights on a coarse dyadic grid the errors have few
+    significant bits, so rounding them to fp16 changes nothing."""
+    g = _rng(31)
+    N, K, T = 4, 256, 7
+    W = (g.integers(-40, 41, (N, K)) * 2.0 ** -9).astype(np.float32)
+    W[:, 0], W[:, 128] = -40 * 2.0 ** -9, 40 * 2.0 ** -9
+    X = _fp16_values(g.standard_normal((T, K)))
+    S = np.ones((1, K), np.float32)
+    assert O.search_losses_operand_model(W, X, S)[0] == O.search_losses(W, X, S)[0]
+
+
+def test_operand_model_token_scaling_is_exact_for_fp16_tokens():
+    """Per-token power-of-two scaling then fp16 rounding is exact for tokens
+    that are already fp16 values of moderate range, so both token treatments
+    score identically; bf16-valued tokens also convert exactly."""
+    g = _rng(32)
+    N, K, T = 5, 384, 11
+    W = _fp16_values(g.standard_normal((N, K)) * 0.02)
+    X = _fp16_values(g.standard_normal((T, K)) * 3)
+    S = O.candidate_scales(O.act_mean_abs(X), np.array([0.0, 0.5, 1.0]))
+    a = O.search_losses_operand_model(W, X, S, x_is_fp16=True)
+    b = O.search_losses_operand_model(W, X, S, x_is_fp16=False)
+    assert np.array_equal(a, b)
+    Xb = (X.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)   # bf16 values
+    c = O.search_losses_operand_model(W, Xb, S, x_is_fp16=False)
+    d = O.search_losses_operand_model(W, Xb.astype(np.float16).astype(np.float32), S, x_is_fp16=True)
+    assert np.array_equal(c, d)
+
+
+def test_operand_model_row_exponent():
+    from oracle.awq import _pow2_row_exponent
+    a = np.array([[0.75, -3.0], [0.0, 0.0], [2.0 ** -30, 1e-31], [40000.0, 1.0]], np.float32)
+    p = _pow2_row_exponent(a)
+    for row, pi in zip(a, p):
+        mx = np.max(np.abs(row))
+        if mx == 0:
+            assert pi == 0
+        else:
+            assert 2.0 ** 13 <= mx * 2.0 ** pi < 2.0 ** 14
