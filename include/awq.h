@@ -1,0 +1,202 @@
+/*
+ * awq.h -- C ABI of the AWQ W4A16 hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The method is activation-aware weight quantization as described in
+ *   "AWQ Math" (aicassindra.com transformer-math series),
+ *   "AWQ > Benefits and Practical Considerations" and "AWQ > Limitations"
+ *   (mbrenndoerfer.com),
+ *   "AWQ vs. GPTQ: Understanding Weight Quantization Principles".
+ *
+ * Four calls make up the path:
+ *   awq_act_stats      per-input-channel mean |x_j| over calibration tokens
+ *   awq_search_scales  s_j = (mean|x_j|)^alpha, alpha chosen on a grid by the
+ *                      layer-output MSE of Q(W diag(s)) diag(s)^-1 x
+ *   awq_quantize_pack  group-128 asymmetric 4-bit round-to-nearest of
+ *                      W diag(s): codes packed 8 per int32, one fp16 step and
+ *                      one uint8 zero point per group
+ *   awq_w4a16_gemm     y = x (dequant W)^T fused: unpack, apply the group step
+ *                      and zero point, optionally the per-channel 1/s
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  Shapes.  W is [N][K] row-major (N = output channels C_out, K = input
+ *    channels C_in); activations are [rows][ldx] row-major with K used
+ *    columns.  The group size is 128 input channels and K must be a multiple
+ *    of it.
+ *  Memory.  Every array argument is a DEVICE pointer on the current HIP device,
+ *    allocated and owned by the caller; the library allocates nothing and keeps
+ *    no state between calls.  Scratch memory is the caller's workspace `ws` of
+ *    at least awq_workspace_bytes(...) bytes, 256-byte aligned.
+ *  Alignment.  Activations, weights and packed codes must be 16-byte aligned
+ *    and leading dimensions multiples of 8 elements (128-bit loads).
+ *  Execution.  Every call validates its arguments on the host, then enqueues
+ *    kernels on `stream` (a hipStream_t; NULL is the null stream) and returns
+ *    without waiting.  Asynchronous device faults surface at the caller's
+ *    synchronisation.  Calls are re-entrant; two calls that share a workspace
+ *    must be ordered on one stream.
+ *  Errors.  On any status other than AWQ_OK nothing was enqueued and the
+ *    outputs are untouched (AWQ_ERR_HIP: a launch failed part way).
+ *  Determinism.  The same inputs give bit-identical outputs on every run: no
+ *    floating-point atomics, fixed reduction orders.
+ *  Numerical domain.  Inputs are finite.  Calibration column sums satisfy
+ *    sum_t |x_tj| < 2^29 (fixed-point range of the statistic).  The group range
+ *    of W diag(s) divided by 15 is below 65504 (the step is stored in fp16).
+ *    Outside this domain results are unspecified.
+ */
+#ifndef AWQ_H
+#define AWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum awq_status {
+  AWQ_OK = 0,
+  AWQ_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  AWQ_ERR_SHAPE = 2,        /* K % group != 0, a size < 0 (or 0 where > 0 needed), ld < K */
+  AWQ_ERR_DTYPE = 3,        /* element type not accepted by this call               */
+  AWQ_ERR_ALIGN = 4,        /* pointer not 16-byte aligned or ld % 8 != 0            */
+  AWQ_ERR_UNSUPPORTED = 5,  /* group_size != 128, n_alpha outside [1, 64], K too big */
+  AWQ_ERR_WORKSPACE = 6,    /* ws NULL or smaller than awq_workspace_bytes(...)      */
+  AWQ_ERR_HIP = 7           /* a HIP launch failed                                   */
+} awq_status;
+
+typedef enum awq_dtype {
+  AWQ_F16 = 0,   /* IEEE binary16                       */
+  AWQ_BF16 = 1,  /* bfloat16                            */
+  AWQ_F32 = 2    /* IEEE binary32 (outputs only)        */
+} awq_dtype;
+
+typedef enum awq_op {
+  AWQ_OP_ACT_STATS = 0,
+  AWQ_OP_SEARCH = 1,
+  AWQ_OP_QUANTIZE = 2,
+  AWQ_OP_GEMM = 3
+} awq_op;
+
+#define AWQ_GROUP 128
+#define AWQ_MAX_ALPHA 64
+#define AWQ_MAX_K 131072
+
+/* Version of this interface (incremented on any signature change). */
+int awq_abi_version(void);
+
+/* Human-readable name of a status value (static storage). */
+const char* awq_status_str(awq_status st);
+
+/* Workspace bytes a call needs for the given sizes (0 if it needs none).
+ * Arguments that an op does not use are ignored. */
+size_t awq_workspace_bytes(awq_op op, int64_t M, int64_t N, int64_t K, int64_t T, int n_alpha);
+
+/*
+ * Calibration statistic: mean_abs[j] = average over t of |x[t][j]|.
+ * "AWQ Math", section "Saliency is an activation property, not a weight
+ * property" (input channels ranked by average |x_j| over a calibration set);
+ * "AWQ > Limitations" (the saliency metric is the average activation
+ * magnitude).
+ *
+ * The sum is exact: each |x| is taken in fixed point with LSB 2^-24 (exact for
+ * fp16; bf16 magnitudes below 2^-17 are truncated to that LSB), summed in
+ * integers, converted once to double, multiplied by 2^-24, divided by T in
+ * double and rounded to float.
+ *
+ *   x         [T][ldx] fp16 or bf16 (xdt), K columns used
+ *   T         calibration tokens, > 0
+ *   K         input channels, > 0, multiple of 8
+ *   ldx       row stride in elements, >= K, multiple of 8
+ *   mean_abs  [K] float, written
+ *   ws        >= awq_workspace_bytes(AWQ_OP_ACT_STATS, 0, 0, K, T, 0)
+ */
+awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int64_t ldx,
+                         float* mean_abs, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Scale search.  "AWQ Math", section "Searching the scale -- no backprop
+ * required": s_j = (s_X,j)^alpha with s_X,j = mean |x_j|, alpha on a small grid
+ * in [0, 1], and the alpha that minimises the mean squared error between the
+ * layer output W x and Q(W diag(s)) diag(s)^-1 x over the calibration tokens
+ * wins.  Q is the quantizer of awq_quantize_pack (fp16 step as stored).
+ *
+ *   candidate i: s_ij = float( pow( max(double(mean_abs[j]), 2^-14), alphas[i] ) )
+ *   loss_i      = (1 / (T N)) sum_t sum_n ( ((W - W_hat_i) x_t)_n )^2
+ *   best        = lowest i with the minimal loss (NaN losses are skipped)
+ *
+ *   w           [N][K] fp16 or bf16 (dt), contiguous
+ *   x_calib     [T][ldx] same dtype as w
+ *   mean_abs    [K] float (output of awq_act_stats)
+ *   alphas      [n_alpha] double, device memory
+ *   n_alpha     1..AWQ_MAX_ALPHA
+ *   group_size  must be 128
+ *   s_out       [K] float: s of the best candidate
+ *   inv_s_out   [K] float: 1.0f / s (IEEE division); may be NULL
+ *   loss_out    [n_alpha] double; may be NULL
+ *   best_idx_out  int32; may be NULL; -1 if every loss is NaN
+ * The error products run on fp16/bf16 matrix cores with fp32 accumulation;
+ * the per-row error is scaled by an exact power of two before rounding to
+ * fp16 so that it stays in the normal range.  Linears that read the same input
+ * may be searched together by passing their row-concatenated W.
+ */
+awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
+                             const void* x_calib, int64_t T, int64_t ldx,
+                             const float* mean_abs, const double* alphas, int n_alpha,
+                             int group_size, float* s_out, float* inv_s_out, double* loss_out,
+                             int32_t* best_idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Group-wise asymmetric 4-bit round-to-nearest of W' = W diag(s).
+ * "AWQ Math", sections "Weight-only quantization and where it breaks"
+ * (Q(w) = step * round(w / step)) and "Shapes, granularity, and complexity"
+ * (groups of 128 input channels, each with its own step and zero point);
+ * "AWQ > Benefits and Practical Considerations" (one scale and one zero point
+ * per 128 weights).  Per group of 128 consecutive k of one row n:
+ *   w'  = float(w) * s_k                      (s == NULL: s = 1, plain RTN)
+ *   lo  = min(0, min w'),  hi = max(0, max w')
+ *   d   = (hi - lo) / 15                      (float, IEEE division)
+ *   step = smallest fp16 >= max(d, 2^-24);   D = float(step)
+ *   z   = clamp(rint(-lo / D), 0, 15)
+ *   q_k = clamp(rint(w'_k / D) + z, 0, 15)    (rint: round half to even)
+ *
+ *   w         [N][K] fp16 or bf16 (dt), contiguous
+ *   s         [K] float or NULL
+ *   qweight   [N][K/8] int32: code of k = 8c + j in bits [4j, 4j+4) of word c
+ *   scales    [N][K/128] fp16 bit patterns (step)
+ *   zeros     [N][K/128] uint8 (z)
+ *   scales_f32_dbg [N][K/128] float (d, before rounding); may be NULL
+ * N == 0 is a no-op.
+ */
+awq_status awq_quantize_pack(const void* w, awq_dtype dt, int64_t N, int64_t K, const float* s,
+                             int group_size, int32_t* qweight, uint16_t* scales, uint8_t* zeros,
+                             float* scales_f32_dbg, void* stream);
+
+/*
+ * Fused W4A16 product.  "AWQ > Benefits and Practical Considerations": the
+ * dequantization unpacks 4-bit integers, applies the group scale and zero
+ * point and optionally the per-channel inverse scale (when it is not folded
+ * into the preceding layer), fused with the matrix multiply so that the fp16
+ * weight matrix is never materialised.
+ *   y[m][n] = sum_k step[n][k/128] * (q[n][k] - z[n][k/128]) * x[m][k] * r[k]
+ * with r = inv_s (or 1 when inv_s == NULL).
+ *
+ *   x        [M][ldx] fp16 or bf16 (xdt)
+ *   qweight, scales, zeros  as written by awq_quantize_pack
+ *   inv_s    [K] float or NULL
+ *   y        [M][ldy] of ydt (F16, BF16 or F32)
+ *   ws       >= awq_workspace_bytes(AWQ_OP_GEMM, M, N, K, 0, 0)
+ * M <= 8 runs the split-K GEMV kernel (fp32 accumulation of exact
+ * int4 x activation products); larger M runs the matrix-core kernel, whose
+ * operands are the dequantized weights rounded to xdt.  M == 0 or N == 0 is a
+ * no-op.
+ */
+awq_status awq_w4a16_gemm(const void* x, awq_dtype xdt, int64_t M, int64_t K, int64_t ldx,
+                          const int32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                          int64_t N, int group_size, const float* inv_s, void* y, awq_dtype ydt,
+                          int64_t ldy, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_H */

@@ -1,0 +1,147 @@
+"""The C ABI library: it loads without a GPU, exports every symbol that
+include/awq.h declares, and rejects bad arguments on the host before any
+launch (so none of these calls touches device memory)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+abi = pytest.importorskip("weight_only_int4_stats_amd._abi")
+
+
+def _lib():
+    if not os.path.exists(abi.LIB_PATH):
+        pytest.fail("libawq_gfx950.so is not built (python -m weight_only_int4_stats_amd.build)")
+    return abi.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = declared_functions()
+    for n in ("awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_w4a16_gemm",
+              "awq_workspace_bytes", "awq_status_str", "awq_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in abi.SIGNATURES, f"binding lacks {name}"
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert lib.awq_abi_version() == 1
+    for code in range(8):
+        assert lib.awq_status_str(code).decode()
+    assert lib.awq_status_str(0).decode() == "ok"
+
+
+def test_workspace_sizes():
+    lib = _lib()
+    assert lib.awq_workspace_bytes(abi.AWQ_OP_ACT_STATS, 0, 0, 4096, 65536, 0) >= 4096 * 8
+    assert lib.awq_workspace_bytes(abi.AWQ_OP_QUANTIZE, 0, 11008, 4096, 0, 0) == 0
+    n = lib.awq_workspace_bytes(abi.AWQ_OP_SEARCH, 0, 11008, 4096, 65536, 20)
+    assert n >= 11008 * 4096 * 2 + 20 * 4096 * 4
+    assert lib.awq_workspace_bytes(abi.AWQ_OP_SEARCH, 0, -1, 4096, 64, 20) == 0
+
+
+# fake device addresses: validation must fail before anything dereferences them
+A = ctypes.c_void_p(0x10000)       # 16-byte aligned
+A2 = ctypes.c_void_p(0x20000)
+A3 = ctypes.c_void_p(0x30000)
+BAD = ctypes.c_void_p(0x10002)     # misaligned
+NULL = None
+E = abi
+
+
+def test_act_stats_validation():
+    lib = _lib()
+    f = lib.awq_act_stats
+    ws_ok = 1 << 20
+    assert f(NULL, E.AWQ_F16, 64, 512, 512, A2, A3, ws_ok, NULL) == 1
+    assert f(A, E.AWQ_F16, 64, 512, 512, NULL, A3, ws_ok, NULL) == 1
+    assert f(A, E.AWQ_F32, 64, 512, 512, A2, A3, ws_ok, NULL) == 3
+    assert f(A, E.AWQ_F16, 0, 512, 512, A2, A3, ws_ok, NULL) == 2        # empty calibration
+    assert f(A, E.AWQ_F16, 64, 512, 500, A2, A3, ws_ok, NULL) == 2       # ld < K
+    assert f(A, E.AWQ_F16, 64, 500, 504, A2, A3, ws_ok, NULL) == 4       # K % 8
+    assert f(BAD, E.AWQ_F16, 64, 512, 512, A2, A3, ws_ok, NULL) == 4
+    assert f(A, E.AWQ_F16, 64, 512, 512, A2, NULL, ws_ok, NULL) == 6
+    assert f(A, E.AWQ_F16, 64, 512, 512, A2, A3, 16, NULL) == 6
+
+
+def test_search_validation():
+    lib = _lib()
+    f = lib.awq_search_scales
+    ws = 1 << 40
+
+    def call(**kw):
+        a = dict(w=A, dt=E.AWQ_F16, N=512, K=512, x=A2, T=64, ldx=512, m=A3, al=A3, na=20, g=128,
+                 s=A2, inv=NULL, loss=NULL, best=NULL, ws=A3, wsb=ws)
+        a.update(kw)
+        return f(a["w"], a["dt"], a["N"], a["K"], a["x"], a["T"], a["ldx"], a["m"], a["al"], a["na"],
+                 a["g"], a["s"], a["inv"], a["loss"], a["best"], a["ws"], a["wsb"], NULL)
+
+    assert call(w=NULL) == 1
+    assert call(s=NULL) == 1
+    assert call(dt=E.AWQ_F32) == 3
+    assert call(g=64) == 5
+    assert call(na=0) == 5
+    assert call(na=65) == 5
+    assert call(K=500, ldx=504) == 2
+    assert call(T=0) == 2
+    assert call(N=0) == 2
+    assert call(ldx=256) == 2
+    assert call(w=BAD) == 4
+    assert call(ws=NULL) == 6
+    assert call(wsb=1024) == 6
+
+
+def test_quantize_validation():
+    lib = _lib()
+    f = lib.awq_quantize_pack
+    assert f(A, E.AWQ_F16, 0, 512, NULL, 128, NULL, NULL, NULL, NULL, NULL) == 0   # N = 0: no-op
+    assert f(NULL, E.AWQ_F16, 4, 512, NULL, 128, A2, A3, A3, NULL, NULL) == 1
+    assert f(A, E.AWQ_F16, 4, 512, NULL, 128, A2, NULL, A3, NULL, NULL) == 1
+    assert f(A, E.AWQ_F32, 4, 512, NULL, 128, A2, A3, A3, NULL, NULL) == 3
+    assert f(A, E.AWQ_F16, 4, 500, NULL, 128, A2, A3, A3, NULL, NULL) == 2
+    assert f(A, E.AWQ_F16, -1, 512, NULL, 128, A2, A3, A3, NULL, NULL) == 2
+    assert f(A, E.AWQ_F16, 4, 512, NULL, 256, A2, A3, A3, NULL, NULL) == 5
+    assert f(BAD, E.AWQ_F16, 4, 512, NULL, 128, A2, A3, A3, NULL, NULL) == 4
+    assert f(A, E.AWQ_F16, 4, 512, BAD, 128, A2, A3, A3, NULL, NULL) == 4
+
+
+def test_gemm_validation():
+    lib = _lib()
+    f = lib.awq_w4a16_gemm
+
+    def call(**kw):
+        a = dict(x=A, xdt=E.AWQ_F16, M=1, K=4096, ldx=4096, q=A2, sc=A3, z=A3, N=11008, g=128,
+                 r=NULL, y=A2, ydt=E.AWQ_F16, ldy=11008)
+        a.update(kw)
+        return f(a["x"], a["xdt"], a["M"], a["K"], a["ldx"], a["q"], a["sc"], a["z"], a["N"], a["g"],
+                 a["r"], a["y"], a["ydt"], a["ldy"], NULL, 0, NULL)
+
+    assert call(M=0, x=NULL) == 0          # empty input: no-op
+    assert call(N=0, ldy=0, q=NULL) == 0
+    assert call(x=NULL) == 1
+    assert call(y=NULL) == 1
+    assert call(xdt=E.AWQ_F32) == 3
+    assert call(ydt=7) == 3
+    assert call(K=4000, ldx=4000) == 2
+    assert call(ldy=100) == 2
+    assert call(M=-1) == 2
+    assert call(g=32) == 5
+    assert call(x=BAD) == 4
+    assert call(ldx=4100) == 4
+    assert call(r=BAD) == 4

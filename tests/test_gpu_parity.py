@@ -1,0 +1,274 @@
+"""GPU vs oracle parity for every step of the hot path, through the C ABI.
+
+Sizes are small enough for the oracle to finish in seconds but span several
+tiles, ragged tails and both dtypes.  Integer and byte outputs (statistics,
+codes, packed words, fp16 steps, zero points, the chosen candidate and its
+scales) must be bit-exact; products are held to max|err| / max|ref| <= 2e-3, where for 16-bit outputs
+the output's own rounding (half an ulp) is not counted;
+search losses to a bound derived from the operand rounding (gpu_util).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from tests.gpu_util import FP16_U, GEMM_TOL, f32, gpu, loss_error_bound, rel_max_err
+
+pytestmark = pytest.mark.gpu
+
+awq = pytest.importorskip("weight_only_int4_stats_amd")
+F16, BF16 = torch.float16, torch.bfloat16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    awq.lib()
+
+
+def _act(T, K, dtype, seed, boost=20.0, tiny=False):
+    x = WL.random_matrix((T, K), torch.float32, seed)
+    x[:, ::97] *= boost
+    if tiny:
+        x[:, 1::53] *= 1e-7
+    return x.to(dtype)
+
+
+# ------------------------------------------------------------- statistics
+@pytest.mark.parametrize("T,K,dtype,ld_pad", [
+    (64, 512, F16, 0), (77, 4096, F16, 0), (64, 11008, F16, 0), (1, 128, F16, 0),
+    (200, 384, BF16, 0), (1000, 8192, BF16, 0), (333, 1024, F16, 64), (96, 2048, BF16, 8),
+])
+def test_act_stats_bit_exact(T, K, dtype, ld_pad):
+    x = _act(T, K, dtype, seed=T * 7 + K, tiny=(dtype == BF16))
+    if ld_pad:
+        big = torch.zeros((T, K + ld_pad), dtype=dtype)
+        big[:, :K] = x
+        xg = gpu(big)[:, :K]
+    else:
+        xg = gpu(x)
+    m = awq.awq_act_stats(xg)
+    torch.cuda.synchronize()
+    ref = O.act_mean_abs(f32(x))
+    assert np.array_equal(m.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------- quantize + pack
+@pytest.mark.parametrize("N,K,dtype,with_s", [
+    (512, 512, F16, False), (37, 4096, F16, True), (300, 11008, BF16, True),
+    (5, 128, F16, True), (129, 1024, BF16, False), (64, 384, F16, True),
+])
+def test_quantize_pack_bit_exact(N, K, dtype, with_s):
+    W = WL.random_matrix((N, K), torch.float32, seed=N + K, scale=0.02)
+    W[:, 3::101] *= 30.0                      # outliers inside some groups
+    W[0, :128] = 0.0                          # an all-zero group
+    W[1, 128 % K:128 % K + 128] = 0.75        # a constant group (or row 1 start)
+    W = W.to(dtype)
+    s = None
+    if with_s:
+        g = np.random.Generator(np.random.PCG64(N * K))
+        s = torch.from_numpy(np.exp(g.uniform(-2.5, 2.5, K)).astype(np.float32))
+    dbg = torch.empty((N, K // 128), dtype=torch.float32, device="cuda")
+    q, sc, z = awq.awq_quantize_pack(gpu(W), None if s is None else gpu(s), scales_f32_dbg=dbg)
+    torch.cuda.synchronize()
+    r = O.quantize_layer(f32(W), None if s is None else s.numpy())
+    assert np.array_equal(dbg.cpu().numpy().view(np.uint32), r["d"].view(np.uint32))
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), r["step"].view(np.uint16))
+    assert np.array_equal(z.cpu().numpy(), r["z"])
+    assert np.array_equal(q.cpu().numpy(), O.pack_codes(r["q"]))
+
+
+# ------------------------------------------------------------- W4A16 product
+def _random_packed(N, K, seed, step_lo=2e-4, step_hi=4e-3):
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = g.integers(0, 16, (N, K)).astype(np.uint8)
+    step = g.uniform(step_lo, step_hi, (N, K // 128)).astype(np.float16)
+    z = g.integers(0, 16, (N, K // 128)).astype(np.uint8)
+    return O.pack_codes(q), step, z
+
+
+def _run_product(M, N, K, dtype, ydt, with_r, seed):
+    words, step, z = _random_packed(N, K, seed)
+    x = _act(M, K, dtype, seed + 1)
+    r = None
+    if with_r:
+        g = np.random.Generator(np.random.PCG64(seed + 2))
+        r = (np.float32(1) / np.exp(g.uniform(-1.5, 1.5, K)).astype(np.float32)).astype(np.float32)
+    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                           gpu(torch.from_numpy(z)), None if r is None else gpu(torch.from_numpy(r)),
+                           out_dtype=ydt)
+    torch.cuda.synchronize()
+    ref = O.w4a16_matmul(f32(x), words, step, z, r)
+    return f32(y), ref
+
+
+@pytest.mark.parametrize("M,N,K,dtype,ydt,with_r", [
+    (1, 512, 512, F16, F16, False), (1, 11008, 4096, F16, F16, True),
+    (1, 1000, 11008, F16, torch.float32, True), (1, 333, 128, BF16, BF16, False),
+    (1, 257, 384, F16, torch.float32, False), (2, 4096, 4096, BF16, torch.float32, True),
+    (3, 700, 2048, F16, F16, True), (8, 11008, 4096, F16, F16, False),
+    (8, 1024, 11008, BF16, torch.float32, True), (5, 96, 1024, F16, torch.float32, False),
+    (1, 64, 28672, F16, torch.float32, True), (4, 130, 28672, BF16, BF16, False),
+])
+def test_gemv_parity(M, N, K, dtype, ydt, with_r):
+    y, ref = _run_product(M, N, K, dtype, ydt, with_r, seed=M * 1000 + N + K)
+    err = rel_max_err(y, ref, ydt)
+    print(f"gemv M={M} N={N} K={K} {dtype} -> {ydt}: rel max err {err:.3e}")
+    assert err <= GEMM_TOL
+
+
+@pytest.mark.parametrize("M,N,K,dtype,ydt,with_r", [
+    (9, 300, 512, F16, torch.float32, False), (32, 4096, 4096, F16, F16, True),
+    (100, 1000, 1024, BF16, torch.float32, True), (256, 512, 8192, BF16, BF16, False),
+    (130, 257, 384, F16, torch.float32, True), (8, 64, 65536, F16, torch.float32, False),
+])
+def test_gemm_parity(M, N, K, dtype, ydt, with_r):
+    y, ref = _run_product(M, N, K, dtype, ydt, with_r, seed=M * 1000 + N + K)
+    err = rel_max_err(y, ref, ydt)
+    print(f"gemm M={M} N={N} K={K} {dtype} -> {ydt}: rel max err {err:.3e}")
+    assert err <= GEMM_TOL
+
+
+def test_product_special_cases():
+    """q == z gives 0; a one-hot x picks the dequantized column.  The GEMV
+    accumulates exact int4 x activation products, so the one-hot column is
+    exact there and q == z leaves only the rounding of the zero-point sum; the
+    matrix-core path rounds step * (q - z) to the operand type, so it is exact
+    for q == z and, with power-of-two steps, for one-hot x."""
+    N, K = 200, 1024
+    words, step, z = _random_packed(N, K, 5)
+    qz = np.repeat(z, 128, axis=1)
+    x = _act(40, K, F16, 6)
+    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(O.pack_codes(qz))),
+                           gpu(torch.from_numpy(step)), gpu(torch.from_numpy(z)),
+                           out_dtype=torch.float32)
+    assert torch.count_nonzero(y).item() == 0
+    y1 = awq.awq_w4a16_gemm(gpu(x[:1]), gpu(torch.from_numpy(O.pack_codes(qz))),
+                            gpu(torch.from_numpy(step)), gpu(torch.from_numpy(z)),
+                            out_dtype=torch.float32)
+    bound = 2.0 ** -20 * 1040 * float(np.max(step.astype(np.float32))) * float(np.abs(f32(x[:1])).sum())
+    assert float(y1.abs().max()) <= bound
+    pow2 = np.ldexp(np.float16(1), np.random.Generator(np.random.PCG64(8)).integers(
+        -12, -5, step.shape)).astype(np.float16)
+    for M, k, st in ((1, 0, step), (1, 777, step), (33, 130, pow2), (17, 1023, pow2)):
+        x = torch.zeros((M, K), dtype=F16)
+        x[:, k] = 1.0
+        y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(st)),
+                               gpu(torch.from_numpy(z)), out_dtype=torch.float32)
+        ref = O.w4a16_matmul(f32(x), words, st, z)
+        assert np.array_equal(f32(y), ref.astype(np.float32))
+
+
+# ------------------------------------------------------------- scale search
+SEARCH_MODEL_RTOL = 1e-5   # GPU loss vs the oracle scored in the same operand precision
+
+
+def _check_search(W, X, dtype, n_alpha=20):
+    """Statistic bit-exact; chosen index, s and 1/s bit-exact against the
+    oracle scored in the matrix-core operand precision (the decision is taken
+    in the same precision on both sides); every loss within SEARCH_MODEL_RTOL
+    of that oracle and within the rigorous rounding bound of the exact fp64
+    losses."""
+    alphas = WL.alpha_grid(n_alpha)
+    m = awq.awq_act_stats(gpu(X))
+    s, inv, L, best = awq.awq_search_scales(gpu(W), gpu(X), m, gpu(torch.from_numpy(alphas)))
+    torch.cuda.synchronize()
+    s, inv, L, best = s.cpu().numpy(), inv.cpu().numpy(), L.cpu().numpy(), int(best.cpu()[0])
+    m_ref = O.act_mean_abs(f32(X))
+    assert np.array_equal(m.cpu().numpy().view(np.uint32), m_ref.view(np.uint32))
+    model = "fp16" if dtype == F16 else "fp16-scaled-x"
+    i_mod, s_mod, inv_mod, L_mod = O.search_scales(f32(W), f32(X), m_ref, alphas, operand_model=model)
+    S = O.candidate_scales(m_ref, alphas)
+    L_ex = O.search_losses(f32(W), f32(X), S)
+    W64, X64 = f32(W).astype(np.float64), f32(X).astype(np.float64)
+    N, K = W64.shape
+    for i in range(n_alpha):
+        assert abs(L[i] - L_mod[i]) <= SEARCH_MODEL_RTOL * L_mod[i], (i, L[i], L_mod[i])
+        r = O.quantize_layer(f32(W), S[i])
+        grid = O.dequantize(r["q"].reshape(N, K // 128, 128), r["D"],
+                            r["z"].astype(np.float32)).reshape(N, K)
+        b, _ = loss_error_bound(W64, X64, O.unscale_activation(grid, S[i]), FP16_U)
+        assert abs(L[i] - L_ex[i]) <= b + 1e-6 * L_ex[i], (i, L[i], L_ex[i], b)
+    order = np.argsort(L_mod)
+    gap = (L_mod[order[1]] - L_mod[order[0]]) / L_mod[order[0]]
+    print(f"search N={N} K={K}: best {i_mod} (exact-scoring best {O.choose_candidate(L_ex)}), "
+          f"gap {gap:.2e}, max loss diff vs model {np.max(np.abs(L - L_mod) / L_mod):.2e}")
+    if gap <= 2 * SEARCH_MODEL_RTOL:
+        pytest.skip(f"ill-posed seed: best and runner-up {gap:.2e} apart (relative)")
+    assert best == i_mod
+    assert np.array_equal(s.view(np.uint32), s_mod.view(np.uint32))
+    assert np.array_equal(inv.view(np.uint32), inv_mod.view(np.uint32))
+
+
+def test_search_single_linear_512():
+    w = WL.workload(1)
+    _check_search(WL.weight(w), WL.calibration(w), F16)
+
+
+@pytest.mark.parametrize("N,K,T,dtype", [(300, 1024, 200, F16), (130, 768, 77, BF16),
+                                           (64, 4096, 64, F16)])
+def test_search_ragged(N, K, T, dtype):
+    W = WL.random_matrix((N, K), torch.float32, seed=N, scale=0.02).to(dtype)
+    X = _act(T, K, dtype, seed=T)
+    _check_search(W, X, dtype)
+
+
+def test_search_single_candidate_and_endpoints():
+    """n_alpha = 1 and the endpoints: alpha = 0 gives s = 1 exactly, alpha = 1
+    gives s = max(m, 2^-14) exactly."""
+    w = WL.workload(1)
+    W, X = gpu(WL.weight(w)), gpu(WL.calibration(w))
+    m = awq.awq_act_stats(X)
+    for a, want in ((0.0, None), (1.0, "m")):
+        al = torch.tensor([a], dtype=torch.float64, device="cuda")
+        s, inv, L, best = awq.awq_search_scales(W, X, m, al)
+        torch.cuda.synchronize()
+        assert int(best.cpu()[0]) == 0
+        if want is None:
+            assert torch.all(s == 1.0).item() and torch.all(inv == 1.0).item()
+        else:
+            assert torch.equal(s, torch.clamp(m, min=2.0 ** -14))
+
+
+def test_quantized_layer_end_to_end_c1():
+    """stats -> search -> quantize with s -> GEMV with 1/s, against the oracle
+    chain on the same inputs."""
+    w = WL.workload(1)
+    W, X = WL.weight(w), WL.calibration(w)
+    x = WL.decode_input(w, 1)
+    m = awq.awq_act_stats(gpu(X))
+    al = gpu(torch.from_numpy(WL.alpha_grid(20)))
+    s, inv, _, _ = awq.awq_search_scales(gpu(W), gpu(X), m, al)
+    q, sc, z = awq.awq_quantize_pack(gpu(W), s)
+    y = awq.awq_w4a16_gemm(gpu(x), q, sc, z, inv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    i_ref, s_ref, inv_ref, _ = O.search_scales(f32(W), f32(X), O.act_mean_abs(f32(X)),
+                                               WL.alpha_grid(20), operand_model="fp16")
+    r = O.quantize_layer(f32(W), s_ref)
+    words = O.pack_codes(r["q"])
+    assert np.array_equal(q.cpu().numpy(), words)
+    ref = O.w4a16_matmul(f32(x), words, r["step"], r["z"], inv_ref)
+    assert rel_max_err(f32(y), ref) <= GEMM_TOL
+    # and the quantized layer tracks the unquantized one
+    yw = f32(x).astype(np.float64) @ f32(W).astype(np.float64).T
+    assert rel_max_err(ref, yw) < 0.1
+
+
+def test_determinism():
+    w = WL.workload(1)
+    W, X = gpu(WL.weight(w)), gpu(WL.calibration(w))
+    al = gpu(torch.from_numpy(WL.alpha_grid(20)))
+    outs = []
+    for _ in range(2):
+        m = awq.awq_act_stats(X)
+        s, inv, L, best = awq.awq_search_scales(W, X, m, al)
+        q, sc, z = awq.awq_quantize_pack(W, s)
+        xx = gpu(WL.prefill_input(w, 64))
+        y = awq.awq_w4a16_gemm(xx, q, sc, z, inv)
+        y1 = awq.awq_w4a16_gemm(xx[:1], q, sc, z, inv)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().clone() for t in (m, s, L, q, sc, z, y, y1)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))

@@ -1,0 +1,112 @@
+// C ABI of the AWQ hot path: argument validation on the host, then the
+// kernel launchers.  Nothing here allocates device memory or keeps state.
+#include <hip/hip_runtime.h>
+
+#include "../../include/awq.h"
+#include "awq_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+bool is_act_dtype(awq_dtype d) { return d == AWQ_F16 || d == AWQ_BF16; }
+bool is_out_dtype(awq_dtype d) { return d == AWQ_F16 || d == AWQ_BF16 || d == AWQ_F32; }
+
+awq_status from_hip(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int awq_abi_version(void) { return 1; }
+
+const char* awq_status_str(awq_status st) {
+  switch (st) {
+    case AWQ_OK: return "ok";
+    case AWQ_ERR_NULL: return "required pointer is NULL";
+    case AWQ_ERR_SHAPE: return "invalid shape (sizes, K % group, leading dimension)";
+    case AWQ_ERR_DTYPE: return "element type not accepted";
+    case AWQ_ERR_ALIGN: return "pointer not 16-byte aligned or leading dimension not a multiple of 8";
+    case AWQ_ERR_UNSUPPORTED: return "unsupported parameter (group size, candidate count, K)";
+    case AWQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case AWQ_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t awq_workspace_bytes(awq_op op, int64_t M, int64_t N, int64_t K, int64_t T, int n_alpha) {
+  if (N < 0 || K < 0 || T < 0 || M < 0) return 0;
+  switch (op) {
+    case AWQ_OP_ACT_STATS: return awq::act_stats_ws_bytes(K);
+    case AWQ_OP_SEARCH:  // the larger of the fp16 and bf16 layouts
+      return awq::search_ws_bytes((int)AWQ_BF16, N, K, T, n_alpha < 1 ? 1 : n_alpha);
+    case AWQ_OP_QUANTIZE: return 0;
+    case AWQ_OP_GEMM: return awq::gemm_ws_bytes(M, N, K);
+  }
+  return 0;
+}
+
+awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int64_t ldx,
+                         float* mean_abs, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !mean_abs) return AWQ_ERR_NULL;
+  if (!is_act_dtype(xdt)) return AWQ_ERR_DTYPE;
+  if (T <= 0 || K <= 0 || ldx < K) return AWQ_ERR_SHAPE;
+  if (K % 8 != 0 || ldx % 8 != 0 || !aligned16(x)) return AWQ_ERR_ALIGN;
+  if (K > AWQ_MAX_K) return AWQ_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < awq::act_stats_ws_bytes(K) || !aligned256(ws)) return AWQ_ERR_WORKSPACE;
+  return from_hip(awq::launch_act_stats(x, (int)xdt, T, K, ldx, mean_abs, ws, (hipStream_t)stream));
+}
+
+awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
+                             const void* x_calib, int64_t T, int64_t ldx,
+                             const float* mean_abs, const double* alphas, int n_alpha,
+                             int group_size, float* s_out, float* inv_s_out, double* loss_out,
+                             int32_t* best_idx_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!w || !x_calib || !mean_abs || !alphas || !s_out) return AWQ_ERR_NULL;
+  if (!is_act_dtype(dt)) return AWQ_ERR_DTYPE;
+  if (group_size != AWQ_GROUP) return AWQ_ERR_UNSUPPORTED;
+  if (n_alpha < 1 || n_alpha > AWQ_MAX_ALPHA) return AWQ_ERR_UNSUPPORTED;
+  if (N <= 0 || K <= 0 || T <= 0 || ldx < K || K % AWQ_GROUP != 0) return AWQ_ERR_SHAPE;
+  if (K > AWQ_MAX_K || N > 0x7FFFFFFF) return AWQ_ERR_UNSUPPORTED;
+  if (ldx % 8 != 0 || !aligned16(w) || !aligned16(x_calib) || !aligned16(mean_abs))
+    return AWQ_ERR_ALIGN;
+  if (!ws || ws_bytes < awq::search_ws_bytes((int)dt, N, K, T, n_alpha) || !aligned256(ws))
+    return AWQ_ERR_WORKSPACE;
+  return from_hip(awq::launch_search(w, (int)dt, N, K, x_calib, T, ldx, mean_abs, alphas, n_alpha,
+                                     s_out, inv_s_out, loss_out, best_idx_out, ws,
+                                     (hipStream_t)stream));
+}
+
+awq_status awq_quantize_pack(const void* w, awq_dtype dt, int64_t N, int64_t K, const float* s,
+                             int group_size, int32_t* qweight, uint16_t* scales, uint8_t* zeros,
+                             float* scales_f32_dbg, void* stream) {
+  if (group_size != AWQ_GROUP) return AWQ_ERR_UNSUPPORTED;
+  if (!is_act_dtype(dt)) return AWQ_ERR_DTYPE;
+  if (N < 0 || K <= 0 || K % AWQ_GROUP != 0) return AWQ_ERR_SHAPE;
+  if (N == 0) return AWQ_OK;
+  if (!w || !qweight || !scales || !zeros) return AWQ_ERR_NULL;
+  if (K > AWQ_MAX_K) return AWQ_ERR_UNSUPPORTED;
+  if (!aligned16(w) || !aligned16(qweight) || (s && !aligned16(s))) return AWQ_ERR_ALIGN;
+  return from_hip(awq::launch_quantize_pack(w, (int)dt, N, K, s, (uint32_t*)qweight, scales, zeros,
+                                            scales_f32_dbg, (hipStream_t)stream));
+}
+
+awq_status awq_w4a16_gemm(const void* x, awq_dtype xdt, int64_t M, int64_t K, int64_t ldx,
+                          const int32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                          int64_t N, int group_size, const float* inv_s, void* y, awq_dtype ydt,
+                          int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  if (group_size != AWQ_GROUP) return AWQ_ERR_UNSUPPORTED;
+  if (!is_act_dtype(xdt) || !is_out_dtype(ydt)) return AWQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K <= 0 || K % AWQ_GROUP != 0 || ldx < K || ldy < N) return AWQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return AWQ_OK;
+  if (!x || !qweight || !scales || !zeros || !y) return AWQ_ERR_NULL;
+  if (K > AWQ_MAX_K) return AWQ_ERR_UNSUPPORTED;
+  if (ldx % 8 != 0 || !aligned16(x) || !aligned16(qweight) || (inv_s && !aligned16(inv_s)))
+    return AWQ_ERR_ALIGN;
+  const size_t need = awq::gemm_ws_bytes(M, N, K);
+  if (need && (!ws || ws_bytes < need || !aligned256(ws))) return AWQ_ERR_WORKSPACE;
+  return from_hip(awq::launch_w4a16(x, (int)xdt, M, K, ldx, (const uint32_t*)qweight, scales,
+                                    zeros, N, inv_s, y, (int)ydt, ldy, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

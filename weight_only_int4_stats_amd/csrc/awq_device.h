@@ -1,0 +1,112 @@
+// Device-side helpers shared by the gfx950 kernels of the AWQ hot path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awqk {
+
+constexpr int kGroup = 128;           // input channels per quantization group
+constexpr int kWave = 64;             // CDNA wavefront width
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Element type tags: 0 = fp16, 1 = bf16 (same values as awq_dtype).
+enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
+  return (float)h;
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+template <int DT>
+__device__ __forceinline__ float to_f32(uint32_t bits16) {
+  if constexpr (DT == DT_F16) return f16_to_f32(bits16);
+  else return bf16_to_f32(bits16);
+}
+// The low / high 16-bit element of a 32-bit word as float.
+template <int DT>
+__device__ __forceinline__ float lo_f32(uint32_t w) {
+  if constexpr (DT == DT_F16) return f16_to_f32(w & 0xFFFFu);
+  else return __uint_as_float(w << 16);
+}
+template <int DT>
+__device__ __forceinline__ float hi_f32(uint32_t w) {
+  if constexpr (DT == DT_F16) return f16_to_f32(w >> 16);
+  else return __uint_as_float(w & 0xFFFF0000u);
+}
+
+// Round-to-nearest-even conversions to 16-bit storage.
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t from_f32(float f) {
+  if constexpr (DT == DT_F16) return f32_to_f16_bits(f);
+  else return f32_to_bf16_bits(f);
+}
+
+// Smallest fp16 >= d for finite d > 0 (round toward +inf), as bits.  For a
+// positive fp16 the next larger value is the next bit pattern (0x7BFF + 1 is
+// +inf, matching IEEE nextUp).
+__device__ __forceinline__ uint32_t f16_round_up_bits(float d) {
+  _Float16 h = (_Float16)d;
+  uint32_t b = __builtin_bit_cast(uint16_t, h);
+  if ((float)h < d) b += 1u;
+  return b;
+}
+
+// Integer zero point and step of one group, shared by the quantizer and the
+// search's error generator so both score and store the same grid.
+struct GroupGrid {
+  float D;          // step as float (fp16 value)
+  float z;          // zero point 0..15 as float
+  float d;          // step before rounding
+  uint32_t step_bits;
+};
+
+__device__ __forceinline__ GroupGrid group_grid(float mn, float mx) {
+  GroupGrid g;
+  const float lo = fminf(mn, 0.0f);
+  const float hi = fmaxf(mx, 0.0f);
+  g.d = (hi - lo) / 15.0f;                            // IEEE division
+  g.step_bits = f16_round_up_bits(fmaxf(g.d, 0x1p-24f));
+  g.D = f16_to_f32(g.step_bits);
+  g.z = fminf(fmaxf(rintf(-lo / g.D), 0.0f), 15.0f);
+  return g;
+}
+
+__device__ __forceinline__ float quant_code(float wp, const GroupGrid& g) {
+  return fminf(fmaxf(rintf(wp / g.D) + g.z, 0.0f), 15.0f);
+}
+
+// Min / max across the 16 lanes of an aligned 16-lane segment.
+__device__ __forceinline__ void seg16_minmax(float& mn, float& mx) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+  }
+}
+
+__device__ __forceinline__ u32x4 ldg128(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Streaming 128-bit load that is not expected to be reused (packed weights).
+__device__ __forceinline__ u32x4 ldg128_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+}  // namespace awqk

@@ -1,0 +1,37 @@
+// Host-side launchers of the gfx950 kernels (one translation unit each).
+// Every launcher enqueues on `st` and returns hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace awq {
+
+// ---- calibration statistic (mean |x|) -------------------------------------
+size_t act_stats_ws_bytes(int64_t K);
+hipError_t launch_act_stats(const void* x, int dt, int64_t T, int64_t K, int64_t ldx,
+                            float* mean_abs, void* ws, hipStream_t st);
+
+// ---- quantize + pack --------------------------------------------------------
+hipError_t launch_quantize_pack(const void* w, int dt, int64_t N, int64_t K, const float* s,
+                                uint32_t* qw, uint16_t* scales, uint8_t* zeros, float* dbg,
+                                hipStream_t st);
+
+// ---- scale search -----------------------------------------------------------
+size_t search_ws_bytes(int dt, int64_t N, int64_t K, int64_t T, int n_alpha);
+hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void* x, int64_t T,
+                         int64_t ldx, const float* mean_abs, const double* alphas, int n_alpha,
+                         float* s_out, float* inv_s_out, double* loss_out, int32_t* best_out,
+                         void* ws, hipStream_t st);
+
+// ---- W4A16 product ----------------------------------------------------------
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_w4a16(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx,
+                        const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros,
+                        int64_t N, const float* inv_s, void* y, int ydt, int64_t ldy, void* ws,
+                        hipStream_t st);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace awq

@@ -1,0 +1,76 @@
+// Rows of 16-bit activations -> fp16 with an exact power-of-two scale per row.
+#pragma once
+
+#include "awq_device.h"
+
+namespace awqk {
+
+// exact power of two p with max|v| * 2^p < 2^14 (0 when max is 0)
+__device__ __forceinline__ int pow2_exp_for(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e;
+  frexpf(amax, &e);
+  return 14 - e;
+}
+
+// Activation rows -> fp16: y_row = fp16(x_row * r * 2^p_row), p_row from the
+// row's max so the row sits in fp16's normal range.  One block per row.  With
+// PERMUTE each 8-element chunk is stored as (k0,k4,k1,k5,k2,k6,k3,k7), the
+// order in which the packed-nibble unpack yields weight pairs.
+template <int DT, bool HAS_R, bool PERMUTE>
+__global__ __launch_bounds__(256) void k_rows_f16(const uint16_t* __restrict__ src, int64_t K,
+                                                  int64_t ld, const float* __restrict__ r,
+                                                  uint16_t* __restrict__ dst,
+                                                  int* __restrict__ pexp) {
+  const int64_t row = blockIdx.x;
+  const uint16_t* s = src + row * ld;
+  const int64_t nch = K >> 3;
+  auto load8 = [&](int64_t c, float v[8]) {
+    const u32x4 raw = ldg128(s + c * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = lo_f32<DT>(raw[j]);
+      v[2 * j + 1] = hi_f32<DT>(raw[j]);
+    }
+    if constexpr (HAS_R) {
+      const f32x4 r0 = *reinterpret_cast<const f32x4*>(r + c * 8);
+      const f32x4 r1 = *reinterpret_cast<const f32x4*>(r + c * 8 + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] *= r0[j];
+        v[4 + j] *= r1[j];
+      }
+    }
+  };
+  float amax = 0.0f;
+  for (int64_t c = threadIdx.x; c < nch; c += 256) {
+    float v[8];
+    load8(c, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  const int p = pow2_exp_for(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+  if (threadIdx.x == 0) pexp[row] = p;
+  uint16_t* d = dst + row * K;
+  for (int64_t c = threadIdx.x; c < nch; c += 256) {
+    float v[8];
+    load8(c, v);
+    uint32_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = f32_to_f16_bits(ldexpf(v[j], p));
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (PERMUTE) o[j] = h[j] | (h[j + 4] << 16);
+      else o[j] = h[2 * j] | (h[2 * j + 1] << 16);
+    }
+    *reinterpret_cast<u32x4*>(d + c * 8) = o;
+  }
+}
+
+}  // namespace awqk

@@ -1,0 +1,699 @@
+// Fused W4A16 product ("AWQ > Benefits and Practical Considerations": the
+// dequantization unpacks 4-bit integers, applies a group scale and zero point
+// and optionally the per-channel inverse scale, fused with the matrix
+// multiply so the fp16 weight matrix is never materialised).
+//
+//   y[m][n] = sum_k step[n][g(k)] * (q[n][k] - z[n][g(k)]) * x[m][k] * r[k]
+//
+// Two kernels:
+//
+// * k_gemv (M <= 8): bandwidth-bound split-K GEMV.  A lane owns a fixed
+//   128-bit chunk of every row (32 codes = a quarter group), so its slice of
+//   x stays in registers for all rows; a wave covers 64 consecutive chunks
+//   (2048 codes) of a row, a block's waves cover the row's K slices, and the
+//   block walks a tile of rows with all of its 128-bit weight loads in flight.
+//   Dequantization is exact and cheap: the nibble pair (q_j, q_j+4) of a word
+//   becomes two fp16 values 1024 + q by OR-ing the exponent bits of 1024 into
+//   them; a packed fp16 dot product with the matching x pair accumulates in
+//   fp32, and the group epilogue subtracts (1024 + z) * sum(x) and applies the
+//   step.  The lane's x slice is fp16: as given for fp16 input, otherwise
+//   (bf16 input or a 1/s factor) x * r is scaled by an exact power of two per
+//   lane and rounded to fp16 once.  Partial sums are reduced across lanes and
+//   waves through LDS in a fixed order.
+//
+// * k_gemm (M > 8): fp16 matrix-core GEMM on 128x128 output tiles, one
+//   128-wide group per K step.  A pre-pass rounds each activation row x * r,
+//   scaled by an exact power of two, to fp16 (exact for bf16 input without
+//   1/s) in the order the nibble unpack produces; a second pre-pass picks a
+//   power of two per weight row so that step * 15 stays inside fp16.  Each
+//   lane dequantizes its packed word of the B fragment to step * (q - z)
+//   rounded once to fp16 and feeds v_mfma_f32_32x32x16_f16; the epilogue
+//   undoes both powers of two exactly.
+#include "awq_device.h"
+#include "awq_internal.h"
+#include "k_rows_f16.h"
+
+namespace awqk {
+
+// ===========================================================================
+// GEMV
+// ===========================================================================
+constexpr int kGvVals = 16;      // partial sums per lane per block (units x M)
+constexpr int64_t kGemvMaxK = 30720;   // 15 waves of 64 chunks: reduction buffers stay in 64 KB LDS
+constexpr int64_t kGemvMaxK8 = 16384;  // 8 waves for 2..8 activation rows
+
+constexpr uint32_t kMagic1024 = 0x64006400u;   // fp16 1024.0 in both halves
+constexpr float kOff1024 = 1024.0f;
+
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+template <int YDT>
+__device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
+  if constexpr (YDT == DT_F32) reinterpret_cast<float*>(y)[idx] = v;
+  else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)from_f32<YDT>(v);
+}
+
+// Row units (RPS rows side by side) whose weights a lane loads up front, per
+// activation-row count.  More units put more bytes in flight per wave; the
+// activation registers limit them for larger MT.
+template <int MT>
+constexpr int gemv_units() { return MT <= 2 ? 8 : 4; }
+
+// LPR: lanes per row segment (16, 32 or 64); MT: activation rows (1, 2, 4, 8).
+// Loads are issued in the order activations, 1/s, weights / steps / zero
+// points, all branch-free (out-of-range rows and chunks read a valid address
+// and are masked afterwards), so every load of the block is in flight before
+// the first wait; the activation slice is converted while the weights arrive.
+template <int DT, int YDT, int LPR, int MT, bool HAS_R>
+__global__ __launch_bounds__(LPR < 64 ? 64 : (MT == 1 ? 1024 : 512)) void k_gemv(
+    const uint16_t* __restrict__ x, int M, int64_t K, int64_t ldx, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N,
+    const float* __restrict__ r, void* __restrict__ y, int64_t ldy) {
+  constexpr int RPS = 64 / LPR;                // rows processed side by side per wave
+  constexpr int UL = gemv_units<MT>();         // row units loaded per lane
+  constexpr int UP = kGvVals / MT;             // row units per reduction pass
+  constexpr int NPASS = (UL + UP - 1) / UP;
+  constexpr int ROWS = UL * RPS;               // rows per block
+  constexpr int NOUT = kGvVals * RPS;          // outputs per reduction pass
+  constexpr bool kScaled = (DT == DT_BF16) || HAS_R;
+
+  extern __shared__ float red[];               // [nw][kGvVals][64] then [nw][NOUT]
+  const int nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int sub = lane / LPR;
+  const int cl = lane % LPR;
+  const int64_t CH = K >> 5;                   // 16-byte chunks per row
+  const int64_t ch = (int64_t)wv * LPR + cl;
+  const bool valid = ch < CH;
+  const int64_t chc = valid ? ch : 0;          // in-bounds chunk for masked lanes
+  const int64_t G = K / kGroup;
+  const int64_t gc = chc >> 2;
+  const int64_t row0 = (int64_t)blockIdx.x * ROWS;
+
+  // ---- 1. activation (and 1/s) loads
+  u32x4 xraw[MT][4];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int cw = 0; cw < 4; ++cw)
+      xraw[m][cw] = ldg128(x + (int64_t)(m < M ? m : 0) * ldx + chc * 32 + cw * 8);
+  f32x4 rr[8];
+  if constexpr (HAS_R) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rr[i] = *reinterpret_cast<const f32x4*>(r + chc * 32 + i * 4);
+  }
+
+  // ---- 2. weights, steps, zero points of all the block's rows
+  u32x4 wq[UL];
+  uint32_t sraw[UL], zraw[UL];
+#pragma unroll
+  for (int u = 0; u < UL; ++u) {
+    int64_t row = row0 + u * RPS + sub;
+    row = row < N ? row : N - 1;
+    wq[u] = ldg128_stream(qw + row * (K >> 3) + chc * 4);
+    sraw[u] = scales[row * G + gc];
+    zraw[u] = zeros[row * G + gc];
+  }
+  // keep every load above this point: nothing below may be hoisted between
+  // them, so all of them are in flight before the first wait
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. activation slice -> fp16 pairs (x_j, x_j+4) per word, sum, scale
+  uint32_t xp[MT][16];
+  float xs[MT], xscale[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    uint32_t h[32];
+    xscale[m] = 1.0f;
+    if constexpr (kScaled) {
+      float v[32];
+#pragma unroll
+      for (int cw = 0; cw < 4; ++cw)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[cw * 8 + 2 * j] = lo_f32<DT>(xraw[m][cw][j]);
+          v[cw * 8 + 2 * j + 1] = hi_f32<DT>(xraw[m][cw][j]);
+        }
+      if constexpr (HAS_R) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] *= rr[i >> 2][i & 3];
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      const int p = pow2_exp_for(amax);
+      xscale[m] = ldexpf(1.0f, -p);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) h[i] = f32_to_f16_bits(ldexpf(v[i], p));
+    } else {
+#pragma unroll
+      for (int cw = 0; cw < 4; ++cw)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h[cw * 8 + 2 * j] = xraw[m][cw][j] & 0xFFFFu;
+          h[cw * 8 + 2 * j + 1] = xraw[m][cw][j] >> 16;
+        }
+    }
+    const bool live = valid && m < M;
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sum += f16_to_f32(h[i]);
+    xs[m] = live ? sum : 0.0f;
+#pragma unroll
+    for (int cw = 0; cw < 4; ++cw)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xp[m][cw * 4 + j] = live ? (h[cw * 8 + j] | (h[cw * 8 + j + 4] << 16)) : 0u;
+  }
+
+  // ---- 4. dot products and the reduction, one pass of UP row units at a time
+  constexpr int LPO = 64 / NOUT;               // lanes per output in the LDS reduction: 4, 2 or 1
+  float* rw = red + wv * (kGvVals * 64);
+  float* r2 = red + nw * (kGvVals * 64);
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
+    float val[kGvVals];
+#pragma unroll
+    for (int uu = 0; uu < UP; ++uu) {
+      const int u = pass * UP + uu;
+      if (u >= UL) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) val[uu * MT + m] = 0.0f;
+        continue;
+      }
+      const bool rowok = valid && (row0 + u * RPS + sub) < N;
+      const float dz = rowok ? f16_to_f32(sraw[u]) : 0.0f;
+      const float cz = kOff1024 + (float)zraw[u];
+      float P[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) P[m] = 0.0f;
+#pragma unroll
+      for (int cw = 0; cw < 4; ++cw) {
+        const uint32_t wword = wq[u][cw];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t pr = ((wword >> (4 * j)) & 0x000F000Fu) | kMagic1024;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) P[m] = dot2h(pr, xp[m][cw * 4 + j], P[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        val[uu * MT + m] = (dz * __builtin_fmaf(-cz, xs[m], P[m])) * xscale[m];
+    }
+
+    if (pass > 0) __syncthreads();               // the previous pass has read its LDS
+#pragma unroll
+    for (int v = 0; v < kGvVals; ++v) rw[v * 64 + lane] = val[v];
+    __syncthreads();
+    {
+      const int o = lane / LPO;
+      const int jj = lane % LPO;
+      const int v = o / RPS;
+      const int osub = o % RPS;
+      const float* src = rw + v * 64 + osub * LPR + jj * 16;
+      float t = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t += src[i];
+#pragma unroll
+      for (int off = LPO / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+      if (jj == 0) r2[wv * NOUT + o] = t;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < NOUT) {
+      const int oo = threadIdx.x;
+      float tot = 0.0f;
+      for (int w = 0; w < nw; ++w) tot += r2[w * NOUT + oo];
+      const int vv = oo / RPS;
+      const int uu = vv / MT;
+      const int m = vv % MT;
+      const int u = pass * UP + uu;
+      const int64_t row = row0 + (int64_t)u * RPS + (oo % RPS);
+      if (u < UL && row < N && m < M) store_y<YDT>(y, (int64_t)m * ldy + row, tot);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Batch-1 GEMV.  The block's waves are (K slice ks, row group rg): a lane owns
+// one 128-bit chunk (32 codes) of K slice ks and walks the UL rows of its
+// group.  The activation x * r is turned into fp16 once per block and staged
+// in LDS (one thread per 8 consecutive k), so the 1/s and x reads are shared
+// by every row of the block; those loads are issued before the weight loads
+// (vector memory counters retire in order) so staging does not wait for the
+// weights.  Each packed word is unpacked with one shift and four and-or
+// operations: nibbles 0/4 and 2/6 become fp16 1024 + q, nibbles 1/5 and 3/7
+// (still 4 bits up) become 1024 + 16 q; the factor 16 and the offsets are
+// removed once per chunk with precomputed sums of the staged activations.
+// Lanes reduce each row with a butterfly of shuffles; K slices combine
+// through LDS in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kG1Units = 4;          // rows per wave
+constexpr int kG1MaxStage = 4;       // 8-element activation chunks staged per thread (K/8 <= 4 x threads)
+constexpr int64_t kG1MaxK = 24576;   // staged activations + sums fit 64 KB of LDS
+
+template <int DT, int YDT, bool HAS_R>
+__global__ __launch_bounds__(1024) void k_gemv1(
+    const uint16_t* __restrict__ x, int64_t K, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N,
+    const float* __restrict__ r, void* __restrict__ y, int nks) {
+  constexpr int UL = kG1Units;
+  extern __shared__ uint32_t lds1[];
+  const int nwv = blockDim.x >> 6;
+  const int nrg = nwv / nks;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int ks = wv % nks;
+  const int rg = wv / nks;
+  const int64_t CH = K >> 5;
+  const int64_t ch = (int64_t)ks * 64 + lane;
+  const bool valid = ch < CH;
+  const int64_t chc = valid ? ch : 0;
+  const int64_t G = K / kGroup;
+  const int64_t gc = chc >> 2;
+  const int64_t rowsb = (int64_t)nrg * UL;
+  const int64_t row0 = (int64_t)blockIdx.x * rowsb + (int64_t)rg * UL;
+  uint32_t* xpair = lds1;                                        // [CH][16] fp16 pairs
+  float* xsum = reinterpret_cast<float*>(lds1 + CH * 16);        // [CH][4]: K0, S, 2^-p, -
+  float* part = xsum + CH * 4;                                   // [nks][rowsb]
+
+  // ---- 0. activation (and 1/s) loads for staging, issued first
+  const int64_t n8 = K >> 3;
+  const int64_t n8q = (n8 + 3) & ~int64_t(3);                    // whole quads of threads
+  u32x4 sx[kG1MaxStage];
+  f32x4 sr0[kG1MaxStage], sr1[kG1MaxStage];
+#pragma unroll
+  for (int i = 0; i < kG1MaxStage; ++i) {
+    const int64_t c8 = threadIdx.x + (int64_t)i * blockDim.x;
+    const int64_t c8c = c8 < n8 ? c8 : 0;
+    if (c8 < n8q) {
+      sx[i] = ldg128(x + c8c * 8);
+      if constexpr (HAS_R) {
+        sr0[i] = *reinterpret_cast<const f32x4*>(r + c8c * 8);
+        sr1[i] = *reinterpret_cast<const f32x4*>(r + c8c * 8 + 4);
+      }
+    }
+  }
+  // ---- 1. weights, steps, zero points (branch-free: rows clamped, masked later)
+  u32x4 wq[UL];
+  uint32_t sraw[UL], zraw[UL];
+#pragma unroll
+  for (int u = 0; u < UL; ++u) {
+    int64_t row = row0 + u;
+    row = row < N ? row : N - 1;
+    wq[u] = ldg128_stream(qw + row * (K >> 3) + chc * 4);
+    sraw[u] = scales[row * G + gc];
+    zraw[u] = zeros[row * G + gc];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. stage fp16(x r 2^p) per 32-chunk (4 threads per chunk)
+#pragma unroll
+  for (int i = 0; i < kG1MaxStage; ++i) {
+    const int64_t c8 = threadIdx.x + (int64_t)i * blockDim.x;
+    if (c8 < n8q) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = lo_f32<DT>(sx[i][j]);
+        v[2 * j + 1] = hi_f32<DT>(sx[i][j]);
+      }
+      if constexpr (HAS_R) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] *= sr0[i][j];
+          v[4 + j] *= sr1[i][j];
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      int p = 0;
+      if constexpr (DT == DT_BF16 || HAS_R) p = pow2_exp_for(amax);
+      uint32_t h[8];
+      float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h[j] = (DT == DT_F16 && !HAS_R) ? (j & 1 ? sx[i][j >> 1] >> 16 : sx[i][j >> 1] & 0xFFFFu)
+                                        : f32_to_f16_bits(ldexpf(v[j], p));
+        if (j & 1) sb += f16_to_f32(h[j]);
+        else sa += f16_to_f32(h[j]);
+      }
+      sa += __shfl_xor(sa, 1);
+      sa += __shfl_xor(sa, 2);
+      sb += __shfl_xor(sb, 1);
+      sb += __shfl_xor(sb, 2);
+      if (c8 < n8) {
+        u32x4 o;
+        o[0] = h[0] | (h[4] << 16);   // pairs with nibbles 0 / 4
+        o[1] = h[2] | (h[6] << 16);   // nibbles 2 / 6 (word >> 8)
+        o[2] = h[1] | (h[5] << 16);   // nibbles 1 / 5, held 16 q
+        o[3] = h[3] | (h[7] << 16);   // nibbles 3 / 7, held 16 q
+        *reinterpret_cast<u32x4*>(xpair + c8 * 4) = o;
+        if ((c8 & 3) == 0) {
+          f32x4 c;
+          c[0] = 1024.0f * sa + 64.0f * sb;
+          c[1] = sa + sb;
+          c[2] = ldexpf(1.0f, -p);
+          c[3] = 0.0f;
+          *reinterpret_cast<f32x4*>(xsum + (c8 >> 2) * 4) = c;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  u32x4 xr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xr[i] = *reinterpret_cast<const u32x4*>(xpair + chc * 16 + i * 4);
+  const f32x4 xc = *reinterpret_cast<const f32x4*>(xsum + chc * 4);
+
+  // ---- 3. dot products
+  float val[UL];
+#pragma unroll
+  for (int u = 0; u < UL; ++u) {
+    const bool rowok = valid && (row0 + u) < N;
+    const float dz = rowok ? f16_to_f32(sraw[u]) * xc[2] : 0.0f;
+    float Pa = 0.0f, Pb = 0.0f;
+#pragma unroll
+    for (int cw = 0; cw < 4; ++cw) {
+      const uint32_t w = wq[u][cw];
+      const uint32_t w8 = w >> 8;
+      Pa = dot2h((w & 0x000F000Fu) | kMagic1024, xr[cw][0], Pa);
+      Pa = dot2h((w8 & 0x000F000Fu) | kMagic1024, xr[cw][1], Pa);
+      Pb = dot2h((w & 0x00F000F0u) | kMagic1024, xr[cw][2], Pb);
+      Pb = dot2h((w8 & 0x00F000F0u) | kMagic1024, xr[cw][3], Pb);
+    }
+    const float P = __builtin_fmaf(Pb, 0.0625f, Pa) - __builtin_fmaf((float)zraw[u], xc[1], xc[0]);
+    val[u] = dz * P;
+  }
+  // ---- 4. butterfly reduce-scatter over the wave (row index = top lane bits), then K slices
+  constexpr int LB = 2;                          // log2(UL)
+#pragma unroll
+  for (int off = 32, n = UL; off >= 1; off >>= 1) {
+    if (n > 1) {
+      const bool upper = (lane & off) != 0;
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) {
+        const float send = upper ? val[i] : val[i + n / 2];
+        const float keep = upper ? val[i + n / 2] : val[i];
+        val[i] = keep + __shfl_xor(send, off);
+      }
+      n >>= 1;
+    } else {
+      val[0] += __shfl_xor(val[0], off);
+    }
+  }
+  if ((lane & ((64 >> LB) - 1)) == 0) part[ks * rowsb + rg * UL + (lane >> (6 - LB))] = val[0];
+  __syncthreads();
+  for (int t = threadIdx.x; t < rowsb; t += blockDim.x) {
+    float tot = 0.0f;
+    for (int k2 = 0; k2 < nks; ++k2) tot += part[k2 * rowsb + t];
+    const int64_t row = (int64_t)blockIdx.x * rowsb + t;
+    if (row < N) store_y<YDT>(y, row, tot);
+  }
+}
+
+template <int DT, int YDT, bool HAS_R>
+hipError_t gemv1_dispatch(const uint16_t* x, int64_t K, const uint32_t* qw, const uint16_t* scales,
+                          const uint8_t* zeros, int64_t N, const float* r, void* y, hipStream_t st) {
+  const int64_t CH = K >> 5;
+  const int nks = (int)((CH + 63) / 64);
+  int nrg = nks >= 8 ? 1 : 8 / nks;
+  if (nks * nrg > 16) nrg = 16 / nks;
+  const int64_t rows = (int64_t)nrg * kG1Units;
+  const int64_t threads = (int64_t)nks * nrg * 64;
+  if (((K >> 3) + 3) / 4 * 4 > kG1MaxStage * threads) return hipErrorInvalidValue;
+  const size_t lds = (size_t)CH * 16 * 4 + (size_t)CH * 4 * 4 + (size_t)nks * rows * 4;
+  hipLaunchKernelGGL((k_gemv1<DT, YDT, HAS_R>), dim3((unsigned)((N + rows - 1) / rows)),
+                     dim3((unsigned)(nks * nrg * 64)), lds, st, x, K, qw, scales, zeros, N, r, y, nks);
+  return hipGetLastError();
+}
+
+// ===========================================================================
+// matrix-core GEMM
+// ===========================================================================
+constexpr int kGT = 128;               // output tile edge (m and n)
+constexpr int kGLd = kGroup + 8;       // LDS row stride of the x tile (16-bit elements)
+
+// Per weight row n: e_n with 15 * max_g step[n][g] * 2^e_n < 2^16, so that
+// step * 2^e_n * (q - z) is finite in fp16.
+__global__ void k_step_exp(const uint16_t* __restrict__ scales, int64_t N, int64_t G,
+                           int* __restrict__ eexp) {
+  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float mx = 0.0f;
+  for (int64_t g = 0; g < G; ++g) mx = fmaxf(mx, f16_to_f32(scales[n * G + g]));
+  int e = 0;
+  if (mx > 0.0f) {
+    int ex;
+    frexpf(mx, &ex);        // mx < 2^ex
+    e = 12 - ex;            // 15 * mx * 2^e < 15 * 2^12 < 65504
+  }
+  eexp[n] = e;
+}
+
+__device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// One packed word (codes of k = 8c + j in bits 4j..4j+3) -> 8 fp16 operands
+// D' * (q - z) in pair order (k_j, k_j+4), j = 0..3; D' = step * 2^e_n.
+__device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 dd, f16x2 nz) {
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t pr = ((w >> (4 * j)) & 0x000F000Fu) | kMagic1024;
+    const f16x2 qz = __builtin_bit_cast(f16x2, pr) + nz;      // q - z, exact
+    out[j] = __builtin_bit_cast(uint32_t, qz * dd);            // rounded once
+  }
+  return out;
+}
+
+template <int YDT>
+__global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ xq, int64_t M, int64_t K,
+                                              const int* __restrict__ pm,
+                                              const uint32_t* __restrict__ qw,
+                                              const uint16_t* __restrict__ scales,
+                                              const uint8_t* __restrict__ zeros,
+                                              const int* __restrict__ en, int64_t N,
+                                              void* __restrict__ y, int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[kGT * kGLd];
+  __shared__ __attribute__((aligned(16))) uint32_t Bq[kGT * 16];
+  __shared__ uint32_t Bd[kGT];     // D' in both fp16 halves
+  __shared__ uint32_t Bz[kGT];     // -(1024 + z) in both fp16 halves
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int64_t m0 = (int64_t)blockIdx.y * kGT;
+  const int64_t n0 = (int64_t)blockIdx.x * kGT;
+  const int64_t G = K / kGroup;
+  const int ecol = (tid < kGT && n0 + tid < N) ? en[n0 + tid] : 0;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  for (int64_t g = 0; g < G; ++g) {
+    const int64_t k0 = g * kGroup;
+    // x tile: 128 rows x 128 k = 2048 chunks of 8 fp16, 8 per thread
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int chn = tid + 256 * i;
+      const int rr = chn >> 4;
+      const int cc = (chn & 15) * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (m0 + rr < M) v = ldg128(xq + (m0 + rr) * K + k0 + cc);
+      *reinterpret_cast<u32x4*>(&As[rr * kGLd + cc]) = v;
+    }
+    // packed words of the group: 128 rows x 16 words = 512 chunks of 4 words
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int chn = tid + 256 * i;
+      const int rr = chn >> 2;
+      const int cc = (chn & 3) * 4;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (n0 + rr < N) v = ldg128_stream(qw + (n0 + rr) * (K >> 3) + g * 16 + cc);
+      *reinterpret_cast<u32x4*>(&Bq[rr * 16 + cc]) = v;
+    }
+    if (tid < kGT) {
+      uint32_t dh = 0u, zh = 0u;
+      if (n0 + tid < N) {
+        dh = f32_to_f16_bits(ldexpf(f16_to_f32(scales[(n0 + tid) * G + g]), ecol));
+        zh = f32_to_f16_bits(-(kOff1024 + (float)zeros[(n0 + tid) * G + g]));
+      }
+      Bd[tid] = dh | (dh << 16);
+      Bz[tid] = zh | (zh << 16);
+    }
+    __syncthreads();
+
+    f16x2 dd[2], nz[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int col = wn * 64 + nb * 32 + (lane & 31);
+      dd[nb] = __builtin_bit_cast(f16x2, Bd[col]);
+      nz[nb] = __builtin_bit_cast(f16x2, Bz[col]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int kw = ks * 2 + (lane >> 5);        // word index within the group
+      u32x4 a[2], b[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        a[mb] = *reinterpret_cast<const u32x4*>(&As[(wm * 64 + mb * 32 + (lane & 31)) * kGLd + kw * 8]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = wn * 64 + nb * 32 + (lane & 31);
+        b[nb] = dequant_word_f16(Bq[col * 16 + kw], dd[nb], nz[nb]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32h(a[mb], b[nb], acc[mb][nb]);
+    }
+    __syncthreads();
+  }
+
+  // 32x32 accumulator layout: column = lane % 32, row = 8 (v / 4) + 4 (lane / 32) + v % 4
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int64_t n = n0 + wn * 64 + nb * 32 + (lane & 31);
+    if (n >= N) continue;
+    const int e = en[n];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (m < M) store_y<YDT>(y, m * ldy + n, ldexpf(acc[mb][nb][v], -(pm[m] + e)));
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int DT, int YDT, bool HAS_R>
+hipError_t gemv_dispatch(const uint16_t* x, int M, int64_t K, int64_t ldx, const uint32_t* qw,
+                         const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
+                         void* y, int64_t ldy, hipStream_t st) {
+  const int64_t CH = K >> 5;
+  const int lpr = CH >= 64 ? 64 : (CH > 16 ? 32 : 16);
+  const int64_t nw = (CH + lpr - 1) / lpr;   // <= 15 (K <= kGemvMaxK)
+  const int rps = 64 / lpr;
+  const int mt = M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8));
+  const int rows = (mt <= 2 ? gemv_units<1>() : gemv_units<8>()) * rps;
+  const dim3 grid((unsigned)((N + rows - 1) / rows));
+  const dim3 block((unsigned)(nw * 64));
+  const size_t lds = (size_t)nw * kGvVals * 64 * 4 + (size_t)nw * kGvVals * rps * 4;
+#define AWQ_GV(LPR, MT)                                                                        \
+  hipLaunchKernelGGL((k_gemv<DT, YDT, LPR, MT, HAS_R>), grid, block, lds, st, x, M, K, ldx, qw, \
+                     scales, zeros, N, r, y, ldy)
+#define AWQ_GV_M(LPR)            \
+  switch (mt) {                  \
+    case 1: AWQ_GV(LPR, 1); break; \
+    case 2: AWQ_GV(LPR, 2); break; \
+    case 4: AWQ_GV(LPR, 4); break; \
+    default: AWQ_GV(LPR, 8); break; \
+  }
+  if (lpr == 64) { AWQ_GV_M(64) }
+  else if (lpr == 32) { AWQ_GV_M(32) }
+  else { AWQ_GV_M(16) }
+#undef AWQ_GV_M
+#undef AWQ_GV
+  return hipGetLastError();
+}
+
+struct GemmWs {
+  uint16_t* xq;
+  int* pm;
+  int* en;
+  size_t bytes;
+};
+
+inline GemmWs gemm_ws(void* ws, int64_t M, int64_t N, int64_t K) {
+  GemmWs w{};
+  char* base = (char*)ws;
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    char* p = base ? base + off : nullptr;
+    off += awq::align_up(b, 256);
+    return p;
+  };
+  w.xq = (uint16_t*)take((size_t)M * K * 2);
+  w.pm = (int*)take((size_t)M * 4);
+  w.en = (int*)take((size_t)N * 4);
+  w.bytes = off;
+  return w;
+}
+
+inline bool use_gemv(int64_t M, int64_t K) {
+  return (M == 1 && K <= kGemvMaxK) || (M <= 8 && K <= kGemvMaxK8);
+}
+
+template <int DT, int YDT, bool HAS_R>
+hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
+                         const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
+                         void* y, int64_t ldy, void* ws, hipStream_t st) {
+  const GemmWs w = gemm_ws(ws, M, N, K);
+  hipLaunchKernelGGL((k_rows_f16<DT, HAS_R, true>), dim3((unsigned)M), dim3(256), 0, st, x, K, ldx,
+                     r, w.xq, w.pm);
+  hipLaunchKernelGGL(k_step_exp, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, scales, N,
+                     K / kGroup, w.en);
+  const dim3 grid((unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT));
+  hipLaunchKernelGGL((k_gemm<YDT>), grid, dim3(256), 0, st, w.xq, M, K, w.pm, qw, scales, zeros,
+                     w.en, N, y, ldy);
+  return hipGetLastError();
+}
+
+template <int DT, int YDT>
+hipError_t w4a16_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
+                          const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
+                          void* y, int64_t ldy, void* ws, hipStream_t st) {
+  if (M == 1 && K <= kG1MaxK) {
+    if (r) return gemv1_dispatch<DT, YDT, true>(x, K, qw, scales, zeros, N, r, y, st);
+    return gemv1_dispatch<DT, YDT, false>(x, K, qw, scales, zeros, N, r, y, st);
+  }
+  if (use_gemv(M, K)) {
+    if (r) return gemv_dispatch<DT, YDT, true>(x, (int)M, K, ldx, qw, scales, zeros, N, r, y, ldy, st);
+    return gemv_dispatch<DT, YDT, false>(x, (int)M, K, ldx, qw, scales, zeros, N, r, y, ldy, st);
+  }
+  if (r) return gemm_dispatch<DT, YDT, true>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, ws, st);
+  return gemm_dispatch<DT, YDT, false>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, ws, st);
+}
+
+}  // namespace awqk
+
+namespace awq {
+
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || awqk::use_gemv(M, K)) return 0;
+  return awqk::gemm_ws(nullptr, M, N, K).bytes;
+}
+
+hipError_t launch_w4a16(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx,
+                        const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros,
+                        int64_t N, const float* inv_s, void* y, int ydt, int64_t ldy, void* ws,
+                        hipStream_t st) {
+  using namespace awqk;
+  const uint16_t* xp = (const uint16_t*)x;
+  if (xdt == DT_F16) {
+    if (ydt == DT_F16) return w4a16_dispatch<DT_F16, DT_F16>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
+    if (ydt == DT_BF16) return w4a16_dispatch<DT_F16, DT_BF16>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
+    return w4a16_dispatch<DT_F16, DT_F32>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
+  }
+  if (ydt == DT_F16) return w4a16_dispatch<DT_BF16, DT_F16>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
+  if (ydt == DT_BF16) return w4a16_dispatch<DT_BF16, DT_BF16>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
+  return w4a16_dispatch<DT_BF16, DT_F32>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
+}
+
+}  // namespace awq
