@@ -134,15 +134,24 @@ def test_gemm_parity(M, N, K, dtype, ydt, with_r):
 def test_product_special_cases():
     """q == z gives 0; a one-hot x picks the dequantized column.  The GEMV
     accumulates exact int4 x activation products, so the one-hot column is
-    exact there and q == z leaves only the rounding of the zero-point sum; the
-    matrix-core path rounds step * (q - z) to the operand type, so it is exact
-    for q == z and, with power-of-two steps, for one-hot x."""
+    exact there and q == z leaves only the rounding of the zero-point sum.  The
+    matrix-core path forms each operand as one fused step * q - fp16(step * z),
+    so q == z leaves the rounding of fp16(step * z) (at most 2^-11 of it) and,
+    with power-of-two steps (step * z exact in fp16), everything is exact."""
     N, K = 200, 1024
     words, step, z = _random_packed(N, K, 5)
     qz = np.repeat(z, 128, axis=1)
     x = _act(40, K, F16, 6)
     y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(O.pack_codes(qz))),
                            gpu(torch.from_numpy(step)), gpu(torch.from_numpy(z)),
+                           out_dtype=torch.float32)
+    zd = step.astype(np.float64) * z.astype(np.float64)                      # [N, G]
+    bound = 2.0 ** -11 * np.abs(f32(x)).astype(np.float64).reshape(40, K // 128, 128).sum(-1) @ zd.T
+    assert np.all(np.abs(f32(y)) <= bound * (1 + 1e-3) + 1e-30)
+    pow2_step = np.ldexp(np.float16(1), np.random.Generator(np.random.PCG64(9)).integers(
+        -12, -5, step.shape)).astype(np.float16)
+    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(O.pack_codes(qz))),
+                           gpu(torch.from_numpy(pow2_step)), gpu(torch.from_numpy(z)),
                            out_dtype=torch.float32)
     assert torch.count_nonzero(y).item() == 0
     y1 = awq.awq_w4a16_gemm(gpu(x[:1]), gpu(torch.from_numpy(O.pack_codes(qz))),

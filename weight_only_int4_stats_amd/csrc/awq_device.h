@@ -20,6 +20,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Element type tags: 0 = fp16, 1 = bf16 (same values as awq_dtype).
 enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
 
+// Two fp16 from a 32-bit pattern.  Takes the value: a vector element such as
+// v[1] must not be handed to __builtin_bit_cast directly (this compiler then
+// reads element 0 of the vector).
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
   _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
   return (float)h;

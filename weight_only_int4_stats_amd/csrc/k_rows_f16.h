@@ -15,7 +15,7 @@ __device__ __forceinline__ int pow2_exp_for(float amax) {
 
 // Activation rows -> fp16: y_row = fp16(x_row * r * 2^p_row), p_row from the
 // row's max so the row sits in fp16's normal range.  One block per row.  With
-// PERMUTE each 8-element chunk is stored as (k0,k4,k1,k5,k2,k6,k3,k7), the
+// PERMUTE each 8-element chunk is stored as (k0,k4,k2,k6,k1,k5,k3,k7), the
 // order in which the packed-nibble unpack yields weight pairs.
 template <int DT, bool HAS_R, bool PERMUTE>
 __global__ __launch_bounds__(256) void k_rows_f16(const uint16_t* __restrict__ src, int64_t K,
@@ -64,10 +64,14 @@ __global__ __launch_bounds__(256) void k_rows_f16(const uint16_t* __restrict__ s
 #pragma unroll
     for (int j = 0; j < 8; ++j) h[j] = f32_to_f16_bits(ldexpf(v[j], p));
     u32x4 o;
+    if constexpr (PERMUTE) {
+      o[0] = h[0] | (h[4] << 16);
+      o[1] = h[2] | (h[6] << 16);
+      o[2] = h[1] | (h[5] << 16);
+      o[3] = h[3] | (h[7] << 16);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (PERMUTE) o[j] = h[j] | (h[j + 4] << 16);
-      else o[j] = h[2 * j] | (h[2 * j + 1] << 16);
+      for (int j = 0; j < 4; ++j) o[j] = h[2 * j] | (h[2 * j + 1] << 16);
     }
     *reinterpret_cast<u32x4*>(d + c * 8) = o;
   }

@@ -437,11 +437,9 @@ hipError_t gemv1_dispatch(const uint16_t* x, int64_t K, const uint32_t* qw, cons
 // ===========================================================================
 // matrix-core GEMM
 // ===========================================================================
-constexpr int kGT = 128;               // output tile edge (m and n)
-constexpr int kGLd = kGroup + 8;       // LDS row stride of the x tile (16-bit elements)
 
-// Per weight row n: e_n with 15 * max_g step[n][g] * 2^e_n < 2^16, so that
-// step * 2^e_n * (q - z) is finite in fp16.
+// Per weight row n: e_n with max_g step[n][g] * 2^e_n in [2^-10, 2^-9), so that
+// D' = step 2^e_n times 2^24 is a finite fp16 and D' (q - z) is a normal fp16.
 __global__ void k_step_exp(const uint16_t* __restrict__ scales, int64_t N, int64_t G,
                            int* __restrict__ eexp) {
   const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -452,7 +450,7 @@ __global__ void k_step_exp(const uint16_t* __restrict__ scales, int64_t N, int64
   if (mx > 0.0f) {
     int ex;
     frexpf(mx, &ex);        // mx < 2^ex
-    e = 12 - ex;            // 15 * mx * 2^e < 15 * 2^12 < 65504
+    e = -9 - ex;            // mx * 2^e in [2^-10, 2^-9): D' 2^24 stays finite in fp16
   }
   eexp[n] = e;
 }
@@ -463,105 +461,156 @@ __device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const 
 }
 
 // One packed word (codes of k = 8c + j in bits 4j..4j+3) -> 8 fp16 operands
-// D' * (q - z) in pair order (k_j, k_j+4), j = 0..3; D' = step * 2^e_n.
-__device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 dd, f16x2 nz) {
+// D' (q - z), k order (0,4 | 2,6 | 1,5 | 3,7).  The masked nibbles are read
+// as fp16 subnormals q 2^-24 (nibbles 1/3/5/7 still 4 bits up: q 2^-20); one
+// packed fma with the fp16 constants D' 2^24 (or D' 2^20) and -D' z gives
+// D' q - D' z with one rounding.  Shift, 4 ands and 4 fmas per word.
+__device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 c24, f16x2 c20, f16x2 nzd) {
+  const uint32_t w8 = w >> 8;
   u32x4 out;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t pr = ((w >> (4 * j)) & 0x000F000Fu) | kMagic1024;
-    const f16x2 qz = __builtin_bit_cast(f16x2, pr) + nz;      // q - z, exact
-    out[j] = __builtin_bit_cast(uint32_t, qz * dd);            // rounded once
-  }
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+      __builtin_bit_cast(f16x2, w & 0x000F000Fu), c24, nzd));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+      __builtin_bit_cast(f16x2, w8 & 0x000F000Fu), c24, nzd));
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+      __builtin_bit_cast(f16x2, w & 0x00F000F0u), c20, nzd));
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+      __builtin_bit_cast(f16x2, w8 & 0x00F000F0u), c20, nzd));
   return out;
 }
 
+// 256 x 256 output tile per block of 8 waves (2 along m x 4 along n, each wave
+// 128 x 64 = 4 x 2 blocks of 32 x 32), 64 k per LDS stage, two LDS stages so
+// that the next stage's global loads are in flight during the current
+// stage's matrix-core work (one barrier per stage).
+constexpr int kMT = 256;                // tile rows (m)
+constexpr int kNT = 256;                // tile columns (n)
+constexpr int kBK = 64;                 // k per stage
+constexpr int kALd = kBK + 8;           // x tile row stride (16-bit elements)
+constexpr int kBLd = 12;                // packed-word tile row stride (words; 8 used)
+
 template <int YDT>
-__global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ xq, int64_t M, int64_t K,
+__global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, int64_t M, int64_t K,
                                               const int* __restrict__ pm,
                                               const uint32_t* __restrict__ qw,
                                               const uint16_t* __restrict__ scales,
                                               const uint8_t* __restrict__ zeros,
                                               const int* __restrict__ en, int64_t N,
                                               void* __restrict__ y, int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kGT * kGLd];
-  __shared__ __attribute__((aligned(16))) uint32_t Bq[kGT * 16];
-  __shared__ uint32_t Bd[kGT];     // D' in both fp16 halves
-  __shared__ uint32_t Bz[kGT];     // -(1024 + z) in both fp16 halves
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kMT * kALd];
+  __shared__ __attribute__((aligned(16))) uint32_t Bq[2][kNT * kBLd];
+  __shared__ __attribute__((aligned(16))) uint32_t Bc[2][kNT * 4];   // D'2^24, D'2^20, -D'z (fp16 pairs)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kGT;
-  const int64_t n0 = (int64_t)blockIdx.x * kGT;
+  const int wm = wv >> 2, wn = wv & 3;
+  const int64_t m0 = (int64_t)blockIdx.y * kMT;
+  const int64_t n0 = (int64_t)blockIdx.x * kNT;
   const int64_t G = K / kGroup;
-  const int ecol = (tid < kGT && n0 + tid < N) ? en[n0 + tid] : 0;
+  const int64_t S = K / kBK;
+  const int bcol = tid & 255;                    // column this thread stages (B side)
+  const bool bcol_ok = n0 + bcol < N;
+  const int64_t bcol_c = bcol_ok ? n0 + bcol : 0;
+  const int ecol = bcol_ok ? en[bcol_c] : 0;
 
-  f32x16 acc[2][2];
+  // per-thread source pointers (advanced by k0 each stage)
+  const uint16_t* asrc[4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 512 * i;
+    const int64_t mr = m0 + (c >> 3);
+    asrc[i] = xq + (mr < M ? mr : 0) * K + (c & 7) * 8;
+  }
+  const uint32_t* bsrc = qw + bcol_c * (K >> 3);
+  const uint16_t* ssrc = scales + bcol_c * G;
+  const uint8_t* zsrc = zeros + bcol_c * G;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  for (int64_t g = 0; g < G; ++g) {
-    const int64_t k0 = g * kGroup;
-    // x tile: 128 rows x 128 k = 2048 chunks of 8 fp16, 8 per thread
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int chn = tid + 256 * i;
-      const int rr = chn >> 4;
-      const int cc = (chn & 15) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m0 + rr < M) v = ldg128(xq + (m0 + rr) * K + k0 + cc);
-      *reinterpret_cast<u32x4*>(&As[rr * kGLd + cc]) = v;
-    }
-    // packed words of the group: 128 rows x 16 words = 512 chunks of 4 words
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int chn = tid + 256 * i;
-      const int rr = chn >> 2;
-      const int cc = (chn & 3) * 4;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (n0 + rr < N) v = ldg128_stream(qw + (n0 + rr) * (K >> 3) + g * 16 + cc);
-      *reinterpret_cast<u32x4*>(&Bq[rr * 16 + cc]) = v;
-    }
-    if (tid < kGT) {
-      uint32_t dh = 0u, zh = 0u;
-      if (n0 + tid < N) {
-        dh = f32_to_f16_bits(ldexpf(f16_to_f32(scales[(n0 + tid) * G + g]), ecol));
-        zh = f32_to_f16_bits(-(kOff1024 + (float)zeros[(n0 + tid) * G + g]));
-      }
-      Bd[tid] = dh | (dh << 16);
-      Bz[tid] = zh | (zh << 16);
-    }
-    __syncthreads();
+  u32x4 ra[4];              // staged x chunks
+  u32x4 rb0, rb1;           // staged packed words (threads < 256)
+  uint32_t rs = 0, rz = 0;  // staged step / zero (threads >= 256)
 
-    f16x2 dd[2], nz[2];
+  auto gload = [&](int64_t s) {
+    const int64_t k0 = s * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra[i] = ldg128(asrc[i] + k0);
+    if (tid < 256) {
+      rb0 = ldg128_stream(bsrc + (k0 >> 3));
+      rb1 = ldg128_stream(bsrc + (k0 >> 3) + 4);
+    } else {
+      rs = ssrc[k0 / kGroup];
+      rz = zsrc[k0 / kGroup];
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 512 * i;
+      // rows past M hold row 0's data: output rows are independent and those are never stored
+      *reinterpret_cast<u32x4*>(&As[buf][(c >> 3) * kALd + (c & 7) * 8]) = ra[i];
+    }
+    if (tid < 256) {
+      // word order (0,2,4,6 | 1,3,5,7): a lane's four k steps are one 16-byte read
+      // columns past N hold column 0's words; their outputs are never stored
+      const u32x4 e = {rb0[0], rb0[2], rb1[0], rb1[2]};
+      const u32x4 o = {rb0[1], rb0[3], rb1[1], rb1[3]};
+      *reinterpret_cast<u32x4*>(&Bq[buf][bcol * kBLd]) = e;
+      *reinterpret_cast<u32x4*>(&Bq[buf][bcol * kBLd + 4]) = o;
+    } else {
+      u32x4 c = {0u, 0u, 0u, 0u};
+      if (bcol_ok) {
+        const float D = ldexpf(f16_to_f32(rs), ecol);        // D' (exact: power-of-two scaling)
+        const uint32_t h24 = f32_to_f16_bits(D * 16777216.0f);
+        const uint32_t h20 = f32_to_f16_bits(D * 1048576.0f);
+        const uint32_t hz = f32_to_f16_bits(-(D * (float)rz));
+        c[0] = h24 | (h24 << 16);
+        c[1] = h20 | (h20 << 16);
+        c[2] = hz | (hz << 16);
+      }
+      *reinterpret_cast<u32x4*>(&Bc[buf][bcol * 4]) = c;
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int64_t s = 0; s < S; ++s) {
+    const int buf = (int)(s & 1);
+    if (s + 1 < S) gload(s + 1);
+    f16x2 c24[2], c20[2], nzd[2];
+    u32x4 bw[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int col = wn * 64 + nb * 32 + (lane & 31);
-      dd[nb] = __builtin_bit_cast(f16x2, Bd[col]);
-      nz[nb] = __builtin_bit_cast(f16x2, Bz[col]);
+      const u32x4 c = *reinterpret_cast<const u32x4*>(&Bc[buf][col * 4]);
+      c24[nb] = as_f16x2(c[0]);
+      c20[nb] = as_f16x2(c[1]);
+      nzd[nb] = as_f16x2(c[2]);
+      bw[nb] = *reinterpret_cast<const u32x4*>(&Bq[buf][col * kBLd + (lane >> 5) * 4]);
     }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int kw = ks * 2 + (lane >> 5);        // word index within the group
-      u32x4 a[2], b[2];
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      u32x4 a[4], b[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        a[mb] = *reinterpret_cast<const u32x4*>(&As[(wm * 64 + mb * 32 + (lane & 31)) * kGLd + kw * 8]);
+      for (int mb = 0; mb < 4; ++mb)
+        a[mb] = *reinterpret_cast<const u32x4*>(
+            &As[buf][(wm * 128 + mb * 32 + (lane & 31)) * kALd + ks * 16 + 8 * (lane >> 5)]);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = wn * 64 + nb * 32 + (lane & 31);
-        b[nb] = dequant_word_f16(Bq[col * 16 + kw], dd[nb], nz[nb]);
-      }
+      for (int nb = 0; nb < 2; ++nb) b[nb] = dequant_word_f16(bw[nb][ks], c24[nb], c20[nb], nzd[nb]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32h(a[mb], b[nb], acc[mb][nb]);
     }
+    if (s + 1 < S) lstore(buf ^ 1);
     __syncthreads();
   }
 
@@ -572,10 +621,10 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ xq, i
     if (n >= N) continue;
     const int e = en[n];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int64_t m = m0 + wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (m < M) store_y<YDT>(y, m * ldy + n, ldexpf(acc[mb][nb][v], -(pm[m] + e)));
       }
   }
@@ -649,8 +698,8 @@ hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
                      r, w.xq, w.pm);
   hipLaunchKernelGGL(k_step_exp, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, scales, N,
                      K / kGroup, w.en);
-  const dim3 grid((unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT));
-  hipLaunchKernelGGL((k_gemm<YDT>), grid, dim3(256), 0, st, w.xq, M, K, w.pm, qw, scales, zeros,
+  const dim3 grid((unsigned)((N + kNT - 1) / kNT), (unsigned)((M + kMT - 1) / kMT));
+  hipLaunchKernelGGL((k_gemm<YDT>), grid, dim3(512), 0, st, w.xq, M, K, w.pm, qw, scales, zeros,
                      w.en, N, y, ldy);
   return hipGetLastError();
 }
