@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
 // ---------------------------------------------------------------------------
 // contraction C = X E'^T, sum of squares per tile
 // ---------------------------------------------------------------------------
-constexpr int kCT = 128;        // tile edge (tokens and rows)
+constexpr int kCT = 256;        // tile edge (tokens and rows)
 constexpr int kCBK = 64;        // k per LDS stage
 constexpr int kCLd = kCBK + 8;  // LDS row stride in 16-bit elements (padding vs bank conflicts)
 
@@ -141,96 +141,123 @@ __device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const 
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// 256 tokens x 256 error rows per block of 8 waves (2 along tokens x 4 along
+// rows; each wave 128 x 64 = 4 x 2 blocks of 32 x 32), 64 k per LDS stage, two
+// stages so the next stage's loads overlap the current matrix-core work.
 // px: per-token power of two of the fp16 tokens (NULL: tokens unscaled).
-__global__ __launch_bounds__(256) void k_err_contract(const uint16_t* __restrict__ X, int64_t T,
+__global__ __launch_bounds__(512) void k_err_contract(const uint16_t* __restrict__ X, int64_t T,
                                                       int64_t ldx, const int* __restrict__ px,
                                                       const uint16_t* __restrict__ E, int64_t N,
                                                       int64_t K, const int* __restrict__ pexp,
                                                       double* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kCT * kCLd];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kCT * kCLd];
-  __shared__ double wsum[4];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kCT * kCLd];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kCT * kCLd];
+  __shared__ double wsum[8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv >> 2, wn = wv & 3;
   const int64_t n0 = (int64_t)blockIdx.x * kCT;   // rows of E (MFMA columns)
   const int64_t t0 = (int64_t)blockIdx.y * kCT;   // tokens (MFMA rows)
+  const int64_t S = K / kCBK;
 
-  f32x16 acc[2][2];
+  // per-thread sources: rows past T / N read row 0 and are excluded in the epilogue
+  const uint16_t* asrc[4];
+  const uint16_t* bsrc[4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 512 * i;
+    const int64_t t = t0 + (c >> 3), n = n0 + (c >> 3);
+    asrc[i] = X + (t < T ? t : 0) * ldx + (c & 7) * 8;
+    bsrc[i] = E + (n < N ? n : 0) * K + (c & 7) * 8;
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  for (int64_t k0 = 0; k0 < K; k0 += kCBK) {
-    // stage: 128 rows x 64 k of each operand = 1024 chunks of 16 B, 4 per thread
+  u32x4 ra[4], rb[4];
+  auto gload = [&](int64_t s) {
+    const int64_t k0 = s * kCBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 256 * i;
-      const int r = ch >> 3;
-      const int cc = (ch & 7) * 8;
-      u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-      if (t0 + r < T) va = ldg128(X + (t0 + r) * ldx + k0 + cc);
-      if (n0 + r < N) vb = ldg128(E + (n0 + r) * K + k0 + cc);
-      *reinterpret_cast<u32x4*>(&As[r * kCLd + cc]) = va;
-      *reinterpret_cast<u32x4*>(&Bs[r * kCLd + cc]) = vb;
+      ra[i] = ldg128(asrc[i] + k0);
+      rb[i] = ldg128(bsrc[i] + k0);
     }
-    __syncthreads();
+  };
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < kCBK; ks += 16) {
-      const int kk = ks + 8 * (lane >> 5);
-      u32x4 a[2], b[2];
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 512 * i;
+      const int off = (c >> 3) * kCLd + (c & 7) * 8;
+      *reinterpret_cast<u32x4*>(&As[buf][off]) = ra[i];
+      *reinterpret_cast<u32x4*>(&Bs[buf][off]) = rb[i];
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int64_t s = 0; s < S; ++s) {
+    const int buf = (int)(s & 1);
+    if (s + 1 < S) gload(s + 1);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        a[mb] = *reinterpret_cast<const u32x4*>(&As[(wm * 64 + mb * 32 + (lane & 31)) * kCLd + kk]);
+    for (int ks = 0; ks < kCBK / 16; ++ks) {
+      const int kk = ks * 16 + 8 * (lane >> 5);
+      u32x4 a[4], b[2];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        a[mb] = *reinterpret_cast<const u32x4*>(&As[buf][(wm * 128 + mb * 32 + (lane & 31)) * kCLd + kk]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        b[nb] = *reinterpret_cast<const u32x4*>(&Bs[(wn * 64 + nb * 32 + (lane & 31)) * kCLd + kk]);
+        b[nb] = *reinterpret_cast<const u32x4*>(&Bs[buf][(wn * 64 + nb * 32 + (lane & 31)) * kCLd + kk]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32h(a[mb], b[nb], acc[mb][nb]);
     }
+    if (s + 1 < S) lstore(buf ^ 1);
     __syncthreads();
   }
 
-  // epilogue: every value a lane holds for block nb belongs to E row n
-  // (32x32 layout: token row = 8 (v / 4) + 4 (lane / 32) + v % 4 of the block)
+  // epilogue: every value a lane holds for block nb belongs to E row n;
+  // token row of value v in block mb: 8 (v / 4) + 4 (lane / 32) + v % 4
   double tot = 0.0;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int64_t n = n0 + wn * 64 + nb * 32 + (lane & 31);
     if (n >= N) continue;
-    if (px == nullptr) {
-      float ssq = 0.0f;
+    double ssq = 0.0;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 4; ++mb) {
+      float part = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) ssq += acc[mb][nb][v] * acc[mb][nb][v];
-      tot += ldexp((double)ssq, -2 * pexp[n]);
-    } else {
-      double ssq = 0.0;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t t = t0 + wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const double c = (double)acc[mb][nb][v];
-          if (t < T) ssq += ldexp(c * c, -2 * px[t]);
+      for (int v = 0; v < 16; ++v) {
+        const int64_t t = t0 + wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (t < T) {
+          const float c = acc[mb][nb][v];
+          if (px == nullptr) part += c * c;
+          else ssq += ldexp((double)c * (double)c, -2 * px[t]);
         }
-      tot += ldexp(ssq, -2 * pexp[n]);
+      }
+      ssq += (double)part;
     }
+    tot += ldexp(ssq, -2 * pexp[n]);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
   if (lane == 0) wsum[wv] = tot;
   __syncthreads();
-  if (tid == 0)
-    partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  if (tid == 0) {
+    double t = 0.0;
+    for (int w = 0; w < 8; ++w) t += wsum[w];
+    partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = t;
+  }
 }
 
 // Fixed-order sum of n doubles by one block of 256 threads -> out[0] = sum / denom.
@@ -353,7 +380,7 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
     else
       hipLaunchKernelGGL(k_err_gen<DT_BF16>, dim3((unsigned)N), dim3(256), 0, st,
                          (const uint16_t*)w, N, K, s_i, sw.E, sw.pexp);
-    hipLaunchKernelGGL(k_err_contract, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st, Xop, T,
+    hipLaunchKernelGGL(k_err_contract, dim3((unsigned)gx, (unsigned)gy), dim3(512), 0, st, Xop, T,
                        ldop, px, sw.E, N, K, sw.pexp, sw.partial);
     hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial, gx * gy, tn,
                        sw.losses + i);
