@@ -257,8 +257,8 @@ def main() -> int:
             "group_size": 128, "bits": 4,
         },
         "roofline": {"bound": "hbm", "achieved": gemv_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gemv_gbs / HBM_PEAK_GBS, "traffic": measured_traffic("k_gemv1"),
-                     "kernel": "k_gemv1 (batch 1)",
+                     "frac": gemv_gbs / HBM_PEAK_GBS, "traffic": measured_traffic("k_gemv1_cu"),
+                     "kernel": "k_gemv1_cu (batch 1, one block per compute unit)",
                      "bytes_per_launch": bytes_a},
         "prefill_gemm": {"bound": "mfma", "achieved": gemm_tflops, "peak": FP16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": gemm_tflops / FP16_MFMA_PEAK_TFLOPS,

@@ -119,6 +119,35 @@ def test_gemv_parity(M, N, K, dtype, ydt, with_r):
     assert err <= GEMM_TOL
 
 
+@pytest.mark.parametrize("N,K,dtype,ydt,with_r", [
+    (6400, 4224, BF16, BF16, True),          # ragged second K slice (4 of 128 chunks)
+    (6145, 8320, F16, torch.float32, False),  # 3 K slices, 2 staged pieces per thread
+    (6200, 28672, BF16, torch.float32, True),  # 7 K slices, 4 staged pieces per thread
+    (12000, 4096, F16, F16, False),
+    (300, 30720, F16, F16, True),             # K beyond the row-block kernel, few rows per block
+])
+def test_gemv_batch1_per_cu_parity(N, K, dtype, ydt, with_r):
+    """Batch-1 shapes served by the one-block-per-compute-unit kernel (many
+    rows, or K past the row-block kernel's staging); sampled output channels
+    against the oracle (channels are independent)."""
+    g = np.random.Generator(np.random.PCG64(N + K))
+    words = g.integers(-2 ** 31, 2 ** 31, (N, K // 8), dtype=np.int64).astype(np.int32)
+    step = g.uniform(2e-4, 4e-3, (N, K // 128)).astype(np.float16)
+    z = g.integers(0, 16, (N, K // 128)).astype(np.uint8)
+    x = _act(1, K, dtype, N + K + 1)
+    r = (np.float32(1) / np.exp(g.uniform(-1.5, 1.5, K)).astype(np.float32)).astype(np.float32) if with_r else None
+    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                           gpu(torch.from_numpy(z)), None if r is None else gpu(torch.from_numpy(r)),
+                           out_dtype=ydt)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 300)), np.arange(N - 40, N),
+                                     g.integers(0, N, 100)]))
+    ref = O.w4a16_matmul_rows(f32(x), words, step, z, rows, r)
+    err = rel_max_err(f32(y)[:, rows], ref, ydt)
+    print(f"gemv batch 1 N={N} K={K} {dtype} -> {ydt}: rel max err {err:.3e} on {len(rows)} channels")
+    assert err <= GEMM_TOL
+
+
 @pytest.mark.parametrize("M,N,K,dtype,ydt,with_r", [
     (9, 300, 512, F16, torch.float32, False), (32, 4096, 4096, F16, F16, True),
     (100, 1000, 1024, BF16, torch.float32, True), (256, 512, 8192, BF16, BF16, False),

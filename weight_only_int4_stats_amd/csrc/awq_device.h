@@ -96,6 +96,13 @@ __device__ __forceinline__ float quant_code(float wp, const GroupGrid& g) {
   return fminf(fmaxf(rintf(wp / g.D) + g.z, 0.0f), 15.0f);
 }
 
+// Raw buffer access: the fourth descriptor word for untyped 32-bit data, an
+// offset that is always out of range (the load returns 0 and reads nothing),
+// and the non-temporal cache policy bit for streamed weights.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kBufferOob = 0x80000000u;
+constexpr int kBufferNt = 2;
+
 // Min / max across the 16 lanes of an aligned 16-lane segment.
 __device__ __forceinline__ void seg16_minmax(float& mn, float& mx) {
 #pragma unroll
@@ -112,6 +119,52 @@ __device__ __forceinline__ u32x4 ldg128(const void* p) {
 // Streaming 128-bit load that is not expected to be reused (packed weights).
 __device__ __forceinline__ u32x4 ldg128_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// A 32-bit constant held in a scalar register.  Three-operand VALU
+// instructions cannot encode a 32-bit literal on this target, so a mask that is
+// meant to feed v_and_or_b32 lives in an SGPR (one scalar operand per VALU op).
+template <uint32_t V>
+__device__ __forceinline__ uint32_t sgpr_const() {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(V));
+  return r;
+}
+// The same, held in a vector register (the second non-literal operand).
+template <uint32_t V>
+__device__ __forceinline__ uint32_t vgpr_const() {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(V));
+  return r;
+}
+
+// Butterfly steps across a wave.  pair_sum32(a, b): lanes 0..31 return
+// a(l) + a(l + 32), lanes 32..63 return b(l - 32) + b(l) (one v_permlane32_swap
+// moves the upper half of a and the lower half of b across).  pair_sum16 is the
+// same between the even and odd 16-lane rows.
+__device__ __forceinline__ float pair_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Value of lane l ^ 1 / l ^ 2 (DPP quad permutes).
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+// Sum over each 16-lane row; lane 16 j ends with the total of row j (DPP
+// mirror, half-mirror and quad exchanges, no LDS traffic).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += quad_xor2(v);
+  v += quad_xor1(v);
+  return v;
 }
 
 }  // namespace awqk

@@ -26,7 +26,7 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
                          void* ws, hipStream_t st);
 
 // ---- W4A16 product ----------------------------------------------------------
-constexpr int64_t kGemv1MaxK = 24576;   // batch-1 GEMV: staged activations fit 64 KB of LDS
+bool gemv1_supported(int64_t K, int64_t N);   // batch-1 GEMV kernels cover this shape
 hipError_t launch_gemv1(const void* x, int xdt, int64_t K, const uint32_t* qw,
                         const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
                         void* y, int ydt, hipStream_t st);

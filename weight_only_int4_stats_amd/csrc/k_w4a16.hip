@@ -511,7 +511,7 @@ template <int DT, int YDT>
 hipError_t w4a16_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
                           const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
                           void* y, int64_t ldy, void* ws, hipStream_t st) {
-  if (M == 1 && K <= awq::kGemv1MaxK)
+  if (M == 1 && awq::gemv1_supported(K, N))
     return awq::launch_gemv1(x, DT, K, qw, scales, zeros, N, r, y, YDT, st);
   if (use_gemv(M, K)) {
     if (r) return gemv_dispatch<DT, YDT, true>(x, (int)M, K, ldx, qw, scales, zeros, N, r, y, ldy, st);
@@ -526,7 +526,8 @@ hipError_t w4a16_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
 namespace awq {
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || awqk::use_gemv(M, K)) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || awqk::use_gemv(M, K) || (M == 1 && gemv1_supported(K, N)))
+    return 0;
   return awqk::gemm_ws(nullptr, M, N, K).bytes;
 }
 
