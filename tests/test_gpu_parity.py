@@ -119,6 +119,40 @@ def test_gemv_parity(M, N, K, dtype, ydt, with_r):
     assert err <= GEMM_TOL
 
 
+def _sampled_product(M, N, K, dtype, ydt, with_r, seed):
+    """Random packed layer (words drawn directly), sampled output channels
+    against the oracle (channels are independent)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    words = g.integers(-2 ** 31, 2 ** 31, (N, K // 8), dtype=np.int64).astype(np.int32)
+    step = g.uniform(2e-4, 4e-3, (N, K // 128)).astype(np.float16)
+    z = g.integers(0, 16, (N, K // 128)).astype(np.uint8)
+    x = _act(M, K, dtype, seed + 1)
+    r = (np.float32(1) / np.exp(g.uniform(-1.5, 1.5, K)).astype(np.float32)).astype(np.float32) if with_r else None
+    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                           gpu(torch.from_numpy(z)), None if r is None else gpu(torch.from_numpy(r)),
+                           out_dtype=ydt)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 300)), np.arange(N - 40, N),
+                                     g.integers(0, N, 100)]))
+    ref = O.w4a16_matmul_rows(f32(x), words, step, z, rows, r)
+    return rel_max_err(f32(y)[:, rows], ref, ydt), len(rows)
+
+
+@pytest.mark.parametrize("M,N,K,dtype,ydt,with_r", [
+    (2, 28672, 8192, BF16, BF16, True),        # per-CU skinny, 7 row tiles per block
+    (12, 5000, 2048, BF16, torch.float32, True),  # 3 token phases per thread
+    (16, 3000, 4096, F16, F16, False),         # 16 tokens, activations fill LDS
+    (5, 11008, 4096, F16, F16, True),
+    (8, 2000, 16384, F16, torch.float32, True),  # activations exceed LDS: pre-pass kernel
+    (16, 700, 11008, BF16, BF16, False),       # ragged K slices, pre-pass kernel
+])
+def test_skinny_product_parity(M, N, K, dtype, ydt, with_r):
+    """2 <= M <= 16: the skinny matrix-core products."""
+    err, nrow = _sampled_product(M, N, K, dtype, ydt, with_r, seed=7 * M + N + K)
+    print(f"skinny M={M} N={N} K={K} {dtype} -> {ydt}: rel max err {err:.3e} on {nrow} channels")
+    assert err <= GEMM_TOL
+
+
 @pytest.mark.parametrize("N,K,dtype,ydt,with_r", [
     (6400, 4224, BF16, BF16, True),          # ragged second K slice (4 of 128 chunks)
     (6145, 8320, F16, torch.float32, False),  # 3 K slices, 2 staged pieces per thread
@@ -128,23 +162,9 @@ def test_gemv_parity(M, N, K, dtype, ydt, with_r):
 ])
 def test_gemv_batch1_per_cu_parity(N, K, dtype, ydt, with_r):
     """Batch-1 shapes served by the one-block-per-compute-unit kernel (many
-    rows, or K past the row-block kernel's staging); sampled output channels
-    against the oracle (channels are independent)."""
-    g = np.random.Generator(np.random.PCG64(N + K))
-    words = g.integers(-2 ** 31, 2 ** 31, (N, K // 8), dtype=np.int64).astype(np.int32)
-    step = g.uniform(2e-4, 4e-3, (N, K // 128)).astype(np.float16)
-    z = g.integers(0, 16, (N, K // 128)).astype(np.uint8)
-    x = _act(1, K, dtype, N + K + 1)
-    r = (np.float32(1) / np.exp(g.uniform(-1.5, 1.5, K)).astype(np.float32)).astype(np.float32) if with_r else None
-    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
-                           gpu(torch.from_numpy(z)), None if r is None else gpu(torch.from_numpy(r)),
-                           out_dtype=ydt)
-    torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 300)), np.arange(N - 40, N),
-                                     g.integers(0, N, 100)]))
-    ref = O.w4a16_matmul_rows(f32(x), words, step, z, rows, r)
-    err = rel_max_err(f32(y)[:, rows], ref, ydt)
-    print(f"gemv batch 1 N={N} K={K} {dtype} -> {ydt}: rel max err {err:.3e} on {len(rows)} channels")
+    rows, or K past the row-block kernel's staging)."""
+    err, nrow = _sampled_product(1, N, K, dtype, ydt, with_r, seed=N + K)
+    print(f"gemv batch 1 N={N} K={K} {dtype} -> {ydt}: rel max err {err:.3e} on {nrow} channels")
     assert err <= GEMM_TOL
 
 

@@ -38,4 +38,7 @@ hipError_t launch_w4a16(const void* x, int xdt, int64_t M, int64_t K, int64_t ld
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
 }  // namespace awq

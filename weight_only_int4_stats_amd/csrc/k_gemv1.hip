@@ -378,18 +378,6 @@ __global__ __launch_bounds__(1024) void k_gemv1_cu(
 
 constexpr size_t kCuLdsReserve = 81 * 1024;
 
-// Compute units of the current device (cached per device).
-inline int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
 
 template <int DT, int YDT, bool HAS_R, int NS, int D, int C>
 hipError_t gemv1_cu_launch(const uint16_t* x, int64_t K, const uint32_t* qw, const uint16_t* scales,
@@ -436,7 +424,7 @@ constexpr int kCuMinRowsPerCu = 24;       // below this the row-block kernel is 
 
 // Which batch-1 kernel serves (K, N): 2 = per-CU, 1 = row-block, 0 = neither.
 inline int gemv1_path(int64_t K, int64_t N) {
-  const int64_t cus = device_cus();
+  const int64_t cus = awq::device_cus();
   const int64_t nblk = N < cus ? N : cus;
   const int64_t rows_max = (N + nblk - 1) / nblk;
   const int64_t CH = K >> 5;
@@ -454,7 +442,7 @@ hipError_t gemv1_dispatch(const uint16_t* x, int64_t K, const uint32_t* qw, cons
   const int path = gemv1_path(K, N);
   const int64_t need = ((K >> 3) + 3) / 4 * 4;     // staged 8-element pieces, whole quads
   if (path == 2) {
-    const int nblk = device_cus();
+    const int nblk = awq::device_cus();
     const int64_t nks = ((K >> 5) + 127) / 128;
     const int64_t threads = nks * (16 / nks) * 64;
     if (need <= threads)
@@ -477,6 +465,18 @@ hipError_t gemv1_dispatch(const uint16_t* x, int64_t K, const uint32_t* qw, cons
 }  // namespace awqk
 
 namespace awq {
+
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 bool gemv1_supported(int64_t K, int64_t N) { return awqk::gemv1_path(K, N) != 0; }
 

@@ -5,236 +5,30 @@
 //
 //   y[m][n] = sum_k step[n][g(k)] * (q[n][k] - z[n][g(k)]) * x[m][k] * r[k]
 //
-// Two kernels:
+// Kernels (the batch-1 GEMV kernels live in their own source):
 //
-// * k_gemv (M <= 8): bandwidth-bound split-K GEMV.  A lane owns a fixed
-//   128-bit chunk of every row (32 codes = a quarter group), so its slice of
-//   x stays in registers for all rows; a wave covers 64 consecutive chunks
-//   (2048 codes) of a row, a block's waves cover the row's K slices, and the
-//   block walks a tile of rows with all of its 128-bit weight loads in flight.
-//   Dequantization is exact and cheap: the nibble pair (q_j, q_j+4) of a word
-//   becomes two fp16 values 1024 + q by OR-ing the exponent bits of 1024 into
-//   them; a packed fp16 dot product with the matching x pair accumulates in
-//   fp32, and the group epilogue subtracts (1024 + z) * sum(x) and applies the
-//   step.  The lane's x slice is fp16: as given for fp16 input, otherwise
-//   (bf16 input or a 1/s factor) x * r is scaled by an exact power of two per
-//   lane and rounded to fp16 once.  Partial sums are reduced across lanes and
-//   waves through LDS in a fixed order.
-//
-// * k_gemm (M > 8): fp16 matrix-core GEMM on 128x128 output tiles, one
-//   128-wide group per K step.  A pre-pass rounds each activation row x * r,
-//   scaled by an exact power of two, to fp16 (exact for bf16 input without
-//   1/s) in the order the nibble unpack produces; a second pre-pass picks a
-//   power of two per weight row so that step * 15 stays inside fp16.  Each
-//   lane dequantizes its packed word of the B fragment to step * (q - z)
-//   rounded once to fp16 and feeds v_mfma_f32_32x32x16_f16; the epilogue
-//   undoes both powers of two exactly.
+// * k_gemm_skinny_cu (M <= 16, activations fit in LDS): one block of 16 waves
+//   per compute unit stages x * r as fp16 once and runs
+//   v_mfma_f32_16x16x32_f16 with 16 weight rows as A and the tokens as B.
+// * k_gemm_skinny (M <= 16 otherwise): the same MFMA mapping, one block per
+//   16 weight rows, activations from a pre-pass.
+// * k_gemm (M > 16): fp16 matrix-core GEMM on 256x256 output tiles.  A
+//   pre-pass rounds each activation row x * r, scaled by an exact power of
+//   two, to fp16 (exact for bf16 input without 1/s) in the order the nibble
+//   unpack produces; a second pre-pass picks a power of two per weight row so
+//   that step * 15 stays inside fp16.  Each lane dequantizes its packed word
+//   to step * (q - z) rounded once to fp16 and feeds v_mfma_f32_32x32x16_f16;
+//   the epilogue undoes both powers of two exactly.
 #include "awq_device.h"
 #include "awq_internal.h"
 #include "k_rows_f16.h"
 
 namespace awqk {
 
-// ===========================================================================
-// GEMV
-// ===========================================================================
-constexpr int kGvVals = 16;      // partial sums per lane per block (units x M)
-constexpr int64_t kGemvMaxK = 30720;   // 15 waves of 64 chunks: reduction buffers stay in 64 KB LDS
-constexpr int64_t kGemvMaxK8 = 16384;  // 8 waves for 2..8 activation rows
-
-constexpr uint32_t kMagic1024 = 0x64006400u;   // fp16 1024.0 in both halves
-constexpr float kOff1024 = 1024.0f;
-
-__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
-}
-
 template <int YDT>
 __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
   if constexpr (YDT == DT_F32) reinterpret_cast<float*>(y)[idx] = v;
   else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)from_f32<YDT>(v);
-}
-
-// Row units (RPS rows side by side) whose weights a lane loads up front, per
-// activation-row count.  More units put more bytes in flight per wave; the
-// activation registers limit them for larger MT.
-template <int MT>
-constexpr int gemv_units() { return MT <= 2 ? 8 : 4; }
-
-// LPR: lanes per row segment (16, 32 or 64); MT: activation rows (1, 2, 4, 8).
-// Loads are issued in the order activations, 1/s, weights / steps / zero
-// points, all branch-free (out-of-range rows and chunks read a valid address
-// and are masked afterwards), so every load of the block is in flight before
-// the first wait; the activation slice is converted while the weights arrive.
-template <int DT, int YDT, int LPR, int MT, bool HAS_R>
-__global__ __launch_bounds__(LPR < 64 ? 64 : (MT == 1 ? 1024 : 512)) void k_gemv(
-    const uint16_t* __restrict__ x, int M, int64_t K, int64_t ldx, const uint32_t* __restrict__ qw,
-    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N,
-    const float* __restrict__ r, void* __restrict__ y, int64_t ldy) {
-  constexpr int RPS = 64 / LPR;                // rows processed side by side per wave
-  constexpr int UL = gemv_units<MT>();         // row units loaded per lane
-  constexpr int UP = kGvVals / MT;             // row units per reduction pass
-  constexpr int NPASS = (UL + UP - 1) / UP;
-  constexpr int ROWS = UL * RPS;               // rows per block
-  constexpr int NOUT = kGvVals * RPS;          // outputs per reduction pass
-  constexpr bool kScaled = (DT == DT_BF16) || HAS_R;
-
-  extern __shared__ float red[];               // [nw][kGvVals][64] then [nw][NOUT]
-  const int nw = blockDim.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int sub = lane / LPR;
-  const int cl = lane % LPR;
-  const int64_t CH = K >> 5;                   // 16-byte chunks per row
-  const int64_t ch = (int64_t)wv * LPR + cl;
-  const bool valid = ch < CH;
-  const int64_t chc = valid ? ch : 0;          // in-bounds chunk for masked lanes
-  const int64_t G = K / kGroup;
-  const int64_t gc = chc >> 2;
-  const int64_t row0 = (int64_t)blockIdx.x * ROWS;
-
-  // ---- 1. activation (and 1/s) loads
-  u32x4 xraw[MT][4];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int cw = 0; cw < 4; ++cw)
-      xraw[m][cw] = ldg128(x + (int64_t)(m < M ? m : 0) * ldx + chc * 32 + cw * 8);
-  f32x4 rr[8];
-  if constexpr (HAS_R) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rr[i] = *reinterpret_cast<const f32x4*>(r + chc * 32 + i * 4);
-  }
-
-  // ---- 2. weights, steps, zero points of all the block's rows
-  u32x4 wq[UL];
-  uint32_t sraw[UL], zraw[UL];
-#pragma unroll
-  for (int u = 0; u < UL; ++u) {
-    int64_t row = row0 + u * RPS + sub;
-    row = row < N ? row : N - 1;
-    wq[u] = ldg128_stream(qw + row * (K >> 3) + chc * 4);
-    sraw[u] = scales[row * G + gc];
-    zraw[u] = zeros[row * G + gc];
-  }
-  // keep every load above this point: nothing below may be hoisted between
-  // them, so all of them are in flight before the first wait
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 3. activation slice -> fp16 pairs (x_j, x_j+4) per word, sum, scale
-  uint32_t xp[MT][16];
-  float xs[MT], xscale[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    uint32_t h[32];
-    xscale[m] = 1.0f;
-    if constexpr (kScaled) {
-      float v[32];
-#pragma unroll
-      for (int cw = 0; cw < 4; ++cw)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[cw * 8 + 2 * j] = lo_f32<DT>(xraw[m][cw][j]);
-          v[cw * 8 + 2 * j + 1] = hi_f32<DT>(xraw[m][cw][j]);
-        }
-      if constexpr (HAS_R) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] *= rr[i >> 2][i & 3];
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      const int p = pow2_exp_for(amax);
-      xscale[m] = ldexpf(1.0f, -p);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) h[i] = f32_to_f16_bits(ldexpf(v[i], p));
-    } else {
-#pragma unroll
-      for (int cw = 0; cw < 4; ++cw)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          h[cw * 8 + 2 * j] = xraw[m][cw][j] & 0xFFFFu;
-          h[cw * 8 + 2 * j + 1] = xraw[m][cw][j] >> 16;
-        }
-    }
-    const bool live = valid && m < M;
-    float sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sum += f16_to_f32(h[i]);
-    xs[m] = live ? sum : 0.0f;
-#pragma unroll
-    for (int cw = 0; cw < 4; ++cw)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xp[m][cw * 4 + j] = live ? (h[cw * 8 + j] | (h[cw * 8 + j + 4] << 16)) : 0u;
-  }
-
-  // ---- 4. dot products and the reduction, one pass of UP row units at a time
-  constexpr int LPO = 64 / NOUT;               // lanes per output in the LDS reduction: 4, 2 or 1
-  float* rw = red + wv * (kGvVals * 64);
-  float* r2 = red + nw * (kGvVals * 64);
-#pragma unroll
-  for (int pass = 0; pass < NPASS; ++pass) {
-    float val[kGvVals];
-#pragma unroll
-    for (int uu = 0; uu < UP; ++uu) {
-      const int u = pass * UP + uu;
-      if (u >= UL) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) val[uu * MT + m] = 0.0f;
-        continue;
-      }
-      const bool rowok = valid && (row0 + u * RPS + sub) < N;
-      const float dz = rowok ? f16_to_f32(sraw[u]) : 0.0f;
-      const float cz = kOff1024 + (float)zraw[u];
-      float P[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) P[m] = 0.0f;
-#pragma unroll
-      for (int cw = 0; cw < 4; ++cw) {
-        const uint32_t wword = wq[u][cw];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t pr = ((wword >> (4 * j)) & 0x000F000Fu) | kMagic1024;
-#pragma unroll
-          for (int m = 0; m < MT; ++m) P[m] = dot2h(pr, xp[m][cw * 4 + j], P[m]);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        val[uu * MT + m] = (dz * __builtin_fmaf(-cz, xs[m], P[m])) * xscale[m];
-    }
-
-    if (pass > 0) __syncthreads();               // the previous pass has read its LDS
-#pragma unroll
-    for (int v = 0; v < kGvVals; ++v) rw[v * 64 + lane] = val[v];
-    __syncthreads();
-    {
-      const int o = lane / LPO;
-      const int jj = lane % LPO;
-      const int v = o / RPS;
-      const int osub = o % RPS;
-      const float* src = rw + v * 64 + osub * LPR + jj * 16;
-      float t = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) t += src[i];
-#pragma unroll
-      for (int off = LPO / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off);
-      if (jj == 0) r2[wv * NOUT + o] = t;
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < NOUT) {
-      const int oo = threadIdx.x;
-      float tot = 0.0f;
-      for (int w = 0; w < nw; ++w) tot += r2[w * NOUT + oo];
-      const int vv = oo / RPS;
-      const int uu = vv / MT;
-      const int m = vv % MT;
-      const int u = pass * UP + uu;
-      const int64_t row = row0 + (int64_t)u * RPS + (oo % RPS);
-      if (u < UL && row < N && m < M) store_y<YDT>(y, (int64_t)m * ldy + row, tot);
-    }
-  }
 }
 
 // ===========================================================================
@@ -433,36 +227,138 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
   }
 }
 
-// ---------------------------------------------------------------------------
-template <int DT, int YDT, bool HAS_R>
-hipError_t gemv_dispatch(const uint16_t* x, int M, int64_t K, int64_t ldx, const uint32_t* qw,
-                         const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
-                         void* y, int64_t ldy, hipStream_t st) {
-  const int64_t CH = K >> 5;
-  const int lpr = CH >= 64 ? 64 : (CH > 16 ? 32 : 16);
-  const int64_t nw = (CH + lpr - 1) / lpr;   // <= 15 (K <= kGemvMaxK)
-  const int rps = 64 / lpr;
-  const int mt = M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8));
-  const int rows = (mt <= 2 ? gemv_units<1>() : gemv_units<8>()) * rps;
-  const dim3 grid((unsigned)((N + rows - 1) / rows));
-  const dim3 block((unsigned)(nw * 64));
-  const size_t lds = (size_t)nw * kGvVals * 64 * 4 + (size_t)nw * kGvVals * rps * 4;
-#define AWQ_GV(LPR, MT)                                                                        \
-  hipLaunchKernelGGL((k_gemv<DT, YDT, LPR, MT, HAS_R>), grid, block, lds, st, x, M, K, ldx, qw, \
-                     scales, zeros, N, r, y, ldy)
-#define AWQ_GV_M(LPR)            \
-  switch (mt) {                  \
-    case 1: AWQ_GV(LPR, 1); break; \
-    case 2: AWQ_GV(LPR, 2); break; \
-    case 4: AWQ_GV(LPR, 4); break; \
-    default: AWQ_GV(LPR, 8); break; \
+// ===========================================================================
+// skinny matrix-core product (2 <= M <= 16)
+// ===========================================================================
+// One block of 4 waves per 16 output channels; wave w takes a quarter of the
+// groups.  v_mfma_f32_16x16x32_f16 with the weights as A (16 channels x 32 k)
+// and the activations as B (32 k x 16 tokens, tokens >= M read as 0).  Lane
+// (row l % 16, block b = l / 16) loads chunk 4 g + b of its row (one 128-bit
+// load per group) and feeds word i of it to the MFMA of step i; the B lane
+// (token l % 16, block b) loads the matching 8 fp16 activations of chunk
+// 4 g + b.  A group's four steps thus use one step and zero point, which turn
+// into the packed-fma constants.  The per-row power of two e_n (as in the
+// GEMM) is found from the row's steps in a prologue; the four waves' 16 x 16
+// partial tiles are added in LDS in a fixed order.
+constexpr int kSkW = 4;                 // waves per block (K quarters)
+constexpr int kSkP = 2;                 // groups in flight per wave
+constexpr int64_t kSkMaxM = 16;         // tokens per B tile
+
+__device__ __forceinline__ f32x4 mfma16h(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <int YDT, int P>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict__ xq, int M, int64_t K,
+                                                     const int* __restrict__ pm,
+                                                     const uint32_t* __restrict__ qw,
+                                                     const uint16_t* __restrict__ scales,
+                                                     const uint8_t* __restrict__ zeros, int64_t N,
+                                                     void* __restrict__ y, int64_t ldy) {
+  __shared__ float red[kSkW][16 * 16];
+  __shared__ float rmax[kSkW][16];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rl = lane & 15;                      // A row / B token
+  const int b = lane >> 4;                       // k block
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int nrows = (int)(N - n0 < 16 ? N - n0 : 16);
+  const int G = (int)(K >> 7);
+  const int g0 = (int)((int64_t)wv * G / kSkW), g1 = (int)((int64_t)(wv + 1) * G / kSkW);
+  const uint32_t KW = (uint32_t)(K >> 3);
+  const bool rowok = rl < nrows;
+
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qw + n0 * KW), (short)0, nrows * (int)KW * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scales + n0 * G), (short)0, nrows * G * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(zeros + n0 * G), (short)0, nrows * G, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)xq, (short)0, M * (int)K * 2, kBufferWord3);
+
+  // ---- slot loads for group g (rows / tokens out of range read 0)
+  // first piece of the row's steps for the power of two (issued before the
+  // group loads: vector memory returns in order)
+  const int npc = (G * 2 + 15) / 16;             // 16-byte pieces of a row's steps
+  const uint32_t srow = (uint32_t)rl * (uint32_t)G * 2;
+  const u32x4 sp0 = __builtin_amdgcn_raw_buffer_load_b128(srs, rowok && b < npc ? srow + 16 * b : kBufferOob, 0, 0);
+
+  u32x4 wa[P], xb[P][4];
+  uint32_t sr[P], zr[P];
+  auto load_group = [&](int slot, int g) {
+    const bool ok = g < g1;
+    const uint32_t woff = (uint32_t)rl * KW * 4 + (uint32_t)(4 * g + b) * 16;
+    wa[slot] = __builtin_amdgcn_raw_buffer_load_b128(wrs, ok && rowok ? woff : kBufferOob, 0, kBufferNt);
+    sr[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, ok && rowok ? (uint32_t)(rl * G + g) * 2 : kBufferOob, 0, 0);
+    zr[slot] = __builtin_amdgcn_raw_buffer_load_b8(zrs, ok && rowok ? (uint32_t)(rl * G + g) : kBufferOob, 0, 0);
+    const uint32_t xoff = ((uint32_t)rl * (uint32_t)K + (uint32_t)(128 * g + 32 * b)) * 2;
+    const bool xok = ok && rl < M;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xb[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xok ? xoff + 16 * i : kBufferOob, 0, 0);
+  };
+#pragma unroll
+  for (int d = 0; d < P; ++d) load_group(d, g0 + d);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- per-row power of two from the row's largest step (all groups; a
+  // piece past the row's end may hold the next row's steps or read 0)
+  auto piece_max = [&](const u32x4& v, int pc, float m) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (pc * 8 + j < G) m = fmaxf(m, f16_to_f32((v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu));
+    return m;
+  };
+  float mx = piece_max(sp0, b, 0.0f);
+  for (int pc = b + 4; pc < npc; pc += 4)
+    mx = piece_max(__builtin_amdgcn_raw_buffer_load_b128(srs, rowok ? srow + 16 * pc : kBufferOob, 0, 0), pc, mx);
+  {
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
   }
-  if (lpr == 64) { AWQ_GV_M(64) }
-  else if (lpr == 32) { AWQ_GV_M(32) }
-  else { AWQ_GV_M(16) }
-#undef AWQ_GV_M
-#undef AWQ_GV
-  return hipGetLastError();
+  int e = 0;
+  if (mx > 0.0f) {
+    int ex;
+    frexpf(mx, &ex);
+    e = -9 - ex;                                 // max step 2^e in [2^-10, 2^-9)
+  }
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int gb = g0; gb < g1; gb += P) {
+#pragma unroll
+    for (int d = 0; d < P; ++d) {
+      if (gb + d >= g1) break;                   // wave-uniform
+      const float D = ldexpf(f16_to_f32(sr[d]), e);
+      const uint32_t h24 = f32_to_f16_bits(D * 16777216.0f);
+      const uint32_t h20 = f32_to_f16_bits(D * 1048576.0f);
+      const uint32_t hz = f32_to_f16_bits(-(D * (float)zr[d]));
+      const f16x2 c24 = as_f16x2(h24 | (h24 << 16));
+      const f16x2 c20 = as_f16x2(h20 | (h20 << 16));
+      const f16x2 nzd = as_f16x2(hz | (hz << 16));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = mfma16h(dequant_word_f16(wa[d][i], c24, c20, nzd), xb[d][i], acc);
+    }
+    if (gb + P >= g1) break;                     // wave-uniform
+#pragma unroll
+    for (int d = 0; d < P; ++d) load_group(d, gb + P + d);
+  }
+
+  // ---- add the four K quarters; 16 x 16 layout: token = lane % 16, row = 4 (lane / 16) + v
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[wv][(4 * b + v) * 16 + rl] = acc[v];
+  if (b == 0) rmax[wv][rl] = (float)e;
+  __syncthreads();
+  const int t = threadIdx.x;                     // one (row, token) per thread
+  const int row = t >> 4, tok = t & 15;
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kSkW; ++w) tot += red[w][t];
+  if (row < nrows && tok < M)
+    store_y<YDT>(y, (int64_t)tok * ldy + n0 + row, ldexpf(tot, -(pm[tok] + (int)rmax[0][row])));
 }
 
 struct GemmWs {
@@ -488,10 +384,6 @@ inline GemmWs gemm_ws(void* ws, int64_t M, int64_t N, int64_t K) {
   return w;
 }
 
-inline bool use_gemv(int64_t M, int64_t K) {
-  return (M == 1 && K <= kGemvMaxK) || (M <= 8 && K <= kGemvMaxK8);
-}
-
 template <int DT, int YDT, bool HAS_R>
 hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
                          const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
@@ -507,15 +399,334 @@ hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Skinny product, one block of 16 waves per compute unit (2 <= M <= 16, the
+// M x K activations in LDS).  The block converts x * r to fp16 once, with an
+// exact power of two per (token, group) from the group's largest |x r| (so
+// every group sits in fp16's normal range) and the eight elements of every
+// packed word in the unpack order.  Block b owns output rows
+// [b N / B, (b + 1) N / B), cut into 16-row tiles; with t tiles each tile's
+// groups are split into S = 16 / t slices and wave w takes the items
+// (tile, slice) w, w + 16, ...  Per group a lane loads one 128-bit chunk of
+// its row plus the step and zero point, reads the matching activations from
+// LDS, runs the group's four MFMAs into a fresh 16 x 16 tile and adds it with
+// the group's activation scale 2^-p.  Slices of a tile are added in LDS in a
+// fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kScWaves = 16;
+constexpr size_t kScRedBytes = (size_t)kScWaves * 256 * 4;      // per-item 16 x 16 partial tiles
+constexpr int kScMaxPieces = 8;                                 // staged 8-element pieces per thread
+
+inline size_t skinny_cu_lds(int64_t M, int64_t K, int64_t rows_max) {
+  const int64_t ntile = (rows_max + 15) / 16;
+  return (size_t)(M + 1) * (K + 8) * 2 + (size_t)(M + 1) * (K / 128) * 4 + kScRedBytes +
+         (size_t)ntile * 16 * 4;
+}
+
+template <int DT, int YDT, bool HAS_R, int NP, int P>
+__global__ __launch_bounds__(1024) void k_gemm_skinny_cu(
+    const uint16_t* __restrict__ x, int M, int64_t K, int64_t ldx, const float* __restrict__ r,
+    const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, int64_t N, void* __restrict__ y, int64_t ldy) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds_sc[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rl = lane & 15;
+  const int b = lane >> 4;
+  const uint32_t K8 = (uint32_t)(K >> 3);
+  const int G = (int)(K >> 7);
+  const uint32_t KW = (uint32_t)(K >> 3);
+  const int64_t r0 = (int64_t)blockIdx.x * N / gridDim.x;
+  const int nrows = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x - r0);
+  const int ntile = (nrows + 15) / 16;
+  int ksl = kScWaves / (ntile > 0 ? ntile : 1);
+  ksl = ksl < 1 ? 1 : (ksl > G ? G : ksl);
+  const int nitems = ntile * ksl;
+
+  // token rows K + 8 halves apart: the 16 tokens of a 128-bit read hit
+  // different banks
+  const int64_t KP = K + 8;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds_sc);                       // [M + 1][KP] (row M = 0)
+  float* pinv = reinterpret_cast<float*>(lds_sc + (M + 1) * KP / 2);       // [M + 1][G] 2^-p
+  float* red = pinv + (M + 1) * G;                                          // [16][256]
+  int* erow = reinterpret_cast<int*>(red + kScWaves * 256);                 // [ntile][16]
+
+  // ---- staging loads (issued first).  Thread t takes piece k8 = t mod K/8 of
+  // the tokens t / (K/8), t / (K/8) + T, ... (T = 1024 / (K/8) token phases),
+  // so 1/s is read once per piece; for K/8 > 1024 it walks k8 = t, t + 1024 ...
+  const uint32_t T = K8 <= 1024u ? 1024u / K8 : 1u;
+  const uint32_t tph = K8 <= 1024u ? (uint32_t)tid / K8 : 0u;
+  const uint32_t k80 = K8 <= 1024u ? (uint32_t)tid - tph * K8 : (uint32_t)tid;
+  const uint32_t ntok = tph < T ? ((uint32_t)M > tph ? ((uint32_t)M - tph + T - 1) / T : 0u) : 0u;
+  const uint32_t nk = K8 <= 1024u ? 1u : (K8 - (uint32_t)tid + 1023u) / 1024u;   // k8 steps (K/8 > 1024)
+  u32x4 sx[NP];
+  f32x4 sr0[NP], sr1[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    // piece i: k8 step i / ntok_max ... with one token phase per thread for K/8 <= 1024
+    const uint32_t j = (uint32_t)i;
+    const bool live = K8 <= 1024u ? j < ntok : j < nk * (uint32_t)M;
+    const uint32_t m = K8 <= 1024u ? tph + j * T : j % (uint32_t)M;
+    const uint32_t k8 = K8 <= 1024u ? k80 : k80 + 1024u * (j / (uint32_t)M);
+    if (live) {
+      sx[i] = ldg128(x + (int64_t)m * ldx + (int64_t)k8 * 8);
+      if constexpr (HAS_R) {
+        sr0[i] = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8);
+        sr1[i] = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8 + 4);
+      }
+    }
+  }
+
+  // ---- first item's weights in flight
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qw + r0 * KW), (short)0, nrows * (int)KW * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scales + r0 * G), (short)0, nrows * G * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(zeros + r0 * G), (short)0, nrows * G, kBufferWord3);
+  int it = wv;
+  int tile = 0, g0 = 0, g1 = 0;
+  auto set_item = [&](int item) {
+    tile = item / ksl;
+    const int ks = item - tile * ksl;
+    g0 = (int)((int64_t)ks * G / ksl);
+    g1 = (int)((int64_t)(ks + 1) * G / ksl);
+  };
+  u32x4 wa[P];
+  uint32_t sr[P], zr[P];
+  bool have = it < nitems;                        // wave-uniform: this wave has an item
+  auto load_group = [&](int slot, int g) {
+    const int row = tile * 16 + rl;
+    const bool ok = have && g < g1 && row < nrows;
+    wa[slot] = __builtin_amdgcn_raw_buffer_load_b128(
+        wrs, ok ? (uint32_t)row * KW * 4 + (uint32_t)(4 * g + b) * 16 : kBufferOob, 0, kBufferNt);
+    sr[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, ok ? (uint32_t)(row * G + g) * 2 : kBufferOob, 0, 0);
+    zr[slot] = __builtin_amdgcn_raw_buffer_load_b8(zrs, ok ? (uint32_t)(row * G + g) : kBufferOob, 0, 0);
+  };
+  // 16-byte pieces of the row's steps, for the row's power of two
+  const int npc = (G * 2 + 15) / 16;
+  auto load_piece = [&](int pc) {
+    const int row = tile * 16 + rl;
+    return __builtin_amdgcn_raw_buffer_load_b128(
+        srs, have && row < nrows && pc < npc ? (uint32_t)row * G * 2 + 16 * pc : kBufferOob, 0, 0);
+  };
+  // branch-free (a wave without an item reads out of range): a conditional
+  // block of loads here would make every later wait count all of them
+  set_item(have ? it : 0);
+  u32x4 sp0 = load_piece(b);
+#pragma unroll
+  for (int d = 0; d < P; ++d) load_group(d, g0 + d);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- stage fp16(x r 2^p) in unpack order (0,4,2,6,1,5,3,7) with p per
+  // (token, group): the group's 16 pieces sit in 16 consecutive lanes
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const uint32_t j = (uint32_t)i;
+    const bool live = K8 <= 1024u ? j < ntok : j < nk * (uint32_t)M;
+    if (K8 <= 1024u ? j >= (((uint32_t)M + T - 1) / T) : j >= ((K8 + 1023u) / 1024u) * (uint32_t)M) break;   // uniform
+    const uint32_t m = K8 <= 1024u ? tph + j * T : j % (uint32_t)M;
+    const uint32_t k8 = K8 <= 1024u ? k80 : k80 + 1024u * (j / (uint32_t)M);
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = live ? lo_f32<DT>(sx[i][q]) : 0.0f;
+      v[2 * q + 1] = live ? hi_f32<DT>(sx[i][q]) : 0.0f;
+    }
+    if constexpr (HAS_R) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] *= live ? sr0[i][q] : 0.0f;
+        v[4 + q] *= live ? sr1[i][q] : 0.0f;
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+    amax = fmaxf(amax, quad_xor1(amax));
+    amax = fmaxf(amax, quad_xor2(amax));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x141, 0xF, 0xF, false)));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x140, 0xF, 0xF, false)));
+    const int p = pow2_exp_for(amax);
+    if (live) {
+      uint32_t h[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) h[q] = f32_to_f16_bits(ldexpf(v[q], p));
+      u32x4 o;
+      o[0] = h[0] | (h[4] << 16);
+      o[1] = h[2] | (h[6] << 16);
+      o[2] = h[1] | (h[5] << 16);
+      o[3] = h[3] | (h[7] << 16);
+      *reinterpret_cast<u32x4*>(xs + (int64_t)m * KP + (int64_t)k8 * 8) = o;
+      if ((k8 & 15u) == 0u) pinv[m * G + (k8 >> 4)] = ldexpf(1.0f, -p);
+    }
+  }
+  for (int64_t c = tid; c < (int64_t)K8; c += 1024)
+    *reinterpret_cast<u32x4*>(xs + (int64_t)M * KP + c * 8) = u32x4{0u, 0u, 0u, 0u};
+  for (int c = tid; c < G; c += 1024) pinv[M * G + c] = 0.0f;
+  __syncthreads();
+
+  // ---- items
+  const int tok = rl < M ? rl : M;               // the lane's token row (row M = 0)
+  const uint32_t xbase = (uint32_t)(tok * KP * 2);
+  for (; it < nitems; it += kScWaves) {
+    if (it != wv) {                               // later items of this wave (only when ksl == 1)
+      set_item(it);
+      sp0 = load_piece(b);
+#pragma unroll
+      for (int d = 0; d < P; ++d) load_group(d, g0 + d);
+    }
+    // row power of two from all of the row's steps
+    auto piece_max = [&](const u32x4& pv, int pc, float m) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (pc * 8 + q < G) m = fmaxf(m, f16_to_f32((pv[q >> 1] >> (16 * (q & 1))) & 0xFFFFu));
+      return m;
+    };
+    float mx = piece_max(sp0, b, 0.0f);
+    for (int pc = b + 4; pc < npc; pc += 4) mx = piece_max(load_piece(pc), pc, mx);
+    {
+      const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    }
+    int e = 0;
+    if (mx > 0.0f) {
+      int ex;
+      frexpf(mx, &ex);
+      e = -9 - ex;                               // max step 2^e in [2^-10, 2^-9)
+    }
+
+    // ring of P groups: slot d is refilled with group g + P right after group
+    // g is consumed (reads past the slice's end are out of range and return 0)
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int gb = g0; gb < g1; gb += P) {
+#pragma unroll
+      for (int d = 0; d < P; ++d) {
+        const int g = gb + d;
+        if (g < g1) {                             // wave-uniform
+          u32x4 xb[4];
+          const uint16_t* xp = reinterpret_cast<const uint16_t*>(
+              reinterpret_cast<const char*>(xs) + xbase + (uint32_t)(128 * g + 32 * b) * 2);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xb[i] = *reinterpret_cast<const u32x4*>(xp + 8 * i);
+          const float gscale = pinv[tok * G + g];
+          const float D = ldexpf(f16_to_f32(sr[d]), e);
+          const uint32_t h24 = f32_to_f16_bits(D * 16777216.0f);
+          const uint32_t h20 = f32_to_f16_bits(D * 1048576.0f);
+          const uint32_t hz = f32_to_f16_bits(-(D * (float)zr[d]));
+          const f16x2 c24 = as_f16x2(h24 | (h24 << 16));
+          const f16x2 c20 = as_f16x2(h20 | (h20 << 16));
+          const f16x2 nzd = as_f16x2(hz | (hz << 16));
+          f32x4 part = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part = mfma16h(dequant_word_f16(wa[d][i], c24, c20, nzd), xb[i], part);
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv) acc[vv] = __builtin_fmaf(part[vv], gscale, acc[vv]);
+        }
+        load_group(d, g + P);
+      }
+    }
+
+    // 16 x 16 layout: token = lane % 16, row = 4 (lane / 16) + v
+    if (ksl == 1) {
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) {
+        const int row = 4 * b + vv;
+        const int erw = __shfl(e, row);
+        if (tile * 16 + row < nrows && rl < M)
+          store_y<YDT>(y, (int64_t)rl * ldy + r0 + tile * 16 + row, ldexpf(acc[vv], -erw));
+      }
+    } else {
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) red[it * 256 + (4 * b + vv) * 16 + rl] = acc[vv];
+      if (it % ksl == 0 && b == 0) erow[tile * 16 + rl] = e;
+    }
+  }
+  if (ksl > 1) {
+    __syncthreads();
+    for (int t = tid; t < ntile * 256; t += 1024) {
+      const int tl = t >> 8, row = (t >> 4) & 15, tk = t & 15;
+      float tot = 0.0f;
+      for (int ks = 0; ks < ksl; ++ks) tot += red[(tl * ksl + ks) * 256 + row * 16 + tk];
+      if (tl * 16 + row < nrows && tk < M)
+        store_y<YDT>(y, (int64_t)tk * ldy + r0 + tl * 16 + row, ldexpf(tot, -erow[tl * 16 + row]));
+    }
+  }
+}
+
+// Pieces of 8 activations each thread stages (0 if the shape does not fit).
+inline int skinny_cu_pieces(int64_t M, int64_t K) {
+  const int64_t K8 = K >> 3;
+  const int64_t per = K8 <= 1024 ? (M + (1024 / K8) - 1) / (1024 / K8) : ((K8 + 1023) / 1024) * M;
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= kScMaxPieces ? 8 : 0;
+}
+
+// Blocks of the per-CU skinny product for (M, N, K); 0 if it does not apply.
+inline int skinny_cu_blocks(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > 16 || skinny_cu_pieces(M, K) == 0) return 0;
+  const int64_t cus = awq::device_cus();
+  const int64_t nblk = N < cus ? N : cus;
+  const int64_t rows_max = (N + nblk - 1) / nblk;
+  if (skinny_cu_lds(M, K, rows_max) > 160 * 1024 || rows_max * (K >> 1) >= (int64_t(1) << 31)) return 0;
+  return (int)nblk;
+}
+
+template <int DT, int YDT, bool HAS_R, int P = 2>
+hipError_t skinny_cu_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
+                              const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
+                              void* y, int64_t ldy, int nblk, hipStream_t st) {
+  if (nblk > N) nblk = (int)N;
+  const int64_t rows_max = (N + nblk - 1) / nblk;
+  size_t lds = skinny_cu_lds(M, K, rows_max);
+  const int np = skinny_cu_pieces(M, K);
+  if (M < 1 || M > 16 || np == 0 || lds > 160 * 1024 || rows_max * (K >> 1) >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  if (lds < 81 * 1024) lds = 81 * 1024;           // one block per compute unit
+  const dim3 grid((unsigned)nblk), block(1024);
+#define AWQ_SC(NP)                                                                                    \
+  hipLaunchKernelGGL((k_gemm_skinny_cu<DT, YDT, HAS_R, NP, P>), grid, block, lds, st, x, (int)M, K, ldx, r, \
+                     qw, scales, zeros, N, y, ldy)
+  if (np == 1) AWQ_SC(1);
+  else if (np == 2) AWQ_SC(2);
+  else if (np == 4) AWQ_SC(4);
+  else AWQ_SC(8);
+#undef AWQ_SC
+  return hipGetLastError();
+}
+
+template <int DT, int YDT, bool HAS_R, int P = kSkP>
+hipError_t skinny_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
+                           const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
+                           void* y, int64_t ldy, void* ws, hipStream_t st) {
+  const GemmWs w = gemm_ws(ws, M, N, K);
+  hipLaunchKernelGGL((k_rows_f16<DT, HAS_R, true>), dim3((unsigned)M), dim3(256), 0, st, x, K, ldx,
+                     r, w.xq, w.pm);
+  hipLaunchKernelGGL((k_gemm_skinny<YDT, P>), dim3((unsigned)((N + 15) / 16)), dim3(64 * kSkW), 0, st,
+                     w.xq, (int)M, K, w.pm, qw, scales, zeros, N, y, ldy);
+  return hipGetLastError();
+}
+
 template <int DT, int YDT>
 hipError_t w4a16_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
                           const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
                           void* y, int64_t ldy, void* ws, hipStream_t st) {
   if (M == 1 && awq::gemv1_supported(K, N))
     return awq::launch_gemv1(x, DT, K, qw, scales, zeros, N, r, y, YDT, st);
-  if (use_gemv(M, K)) {
-    if (r) return gemv_dispatch<DT, YDT, true>(x, (int)M, K, ldx, qw, scales, zeros, N, r, y, ldy, st);
-    return gemv_dispatch<DT, YDT, false>(x, (int)M, K, ldx, qw, scales, zeros, N, r, y, ldy, st);
+  if (const int nblk = skinny_cu_blocks(M, N, K)) {
+    // deeper ring for long K slices (few rows per block)
+    const int64_t rows = (N + nblk - 1) / nblk, tiles = (rows + 15) / 16;
+    const bool deep = (K / kGroup) * tiles >= 16 * 16;
+    if (r) return deep ? skinny_cu_dispatch<DT, YDT, true, 4>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, nblk, st)
+                       : skinny_cu_dispatch<DT, YDT, true, 2>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, nblk, st);
+    return deep ? skinny_cu_dispatch<DT, YDT, false, 4>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, nblk, st)
+                : skinny_cu_dispatch<DT, YDT, false, 2>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, nblk, st);
+  }
+  if (M <= kSkMaxM) {
+    if (r) return skinny_dispatch<DT, YDT, true>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, ws, st);
+    return skinny_dispatch<DT, YDT, false>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, ws, st);
   }
   if (r) return gemm_dispatch<DT, YDT, true>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, ws, st);
   return gemm_dispatch<DT, YDT, false>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, ws, st);
@@ -526,7 +737,7 @@ hipError_t w4a16_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
 namespace awq {
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || awqk::use_gemv(M, K) || (M == 1 && gemv1_supported(K, N)))
+  if (M <= 0 || N <= 0 || K <= 0 || (M == 1 && gemv1_supported(K, N)) || awqk::skinny_cu_blocks(M, N, K))
     return 0;
   return awqk::gemm_ws(nullptr, M, N, K).bytes;
 }
