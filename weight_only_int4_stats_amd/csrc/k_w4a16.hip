@@ -35,21 +35,37 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
 // matrix-core GEMM
 // ===========================================================================
 
-// Per weight row n: e_n with max_g step[n][g] * 2^e_n in [2^-10, 2^-9), so that
-// D' = step 2^e_n times 2^24 is a finite fp16 and D' (q - z) is a normal fp16.
-__global__ void k_step_exp(const uint16_t* __restrict__ scales, int64_t N, int64_t G,
-                           int* __restrict__ eexp) {
-  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Per weight row n (one wave): e_n with max_g step[n][g] 2^e_n in [2^-10, 2^-9),
+// so that D' = step 2^e_n times 2^24 is a finite fp16 and D' (q - z) a normal
+// fp16; then, for every group g, the fp16 constants of the packed-fma
+// dequantization, group-major so a block's columns are contiguous:
+//   ctab[g][n] = (fp16(D' 2^24) | fp16(D' 2^20) << 16, fp16(-D' z) twice).
+__global__ __launch_bounds__(256) void k_gemm_consts(const uint16_t* __restrict__ scales,
+                                                     const uint8_t* __restrict__ zeros, int64_t N,
+                                                     int64_t G, int* __restrict__ en,
+                                                     uint32_t* __restrict__ ctab) {
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (n >= N) return;
   float mx = 0.0f;
-  for (int64_t g = 0; g < G; ++g) mx = fmaxf(mx, f16_to_f32(scales[n * G + g]));
+  for (int64_t g = lane; g < G; g += 64) mx = fmaxf(mx, f16_to_f32(scales[n * G + g]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   int e = 0;
   if (mx > 0.0f) {
     int ex;
     frexpf(mx, &ex);        // mx < 2^ex
-    e = -9 - ex;            // mx * 2^e in [2^-10, 2^-9): D' 2^24 stays finite in fp16
+    e = -9 - ex;            // mx 2^e in [2^-10, 2^-9)
   }
-  eexp[n] = e;
+  if (lane == 0) en[n] = e;
+  for (int64_t g = lane; g < G; g += 64) {
+    const float D = ldexpf(f16_to_f32(scales[n * G + g]), e);   // exact: power-of-two scaling
+    const uint32_t h24 = f32_to_f16_bits(D * 16777216.0f);
+    const uint32_t h20 = f32_to_f16_bits(D * 1048576.0f);
+    const uint32_t hz = f32_to_f16_bits(-(D * (float)zeros[n * G + g]));
+    ctab[(g * N + n) * 2] = h24 | (h20 << 16);
+    ctab[(g * N + n) * 2 + 1] = hz | (hz << 16);
+  }
 }
 
 __device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const f32x16& c) {
@@ -77,51 +93,120 @@ __device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 c24, f16x2 c
 }
 
 // 256 x 256 output tile per block of 8 waves (2 along m x 4 along n, each wave
-// 128 x 64 = 4 x 2 blocks of 32 x 32), 64 k per LDS stage, two LDS stages so
-// that the next stage's global loads are in flight during the current
-// stage's matrix-core work (one barrier per stage).
+// 128 x 64 = 4 x 2 blocks of 32 x 32), 64 k per stage, three LDS stages
+// filled by LDS DMA (buffer_load ... lds) two stages ahead of the matrix-core
+// work:
+//   A  256 rows x 64 k of fp16 activations, row r's 16-byte chunk c stored at
+//      chunk c ^ (r mod 8) (the 32 rows of a fragment read hit all banks)
+//   B  256 columns x 8 packed words, as in memory
+//   C  256 columns of dequantization constants (8 bytes each)
+// Tiles are ordered for the chip's eight L2 slices: block i runs on slice
+// i mod 8, so slice x takes the x-th eighth of the tiles in m-major order and
+// its concurrent blocks share activation stages in its L2.
 constexpr int kMT = 256;                // tile rows (m)
 constexpr int kNT = 256;                // tile columns (n)
 constexpr int kBK = 64;                 // k per stage
-constexpr int kALd = kBK + 8;           // x tile row stride (16-bit elements)
-constexpr int kBLd = 12;                // packed-word tile row stride (words; 8 used)
+constexpr int kXcds = 8;                // L2 slices (block i -> slice i mod 8)
+constexpr int kAStage = kMT * kBK * 2;  // 32 KB
+constexpr int kBStage = kNT * 8 * 4;    // 8 KB
+constexpr int kCStage = kNT * 8;        // 2 KB
+constexpr int kStage = kAStage + kBStage + kCStage;
+
+inline int64_t gemm_blocks(int64_t M, int64_t N) {
+  const int64_t T = ((N + kNT - 1) / kNT) * ((M + kMT - 1) / kMT);
+  return kXcds * ((T + kXcds - 1) / kXcds);
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: base address, stride 0, size in bytes, untyped dwords.
+__device__ __forceinline__ i32x4 rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = (int32_t)(uint32_t)a;
+  r[1] = (int32_t)((uint32_t)(a >> 32) & 0xFFFFu);
+  r[2] = (int32_t)bytes;
+  r[3] = kBufferWord3;
+  return r;
+}
+
+// 16 bytes per lane from a raw buffer into LDS at lds + 16 lane (LDS DMA; an
+// offset past the buffer's end writes 0).  The copy writes no register.  It is
+// issued from asm so that the compiler, which cannot tell which LDS stage a
+// copy fills, adds no wait of its own before the other stages' LDS reads: the
+// caller waits for the copies explicitly (vector memory counter, in order)
+// before the barrier that publishes a stage.
+// m0 (the LDS base of the copy) is saved and restored around it.
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void dma16_nt(const i32x4& r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen nt lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
 
 template <int YDT>
 __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, int64_t M, int64_t K,
                                               const int* __restrict__ pm,
                                               const uint32_t* __restrict__ qw,
-                                              const uint16_t* __restrict__ scales,
-                                              const uint8_t* __restrict__ zeros,
+                                              const uint32_t* __restrict__ ctab,
                                               const int* __restrict__ en, int64_t N,
                                               void* __restrict__ y, int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kMT * kALd];
-  __shared__ __attribute__((aligned(16))) uint32_t Bq[2][kNT * kBLd];
-  __shared__ __attribute__((aligned(16))) uint32_t Bc[2][kNT * 4];   // D'2^24, D'2^20, -D'z (fp16 pairs)
+  // three LDS arrays, the loop unrolled by three: each stage is a known array
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[kStage];
+
+  // ---- tile of this block
+  const int64_t ntile = (N + kNT - 1) / kNT, mtile = (M + kMT - 1) / kMT, T = ntile * mtile;
+  const int64_t per = (T + kXcds - 1) / kXcds;
+  const int64_t slot = blockIdx.x / kXcds;
+  const int64_t t = (int64_t)(blockIdx.x % kXcds) * per + slot;
+  if (slot >= per || t >= T) return;
+  const int64_t mt = t / ntile;
+  const int64_t m0 = mt * kMT;
+  const int64_t n0 = (t - mt * ntile) * kNT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
-  const int64_t m0 = (int64_t)blockIdx.y * kMT;
-  const int64_t n0 = (int64_t)blockIdx.x * kNT;
   const int64_t G = K / kGroup;
   const int64_t S = K / kBK;
-  const int bcol = tid & 255;                    // column this thread stages (B side)
-  const bool bcol_ok = n0 + bcol < N;
-  const int64_t bcol_c = bcol_ok ? n0 + bcol : 0;
-  const int ecol = bcol_ok ? en[bcol_c] : 0;
+  const int rows = (int)(M - m0 < kMT ? M - m0 : kMT);
+  const int cols = (int)(N - n0 < kNT ? N - n0 : kNT);
+  const i32x4 ars = rsrc4(xq + m0 * K, (uint32_t)(rows * K * 2));
+  const i32x4 brs = rsrc4(qw + n0 * (K >> 3), (uint32_t)(cols * (K >> 1)));
+  const i32x4 crs = rsrc4(ctab + n0 * 2, (uint32_t)(((G - 1) * N + cols) * 8));
 
-  // per-thread source pointers (advanced by k0 each stage)
-  const uint16_t* asrc[4];
+  // A copy j (0..31) fills LDS bytes [1024 j, 1024 j + 1024) = rows 8 j .. 8 j + 7;
+  // wave w issues j = 4 w + u.  Lane i: row r = 8 j + i / 8 at LDS chunk i % 8,
+  // which holds global chunk (i % 8) ^ (r % 8).
+  uint32_t aoff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 512 * i;
-    const int64_t mr = m0 + (c >> 3);
-    asrc[i] = xq + (mr < M ? mr : 0) * K + (c & 7) * 8;
+  for (int u = 0; u < 4; ++u) {
+    const int r = 8 * (4 * wv + u) + (lane >> 3);
+    aoff[u] = (uint32_t)(r * K * 2 + (((lane & 7) ^ (r & 7)) * 16));
   }
-  const uint32_t* bsrc = qw + bcol_c * (K >> 3);
-  const uint16_t* ssrc = scales + bcol_c * G;
-  const uint8_t* zsrc = zeros + bcol_c * G;
+  // B: wave w copies columns 32 w .. 32 w + 31 (two lanes per column)
+  const uint32_t boff = (uint32_t)((32 * wv + (lane >> 1)) * (K >> 1) + (lane & 1) * 16);
+  // C: waves 0 and 1 copy 128 columns each (two columns per lane)
+  const uint32_t coff = (uint32_t)((wv * 128 + lane * 2) * 8);
+
+  auto issue = [&](int64_t s, const uint8_t* base) {
+    const uint32_t k0 = (uint32_t)(s * kBK);
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(base));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dma16(ars, lb + (4 * wv + u) * 1024, aoff[u], k0 * 2);
+    dma16_nt(brs, lb + kAStage + wv * 1024, boff, k0 >> 1);
+    if (wv < 2) dma16(crs, lb + kAStage + kBStage + wv * 1024, coff, (uint32_t)((k0 / kGroup) * N * 8));
+  };
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -131,75 +216,29 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  u32x4 ra[4];              // staged x chunks
-  u32x4 rb0, rb1;           // staged packed words (threads < 256)
-  uint32_t rs = 0, rz = 0;  // staged step / zero (threads >= 256)
-
-  auto gload = [&](int64_t s) {
-    const int64_t k0 = s * kBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = ldg128(asrc[i] + k0);
-    if (tid < 256) {
-      rb0 = ldg128_stream(bsrc + (k0 >> 3));
-      rb1 = ldg128_stream(bsrc + (k0 >> 3) + 4);
-    } else {
-      rs = ssrc[k0 / kGroup];
-      rz = zsrc[k0 / kGroup];
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 512 * i;
-      // rows past M hold row 0's data: output rows are independent and those are never stored
-      *reinterpret_cast<u32x4*>(&As[buf][(c >> 3) * kALd + (c & 7) * 8]) = ra[i];
-    }
-    if (tid < 256) {
-      // word order (0,2,4,6 | 1,3,5,7): a lane's four k steps are one 16-byte read
-      // columns past N hold column 0's words; their outputs are never stored
-      const u32x4 e = {rb0[0], rb0[2], rb1[0], rb1[2]};
-      const u32x4 o = {rb0[1], rb0[3], rb1[1], rb1[3]};
-      *reinterpret_cast<u32x4*>(&Bq[buf][bcol * kBLd]) = e;
-      *reinterpret_cast<u32x4*>(&Bq[buf][bcol * kBLd + 4]) = o;
-    } else {
-      u32x4 c = {0u, 0u, 0u, 0u};
-      if (bcol_ok) {
-        const float D = ldexpf(f16_to_f32(rs), ecol);        // D' (exact: power-of-two scaling)
-        const uint32_t h24 = f32_to_f16_bits(D * 16777216.0f);
-        const uint32_t h20 = f32_to_f16_bits(D * 1048576.0f);
-        const uint32_t hz = f32_to_f16_bits(-(D * (float)rz));
-        c[0] = h24 | (h24 << 16);
-        c[1] = h20 | (h20 << 16);
-        c[2] = hz | (hz << 16);
-      }
-      *reinterpret_cast<u32x4*>(&Bc[buf][bcol * 4]) = c;
-    }
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int64_t s = 0; s < S; ++s) {
-    const int buf = (int)(s & 1);
-    if (s + 1 < S) gload(s + 1);
+  auto compute = [&](const uint8_t* base) {
     f16x2 c24[2], c20[2], nzd[2];
     u32x4 bw[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int col = wn * 64 + nb * 32 + (lane & 31);
-      const u32x4 c = *reinterpret_cast<const u32x4*>(&Bc[buf][col * 4]);
-      c24[nb] = as_f16x2(c[0]);
-      c20[nb] = as_f16x2(c[1]);
-      nzd[nb] = as_f16x2(c[2]);
-      bw[nb] = *reinterpret_cast<const u32x4*>(&Bq[buf][col * kBLd + (lane >> 5) * 4]);
+      const uint2 c = *reinterpret_cast<const uint2*>(base + kAStage + kBStage + col * 8);
+      c24[nb] = as_f16x2((c.x & 0xFFFFu) | (c.x << 16));
+      c20[nb] = as_f16x2((c.x >> 16) | (c.x & 0xFFFF0000u));
+      nzd[nb] = as_f16x2(c.y);
+      // words [col][8]: this lane half takes words (lane / 32) + 2 ks, ks = 0..3
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(base + kAStage + col * 32);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(base + kAStage + col * 32 + 16);
+      bw[nb] = (lane >> 5) ? u32x4{lo[1], lo[3], hi[1], hi[3]} : u32x4{lo[0], lo[2], hi[0], hi[2]};
     }
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       u32x4 a[4], b[2];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        a[mb] = *reinterpret_cast<const u32x4*>(
-            &As[buf][(wm * 128 + mb * 32 + (lane & 31)) * kALd + ks * 16 + 8 * (lane >> 5)]);
+      for (int mb = 0; mb < 4; ++mb) {
+        const int r = wm * 128 + mb * 32 + (lane & 31);
+        a[mb] = *reinterpret_cast<const u32x4*>(base + r * 128 + (((2 * ks + (lane >> 5)) ^ (r & 7)) * 16));
+      }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) b[nb] = dequant_word_f16(bw[nb][ks], c24[nb], c20[nb], nzd[nb]);
 #pragma unroll
@@ -207,8 +246,29 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32h(a[mb], b[nb], acc[mb][nb]);
     }
-    if (s + 1 < S) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  // stages 0 and 1 in flight; copies per wave and stage: 5 (6 for waves 0, 1)
+  issue(0, lds0);
+  issue(1, lds1);
+  const bool six = wv < 2;
+  auto step = [&](int64_t s, const uint8_t* cur, const uint8_t* nxt2) {
+    // stage s landed: all copies but stage s + 1's (s_waitcnt encoding on this
+    // target: vmcnt[3:0] | expcnt 7 << 4 | lgkmcnt 15 << 8)
+    if (s + 1 < S) {
+      if (six) __builtin_amdgcn_s_waitcnt(0x0F76);
+      else __builtin_amdgcn_s_waitcnt(0x0F75);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    __builtin_amdgcn_s_barrier();
+    if (s + 2 < S) issue(s + 2, nxt2);
+    compute(cur);
+  };
+  for (int64_t s = 0; s < S; s += 3) {
+    step(s, lds0, lds2);
+    if (s + 1 < S) step(s + 1, lds1, lds0);
+    if (s + 2 < S) step(s + 2, lds2, lds1);
   }
 
   // 32x32 accumulator layout: column = lane % 32, row = 8 (v / 4) + 4 (lane / 32) + v % 4
@@ -365,6 +425,7 @@ struct GemmWs {
   uint16_t* xq;
   int* pm;
   int* en;
+  uint32_t* ctab;
   size_t bytes;
 };
 
@@ -380,6 +441,7 @@ inline GemmWs gemm_ws(void* ws, int64_t M, int64_t N, int64_t K) {
   w.xq = (uint16_t*)take((size_t)M * K * 2);
   w.pm = (int*)take((size_t)M * 4);
   w.en = (int*)take((size_t)N * 4);
+  w.ctab = (uint32_t*)take((size_t)N * (K / kGroup) * 8);
   w.bytes = off;
   return w;
 }
@@ -391,11 +453,10 @@ hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
   const GemmWs w = gemm_ws(ws, M, N, K);
   hipLaunchKernelGGL((k_rows_f16<DT, HAS_R, true>), dim3((unsigned)M), dim3(256), 0, st, x, K, ldx,
                      r, w.xq, w.pm);
-  hipLaunchKernelGGL(k_step_exp, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, scales, N,
-                     K / kGroup, w.en);
-  const dim3 grid((unsigned)((N + kNT - 1) / kNT), (unsigned)((M + kMT - 1) / kMT));
-  hipLaunchKernelGGL((k_gemm<YDT>), grid, dim3(512), 0, st, w.xq, M, K, w.pm, qw, scales, zeros,
-                     w.en, N, y, ldy);
+  hipLaunchKernelGGL(k_gemm_consts, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, scales, zeros, N,
+                     K / kGroup, w.en, w.ctab);
+  hipLaunchKernelGGL((k_gemm<YDT>), dim3((unsigned)gemm_blocks(M, N)), dim3(512), 0, st, w.xq, M, K, w.pm,
+                     qw, w.ctab, w.en, N, y, ldy);
   return hipGetLastError();
 }
 
