@@ -80,6 +80,10 @@ typedef enum awq_op {
 #define AWQ_GROUP 128
 #define AWQ_MAX_ALPHA 64
 #define AWQ_MAX_K 131072
+/* Largest calibration row stride (elements) of awq_search_scales: 256 rows of
+ * it must span less than 2^31 bytes (the error product addresses a tile of
+ * tokens with 32-bit offsets). */
+#define AWQ_MAX_LDX_SEARCH 4194304
 
 /* Version of this interface (incremented on any signature change). */
 int awq_abi_version(void);
@@ -125,7 +129,7 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
  *   best        = lowest i with the minimal loss (NaN losses are skipped)
  *
  *   w           [N][K] fp16 or bf16 (dt), contiguous
- *   x_calib     [T][ldx] same dtype as w
+ *   x_calib     [T][ldx] same dtype as w; ldx <= AWQ_MAX_LDX_SEARCH
  *   mean_abs    [K] float (output of awq_act_stats)
  *   alphas      [n_alpha] double, device memory
  *   n_alpha     1..AWQ_MAX_ALPHA

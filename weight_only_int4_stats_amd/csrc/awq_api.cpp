@@ -67,7 +67,7 @@ awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
   if (group_size != AWQ_GROUP) return AWQ_ERR_UNSUPPORTED;
   if (n_alpha < 1 || n_alpha > AWQ_MAX_ALPHA) return AWQ_ERR_UNSUPPORTED;
   if (N <= 0 || K <= 0 || T <= 0 || ldx < K || K % AWQ_GROUP != 0) return AWQ_ERR_SHAPE;
-  if (K > AWQ_MAX_K || N > 0x7FFFFFFF) return AWQ_ERR_UNSUPPORTED;
+  if (K > AWQ_MAX_K || N > 0x7FFFFFFF || ldx > AWQ_MAX_LDX_SEARCH) return AWQ_ERR_UNSUPPORTED;
   if (ldx % 8 != 0 || !aligned16(w) || !aligned16(x_calib) || !aligned16(mean_abs))
     return AWQ_ERR_ALIGN;
   if (!ws || ws_bytes < awq::search_ws_bytes((int)dt, N, K, T, n_alpha) || !aligned256(ws))

@@ -167,4 +167,61 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// ---- matrix cores and LDS DMA ----------------------------------------------
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// D += A B for one 32 x 32 x 16 fp16 block (fp32 accumulation).  A lane holds
+// 8 k of row l % 32 (k half l / 32); the result lane holds column l % 32 and
+// rows 8 (v / 4) + 4 (l / 32) + v % 4 of its 16 values.
+__device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Raw buffer descriptor: base address, stride 0, size in bytes, untyped dwords.
+// The arguments must be the same in every lane; the words are taken from the
+// first active lane so that the descriptor lives in scalar registers.
+__device__ __forceinline__ i32x4 rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+  r[3] = kBufferWord3;
+  return r;
+}
+
+// 16 bytes per lane from a raw buffer into LDS at lds + 16 lane (LDS DMA; an
+// offset past the buffer's end writes 0).  The copy writes no register.  It is
+// issued from asm so that the compiler, which cannot tell which LDS stage a
+// copy fills, adds no wait of its own before the other stages' LDS reads: the
+// caller waits for the copies explicitly (vector memory counter, in order)
+// before the barrier that publishes a stage.
+// m0 (the LDS base of the copy) is saved and restored around it.
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void dma16_nt(const i32x4& r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen nt lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// Workgroup barrier that waits for nothing: the LDS DMA copies a wave has in
+// flight are waited for explicitly (waitcnt_vm) before it, where __syncthreads
+// would wait for all of them.  The memory clobber keeps the compiler from
+// moving LDS reads across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt immediates on this target: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] in bits [15:14].  waitcnt_vm waits for the vector memory counter
+// only (n <= 63), waitcnt_vm_lgkm0 also for every LDS access of the wave.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
 }  // namespace awqk

@@ -12,7 +12,7 @@
 //                   a first pass finds max|E| of the row, a second writes
 //                   E * 2^p (p chosen so the row fits fp16's normal range) as
 //                   fp16 into the workspace, with p per row.
-//   2. k_err_contract  128x128 tiles of C = X E'^T with fp16 MFMA (fp32
+//   2. k_err_contract  256x256 tiles of C = X E'^T with fp16 MFMA (fp32
 //                   accumulation); the epilogue squares and sums the tile,
 //                   undoes the powers of two in double, and writes one double
 //                   per tile.  bf16 calibration tokens are first rounded to
@@ -132,122 +132,233 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
 // ---------------------------------------------------------------------------
 // contraction C = X E'^T, sum of squares per tile
 // ---------------------------------------------------------------------------
-constexpr int kCT = 256;        // tile edge (tokens and rows)
-constexpr int kCBK = 64;        // k per LDS stage
-constexpr int kCLd = kCBK + 8;  // LDS row stride in 16-bit elements (padding vs bank conflicts)
+// 256 tokens x 256 error rows per block of 4 waves, one per SIMD (2 along
+// tokens x 2 along rows; each wave 128 x 128 = 4 x 4 blocks of 32 x 32, whose
+// 256 accumulators per lane sit in the accumulation registers).  32 k per
+// stage; four LDS stages, filled by LDS DMA (buffer_load ... lds) three stages
+// ahead of the matrix-core work.  A stage holds both operands, 256 rows x 32 k
+// of fp16 each (64 bytes a row, a quarter of the 64 banks); row r's 16-byte
+// chunk c sits at chunk c ^ ((r / 4) mod 4), so the 16 rows that one 16-lane
+// pass of a 128-bit read touches land on 16 different bank slots.
+// Inside a wave the operand fragments of the next 16 k are read from LDS
+// while the 16 products of the current 16 k run (two register sets).
+// Tile order: block i runs on L2 slice i mod 8 and slice x takes the x-th
+// eighth of the tiles in band order (bands of 8 error-row tiles; inside a band
+// token tiles, then the band's row tiles), so the 32 blocks a slice runs at
+// once share 4 token tiles and 8 error-row tiles through its L2.
+constexpr int kCT = 256;                 // tile edge (tokens and rows)
+constexpr int kCBK = 32;                 // k per stage
+constexpr int kCOp = kCT * kCBK * 2;     // bytes per operand and stage (16 KB)
+constexpr int kCWaves = 4;
+constexpr int kCCopies = 2 * (kCOp / 1024) / kCWaves;   // 1 KB copies per wave and stage (8)
+constexpr int kCBand = 8;                // error-row tiles per band
+constexpr int kCXcds = 8;                // L2 slices (block i -> slice i mod 8)
 
-__device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+inline int64_t contract_blocks(int64_t T, int64_t N) {
+  const int64_t tiles = ((T + kCT - 1) / kCT) * ((N + kCT - 1) / kCT);
+  return kCXcds * ((tiles + kCXcds - 1) / kCXcds);
 }
 
-// 256 tokens x 256 error rows per block of 8 waves (2 along tokens x 4 along
-// rows; each wave 128 x 64 = 4 x 2 blocks of 32 x 32), 64 k per LDS stage, two
-// stages so the next stage's loads overlap the current matrix-core work.
+struct Frags {
+  u32x4 a[4], b[4];
+};
+
 // px: per-token power of two of the fp16 tokens (NULL: tokens unscaled).
-__global__ __launch_bounds__(512) void k_err_contract(const uint16_t* __restrict__ X, int64_t T,
+// partial[ty * gx + tx] = sum of squares of tile (token tile ty, row tile tx).
+__global__ __launch_bounds__(256) void k_err_contract(const uint16_t* __restrict__ X, int64_t T,
                                                       int64_t ldx, const int* __restrict__ px,
                                                       const uint16_t* __restrict__ E, int64_t N,
                                                       int64_t K, const int* __restrict__ pexp,
                                                       double* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kCT * kCLd];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kCT * kCLd];
-  __shared__ double wsum[8];
+  // four LDS arrays, the loop unrolled by four: each stage is a known array
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[2 * kCOp];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[2 * kCOp];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[2 * kCOp];
+  __shared__ __attribute__((aligned(16))) uint8_t lds3[2 * kCOp];
+  __shared__ double wsum[kCWaves];
+
+  // ---- tile of this block
+  const int64_t gx = (N + kCT - 1) / kCT, gy = (T + kCT - 1) / kCT, tiles = gx * gy;
+  const int64_t per = (tiles + kCXcds - 1) / kCXcds;
+  const int64_t slot = blockIdx.x / kCXcds;
+  const int64_t o = (int64_t)(blockIdx.x % kCXcds) * per + slot;
+  if (slot >= per || o >= tiles) return;
+  const int64_t band = o / (gy * kCBand);
+  const int64_t rb = o - band * gy * kCBand;
+  const int64_t bw = gx - band * kCBand < kCBand ? gx - band * kCBand : kCBand;
+  const int64_t ty = rb / bw;
+  const int64_t tx = band * kCBand + (rb - ty * bw);
+  const int64_t t0 = ty * kCT;   // tokens (MFMA rows)
+  const int64_t n0 = tx * kCT;   // rows of E (MFMA columns)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int wm = wv >> 2, wn = wv & 3;
-  const int64_t n0 = (int64_t)blockIdx.x * kCT;   // rows of E (MFMA columns)
-  const int64_t t0 = (int64_t)blockIdx.y * kCT;   // tokens (MFMA rows)
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
   const int64_t S = K / kCBK;
+  const int64_t rows = T - t0 < kCT ? T - t0 : kCT;
+  const int64_t cols = N - n0 < kCT ? N - n0 : kCT;
+  // rows past T / N fall outside the descriptors and arrive as zeros
+  const i32x4 ars = rsrc4(X + t0 * ldx, (uint32_t)((rows - 1) * ldx * 2 + K * 2));
+  const i32x4 brs = rsrc4(E + n0 * K, (uint32_t)(cols * K * 2));
 
-  // per-thread sources: rows past T / N read row 0 and are excluded in the epilogue
-  const uint16_t* asrc[4];
-  const uint16_t* bsrc[4];
+  // Copy j (0..15) of an operand fills its bytes [1024 j, 1024 j + 1024) =
+  // rows 16 j .. 16 j + 15; wave w issues j = 4 w + u.  Lane i: row
+  // r = 16 j + i / 4 at chunk i % 4, which holds global chunk (i % 4) ^ ((r / 4) % 4).
+  uint32_t aoff[4], boff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 512 * i;
-    const int64_t t = t0 + (c >> 3), n = n0 + (c >> 3);
-    asrc[i] = X + (t < T ? t : 0) * ldx + (c & 7) * 8;
-    bsrc[i] = E + (n < N ? n : 0) * K + (c & 7) * 8;
+  for (int u = 0; u < 4; ++u) {
+    const int r = 16 * (4 * wv + u) + (lane >> 2);
+    const uint32_t ch = (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
+    aoff[u] = (uint32_t)(r * ldx * 2) + ch;
+    boff[u] = (uint32_t)(r * K * 2) + ch;
   }
-
-  f32x16 acc[4][2];
+  // copy u (0..7) of stage s into the stage array at base: A copies 0..3, B 4..7
+  auto copy = [&](int64_t s, const uint8_t* base, int u) {
+    const uint32_t kb = (uint32_t)(s * kCBK * 2);
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(base));
+    if (u < 4) dma16(ars, lb + (4 * wv + u) * 1024, aoff[u], kb);
+    else dma16(brs, lb + kCOp + (4 * wv + u - 4) * 1024, boff[u - 4], kb);
+  };
+  auto issue = [&](int64_t s, const uint8_t* base) {
+#pragma unroll
+    for (int u = 0; u < kCCopies; ++u) copy(s, base, u);
+  };
+  f32x16 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int64_t s) {
-    const int64_t k0 = s * kCBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ldg128(asrc[i] + k0);
-      rb[i] = ldg128(bsrc[i] + k0);
+  // fragment i (0..7) of 16 k (half ks of a stage), in the order the products
+  // use them: a0 b0 b1 b2 b3 a1 a2 a3 (A lane = token row, B lane = E row,
+  // both 8 k of chunk 2 ks + lane / 32)
+  auto read1 = [&](const uint8_t* base, int ks, Frags& f, int i) {
+    const int c = 2 * ks + (lane >> 5);
+    if (i >= 1 && i <= 4) {
+      const int r = wn * 128 + (i - 1) * 32 + (lane & 31);
+      f.b[i - 1] = *reinterpret_cast<const u32x4*>(base + kCOp + r * 64 + ((c ^ ((r >> 2) & 3)) * 16));
+    } else {
+      const int mb = i == 0 ? 0 : i - 4;
+      const int r = wm * 128 + mb * 32 + (lane & 31);
+      f.a[mb] = *reinterpret_cast<const u32x4*>(base + r * 64 + ((c ^ ((r >> 2) & 3)) * 16));
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 512 * i;
-      const int off = (c >> 3) * kCLd + (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(&As[buf][off]) = ra[i];
-      *reinterpret_cast<u32x4*>(&Bs[buf][off]) = rb[i];
-    }
+  // products 2 i and 2 i + 1 of the 16 (token block i / 2, row blocks 2 (i % 2) + 0, 1)
+  auto mma2 = [&](const Frags& f, int i) {
+    const int mb = i >> 1, nb = (i & 1) * 2;
+    acc[mb][nb] = mfma32h(f.a[mb], f.b[nb], acc[mb][nb]);
+    acc[mb][nb + 1] = mfma32h(f.a[mb], f.b[nb + 1], acc[mb][nb + 1]);
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int64_t s = 0; s < S; ++s) {
-    const int buf = (int)(s & 1);
-    if (s + 1 < S) gload(s + 1);
+  // K is a multiple of 128, so S is a multiple of 4 (and at least 4): the
+  // loop below runs whole groups of four stages and the last group is peeled,
+  // which keeps every wait count a constant.
+  Frags f0, f1;
+  // prologue: stages 0..2 in flight, stage 0 published, stage 3 issued
+  issue(0, lds0);
+  issue(1, lds1);
+  issue(2, lds2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCCopies));
+  lds_barrier();
+  issue(3, lds3);
 #pragma unroll
-    for (int ks = 0; ks < kCBK / 16; ++ks) {
-      const int kk = ks * 16 + 8 * (lane >> 5);
-      u32x4 a[4], b[2];
+  for (int i = 0; i < 8; ++i) read1(lds0, 0, f0, i);
+
+  // Stage s in two halves of 16 products.  First half: the products of f0
+  // (first 16 k), with the second 16 k read into f1 one fragment per two
+  // products.  Then stage s + 1 is published, once all but the `ahead` stages
+  // copied after it have landed and every LDS read of the wave has returned
+  // (so all of stage s has been read); second half: the products of f1, with
+  // one copy of stage s + 4 into stage s's array and one fragment of stage
+  // s + 1's first 16 k per two products.  Issuing copies and reads between
+  // products keeps the matrix pipe fed while they queue; scheduling barriers
+  // hold that order.
+  auto stage = [&](int64_t s, const uint8_t* cur, const uint8_t* nxt, int ahead, bool refill) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        a[mb] = *reinterpret_cast<const u32x4*>(&As[buf][(wm * 128 + mb * 32 + (lane & 31)) * kCLd + kk]);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        b[nb] = *reinterpret_cast<const u32x4*>(&Bs[buf][(wn * 64 + nb * 32 + (lane & 31)) * kCLd + kk]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32h(a[mb], b[nb], acc[mb][nb]);
+    for (int i = 0; i < 8; ++i) {
+      mma2(f0, i);
+      read1(cur, 1, f1, i);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (s + 1 < S) lstore(buf ^ 1);
-    __syncthreads();
+    if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kCCopies));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCCopies));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      mma2(f1, i);
+      if (refill) copy(s + 4, cur, i);
+      read1(nxt, 0, f0, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int64_t s = 0;
+  for (; s < S - 4; s += 4) {
+    stage(s, lds0, lds1, 2, true);
+    stage(s + 1, lds1, lds2, 2, true);
+    stage(s + 2, lds2, lds3, 2, true);
+    stage(s + 3, lds3, lds0, 2, true);
   }
-
-  // epilogue: every value a lane holds for block nb belongs to E row n;
-  // token row of value v in block mb: 8 (v / 4) + 4 (lane / 32) + v % 4
-  double tot = 0.0;
+  stage(s, lds0, lds1, 2, false);
+  stage(s + 1, lds1, lds2, 1, false);
+  stage(s + 2, lds2, lds3, 0, false);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int64_t n = n0 + wn * 64 + nb * 32 + (lane & 31);
-    if (n >= N) continue;
-    double ssq = 0.0;
+  for (int i = 0; i < 8; ++i) {
+    mma2(f0, i);
+    read1(lds3, 1, f1, i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mma2(f1, i);
+
+  // epilogue.  Lane value v of block (mb, nb) belongs to E row
+  // n = n0 + wn 128 + nb 32 + lane % 32 and token
+  // t = t0 + wm 128 + mb 32 + 8 (v / 4) + 4 (lane / 32) + v % 4.  Tokens past T
+  // were copied as zeros, so their products are 0 and need no mask (the token
+  // scale index is clamped); columns past N are skipped.
+  // the power of two of each E row this lane's results belong to
+  int pe[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t n = n0 + wn * 128 + nb * 32 + (lane & 31);
+    pe[nb] = pexp[n < N ? n : N - 1];
+  }
+  double tot = 0.0;
+  if (px == nullptr) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      float q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) q[v & 3] = fmaf(acc[mb][nb][v], acc[mb][nb][v], q[v & 3]);
+      const double ssq = ((double)q[0] + (double)q[1]) + ((double)q[2] + (double)q[3]);
+      if (n0 + wn * 128 + nb * 32 + (lane & 31) < N) tot += ldexp(ssq, -2 * pe[nb]);
+    }
+  } else {
+    double ssq[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      float part = 0.0f;
+      int ps[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t t = t0 + wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (t < T) {
-          const float c = acc[mb][nb][v];
-          if (px == nullptr) part += c * c;
-          else ssq += ldexp((double)c * (double)c, -2 * px[t]);
-        }
+        ps[v] = px[t < T ? t : T - 1];
       }
-      ssq += (double)part;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const double c = (double)acc[mb][nb][v];
+          ssq[nb] += ldexp(c * c, -2 * ps[v]);
+        }
     }
-    tot += ldexp(ssq, -2 * pexp[n]);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      if (n0 + wn * 128 + nb * 32 + (lane & 31) < N) tot += ldexp(ssq[nb], -2 * pe[nb]);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
@@ -255,8 +366,8 @@ __global__ __launch_bounds__(512) void k_err_contract(const uint16_t* __restrict
   __syncthreads();
   if (tid == 0) {
     double t = 0.0;
-    for (int w = 0; w < 8; ++w) t += wsum[w];
-    partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = t;
+    for (int w = 0; w < kCWaves; ++w) t += wsum[w];
+    partial[ty * gx + tx] = t;
   }
 }
 
@@ -380,7 +491,7 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
     else
       hipLaunchKernelGGL(k_err_gen<DT_BF16>, dim3((unsigned)N), dim3(256), 0, st,
                          (const uint16_t*)w, N, K, s_i, sw.E, sw.pexp);
-    hipLaunchKernelGGL(k_err_contract, dim3((unsigned)gx, (unsigned)gy), dim3(512), 0, st, Xop, T,
+    hipLaunchKernelGGL(k_err_contract, dim3((unsigned)contract_blocks(T, N)), dim3(256), 0, st, Xop, T,
                        ldop, px, sw.E, N, K, sw.pexp, sw.partial);
     hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial, gx * gy, tn,
                        sw.losses + i);

@@ -68,10 +68,6 @@ __global__ __launch_bounds__(256) void k_gemm_consts(const uint16_t* __restrict_
   }
 }
 
-__device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
 
 // One packed word (codes of k = 8c + j in bits 4j..4j+3) -> 8 fp16 operands
 // D' (q - z), k order (0,4 | 2,6 | 1,5 | 3,7).  The masked nibbles are read
@@ -97,8 +93,11 @@ __device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 c24, f16x2 c
 // filled by LDS DMA (buffer_load ... lds) two stages ahead of the matrix-core
 // work:
 //   A  256 rows x 64 k of fp16 activations, row r's 16-byte chunk c stored at
-//      chunk c ^ (r mod 8) (the 32 rows of a fragment read hit all banks)
-//   B  256 columns x 8 packed words, as in memory
+//      chunk c ^ ((r / 2) mod 8): a 128-byte row is half the width of the 64
+//      banks, so the 16 rows that one 16-lane pass of a 128-bit read touches
+//      land on 16 different 16-byte bank slots
+//   B  256 columns x 8 packed words; per 32 columns the first 16 bytes of
+//      each column, then the last 16 (again 16 lanes -> 16 bank slots)
 //   C  256 columns of dequantization constants (8 bytes each)
 // Tiles are ordered for the chip's eight L2 slices: block i runs on slice
 // i mod 8, so slice x takes the x-th eighth of the tiles in m-major order and
@@ -115,40 +114,6 @@ constexpr int kStage = kAStage + kBStage + kCStage;
 inline int64_t gemm_blocks(int64_t M, int64_t N) {
   const int64_t T = ((N + kNT - 1) / kNT) * ((M + kMT - 1) / kMT);
   return kXcds * ((T + kXcds - 1) / kXcds);
-}
-
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor: base address, stride 0, size in bytes, untyped dwords.
-__device__ __forceinline__ i32x4 rsrc4(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  i32x4 r;
-  r[0] = (int32_t)(uint32_t)a;
-  r[1] = (int32_t)((uint32_t)(a >> 32) & 0xFFFFu);
-  r[2] = (int32_t)bytes;
-  r[3] = kBufferWord3;
-  return r;
-}
-
-// 16 bytes per lane from a raw buffer into LDS at lds + 16 lane (LDS DMA; an
-// offset past the buffer's end writes 0).  The copy writes no register.  It is
-// issued from asm so that the compiler, which cannot tell which LDS stage a
-// copy fills, adds no wait of its own before the other stages' LDS reads: the
-// caller waits for the copies explicitly (vector memory counter, in order)
-// before the barrier that publishes a stage.
-// m0 (the LDS base of the copy) is saved and restored around it.
-__device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  uint32_t keep;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(keep) : "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
-}
-__device__ __forceinline__ void dma16_nt(const i32x4& r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  uint32_t keep;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen nt lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(keep) : "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
 template <int YDT>
@@ -187,15 +152,16 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
 
   // A copy j (0..31) fills LDS bytes [1024 j, 1024 j + 1024) = rows 8 j .. 8 j + 7;
   // wave w issues j = 4 w + u.  Lane i: row r = 8 j + i / 8 at LDS chunk i % 8,
-  // which holds global chunk (i % 8) ^ (r % 8).
+  // which holds global chunk (i % 8) ^ ((r / 2) % 8).
   uint32_t aoff[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 8 * (4 * wv + u) + (lane >> 3);
-    aoff[u] = (uint32_t)(r * K * 2 + (((lane & 7) ^ (r & 7)) * 16));
+    aoff[u] = (uint32_t)(r * K * 2 + (((lane & 7) ^ ((r >> 1) & 7)) * 16));
   }
-  // B: wave w copies columns 32 w .. 32 w + 31 (two lanes per column)
-  const uint32_t boff = (uint32_t)((32 * wv + (lane >> 1)) * (K >> 1) + (lane & 1) * 16);
+  // B: wave w copies columns 32 w .. 32 w + 31; lane i takes half i / 32 of
+  // column 32 w + i % 32
+  const uint32_t boff = (uint32_t)((32 * wv + (lane & 31)) * (K >> 1) + (lane >> 5) * 16);
   // C: waves 0 and 1 copy 128 columns each (two columns per lane)
   const uint32_t coff = (uint32_t)((wv * 128 + lane * 2) * 8);
 
@@ -226,9 +192,10 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
       c24[nb] = as_f16x2((c.x & 0xFFFFu) | (c.x << 16));
       c20[nb] = as_f16x2((c.x >> 16) | (c.x & 0xFFFF0000u));
       nzd[nb] = as_f16x2(c.y);
-      // words [col][8]: this lane half takes words (lane / 32) + 2 ks, ks = 0..3
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(base + kAStage + col * 32);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(base + kAStage + col * 32 + 16);
+      // words 0..7 of the column; this lane half takes words (lane / 32) + 2 ks, ks = 0..3
+      const uint8_t* bp = base + kAStage + (col >> 5) * 1024 + (col & 31) * 16;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(bp);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(bp + 512);
       bw[nb] = (lane >> 5) ? u32x4{lo[1], lo[3], hi[1], hi[3]} : u32x4{lo[0], lo[2], hi[0], hi[2]};
     }
 #pragma unroll
@@ -237,7 +204,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const int r = wm * 128 + mb * 32 + (lane & 31);
-        a[mb] = *reinterpret_cast<const u32x4*>(base + r * 128 + (((2 * ks + (lane >> 5)) ^ (r & 7)) * 16));
+        a[mb] = *reinterpret_cast<const u32x4*>(base + r * 128 + (((2 * ks + (lane >> 5)) ^ ((r >> 1) & 7)) * 16));
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) b[nb] = dequant_word_f16(bw[nb][ks], c24[nb], c20[nb], nzd[nb]);
@@ -253,13 +220,12 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
   issue(1, lds1);
   const bool six = wv < 2;
   auto step = [&](int64_t s, const uint8_t* cur, const uint8_t* nxt2) {
-    // stage s landed: all copies but stage s + 1's (s_waitcnt encoding on this
-    // target: vmcnt[3:0] | expcnt 7 << 4 | lgkmcnt 15 << 8)
+    // stage s landed: all copies but stage s + 1's
     if (s + 1 < S) {
-      if (six) __builtin_amdgcn_s_waitcnt(0x0F76);
-      else __builtin_amdgcn_s_waitcnt(0x0F75);
+      if (six) __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
     } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
     __builtin_amdgcn_s_barrier();
     if (s + 2 < S) issue(s + 2, nxt2);
