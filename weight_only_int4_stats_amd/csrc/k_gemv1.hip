@@ -243,8 +243,9 @@ __global__ __launch_bounds__(1024) void k_gemv1_rows(
 // registers for all of its rows.  Row group rg walks the block's rows
 // rg, rg + nrg, ...; D rows of packed words, steps and zero points are kept in
 // flight ahead of the row being reduced.  Each group of D row dot products is
-// reduce-scattered across the wave, the per-slice partial sums go to LDS, and
-// the slices are added in a fixed order at the end.
+// reduce-scattered across the wave; with one K slice the row sums are stored
+// at once, otherwise the per-slice partial sums go to LDS and the slices are
+// added in a fixed order at the end.
 // ---------------------------------------------------------------------------
 template <int DT, int YDT, bool HAS_R, int NS, int D, int C>
 __global__ __launch_bounds__(1024) void k_gemv1_cu(
@@ -361,13 +362,17 @@ __global__ __launch_bounds__(1024) void k_gemv1_cu(
       v = row16_sum(v);
       constexpr int LB = D >= 3 ? 2 : D == 2 ? 1 : 0;
       const int jd = j0 + (lane >> (6 - LB));
-      if ((lane & ((64 >> LB) - 1)) == 0 && jd < nj && jd < j0 + D) part[ks * rows_max + rg + nrg * jd] = v;
+      if ((lane & ((64 >> LB) - 1)) == 0 && jd < nj && jd < j0 + D) {
+        if (nks == 1) store_y1<YDT>(y, r0 + rg + nrg * jd, v);   // one K slice: the row is complete
+        else part[ks * rows_max + rg + nrg * jd] = v;
+      }
       j0 += D;
       if (j0 >= nj) break;                           // wave-uniform
 #pragma unroll
       for (int d = 0; d < D; ++d) load_row(d, j0 + d);
     }
   }
+  if (nks == 1) return;                             // block-uniform
   __syncthreads();
   for (int t = threadIdx.x; t < nrows; t += blockDim.x) {
     float tot = 0.0f;
