@@ -267,10 +267,14 @@ def test_search_single_linear_512():
 
 @pytest.mark.parametrize("N,K,T,dtype,ld_pad", [(300, 1024, 200, F16, 0), (130, 768, 77, BF16, 0),
                                                   (64, 4096, 64, F16, 0), (2500, 256, 520, F16, 24),
-                                                  (1100, 128, 300, BF16, 8)])
+                                                  (1100, 128, 300, BF16, 8),
+                                                  (300, 256, 4096, F16, 0), (200, 384, 3000, BF16, 8),
+                                                  (256, 1024, 8192, F16, 0)])
 def test_search_ragged(N, K, T, dtype, ld_pad):
     """Ragged token and row tiles; 2500 rows = 10 tiles of 256, two tile bands
-    of the contraction's order, the second narrower; padded token rows."""
+    of the contraction's order, the second narrower; padded token rows.  The
+    last three shapes (T well above K) take the Gram form of the loss: ragged
+    token chunks, a ragged tile of G (384 = 256 + 128) and bf16 tokens."""
     W = WL.random_matrix((N, K), torch.float32, seed=N, scale=0.02).to(dtype)
     X = gpu(_act(T, K + ld_pad, dtype, seed=T))[:, :K]     # strided view on the device
     _check_search(W, X, dtype)

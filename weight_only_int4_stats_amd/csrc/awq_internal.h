@@ -25,6 +25,15 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
                          float* s_out, float* inv_s_out, double* loss_out, int32_t* best_out,
                          void* ws, hipStream_t st);
 
+// Gram form of the search loss (k_gram.hip): Xt [K][Tp] 16-bit, G [K][K] fp64,
+// P [K][2K] fp16 (high and low parts of each row of G scaled by 2^-sk[k]).
+int64_t gram_tokens_padded(int64_t T);
+int64_t gram_loss_tiles(int64_t N, int64_t K);
+hipError_t launch_gram_prepare(const void* x, int dt, int64_t T, int64_t K, int64_t ldx,
+                               uint16_t* Xt, double* G, uint16_t* P, int* sk, hipStream_t st);
+hipError_t launch_gram_loss(const uint16_t* E, int64_t N, int64_t K, const int* pexp,
+                            const uint16_t* P, const int* sk, double* partial, hipStream_t st);
+
 // ---- W4A16 product ----------------------------------------------------------
 bool gemv1_supported(int64_t K, int64_t N);   // batch-1 GEMV kernels cover this shape
 hipError_t launch_gemv1(const void* x, int xdt, int64_t K, const uint32_t* qw,

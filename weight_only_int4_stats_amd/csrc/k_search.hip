@@ -24,6 +24,7 @@
 // the result is bit-reproducible.
 #include "awq_device.h"
 #include "awq_internal.h"
+#include "k_contract.h"
 #include "k_rows_f16.h"
 
 namespace awqk {
@@ -132,25 +133,12 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
 // ---------------------------------------------------------------------------
 // contraction C = X E'^T, sum of squares per tile
 // ---------------------------------------------------------------------------
-// 256 tokens x 256 error rows per block of 4 waves, one per SIMD (2 along
-// tokens x 2 along rows; each wave 128 x 128 = 4 x 4 blocks of 32 x 32, whose
-// 256 accumulators per lane sit in the accumulation registers).  32 k per
-// stage; four LDS stages, filled by LDS DMA (buffer_load ... lds) three stages
-// ahead of the matrix-core work.  A stage holds both operands, 256 rows x 32 k
-// of fp16 each (64 bytes a row, a quarter of the 64 banks); row r's 16-byte
-// chunk c sits at chunk c ^ ((r / 4) mod 4), so the 16 rows that one 16-lane
-// pass of a 128-bit read touches land on 16 different bank slots.
-// Inside a wave the operand fragments of the next 16 k are read from LDS
-// while the 16 products of the current 16 k run (two register sets).
+// C = X E'^T on 256 x 256 tiles (tokens x error rows; the shared contraction
+// core), the squares of each tile summed in the epilogue.
 // Tile order: block i runs on L2 slice i mod 8 and slice x takes the x-th
 // eighth of the tiles in band order (bands of 8 error-row tiles; inside a band
 // token tiles, then the band's row tiles), so the 32 blocks a slice runs at
 // once share 4 token tiles and 8 error-row tiles through its L2.
-constexpr int kCT = 256;                 // tile edge (tokens and rows)
-constexpr int kCBK = 32;                 // k per stage
-constexpr int kCOp = kCT * kCBK * 2;     // bytes per operand and stage (16 KB)
-constexpr int kCWaves = 4;
-constexpr int kCCopies = 2 * (kCOp / 1024) / kCWaves;   // 1 KB copies per wave and stage (8)
 constexpr int kCBand = 8;                // error-row tiles per band
 constexpr int kCXcds = 8;                // L2 slices (block i -> slice i mod 8)
 
@@ -158,10 +146,6 @@ inline int64_t contract_blocks(int64_t T, int64_t N) {
   const int64_t tiles = ((T + kCT - 1) / kCT) * ((N + kCT - 1) / kCT);
   return kCXcds * ((tiles + kCXcds - 1) / kCXcds);
 }
-
-struct Frags {
-  u32x4 a[4], b[4];
-};
 
 // px: per-token power of two of the fp16 tokens (NULL: tokens unscaled).
 // partial[ty * gx + tx] = sum of squares of tile (token tile ty, row tile tx).
@@ -171,10 +155,10 @@ __global__ __launch_bounds__(256) void k_err_contract(const uint16_t* __restrict
                                                       int64_t K, const int* __restrict__ pexp,
                                                       double* __restrict__ partial) {
   // four LDS arrays, the loop unrolled by four: each stage is a known array
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[2 * kCOp];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[2 * kCOp];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[2 * kCOp];
-  __shared__ __attribute__((aligned(16))) uint8_t lds3[2 * kCOp];
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kCStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kCStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[kCStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds3[kCStage];
   __shared__ double wsum[kCWaves];
 
   // ---- tile of this block
@@ -195,35 +179,18 @@ __global__ __launch_bounds__(256) void k_err_contract(const uint16_t* __restrict
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 1, wn = wv & 1;
-  const int64_t S = K / kCBK;
   const int64_t rows = T - t0 < kCT ? T - t0 : kCT;
   const int64_t cols = N - n0 < kCT ? N - n0 : kCT;
   // rows past T / N fall outside the descriptors and arrive as zeros
-  const i32x4 ars = rsrc4(X + t0 * ldx, (uint32_t)((rows - 1) * ldx * 2 + K * 2));
-  const i32x4 brs = rsrc4(E + n0 * K, (uint32_t)(cols * K * 2));
+  ContractSrc cs;
+  cs.ars = rsrc4(X + t0 * ldx, (uint32_t)((rows - 1) * ldx * 2 + K * 2));
+  cs.a_ld = (uint32_t)(ldx * 2);
+  cs.brs = rsrc4(E + n0 * K, (uint32_t)(cols * K * 2));
+  cs.b_ld = (uint32_t)(K * 2);
+  cs.k0 = 0;
+  cs.a_wrap = 0;
+  cs.S = K / kCBK;
 
-  // Copy j (0..15) of an operand fills its bytes [1024 j, 1024 j + 1024) =
-  // rows 16 j .. 16 j + 15; wave w issues j = 4 w + u.  Lane i: row
-  // r = 16 j + i / 4 at chunk i % 4, which holds global chunk (i % 4) ^ ((r / 4) % 4).
-  uint32_t aoff[4], boff[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 16 * (4 * wv + u) + (lane >> 2);
-    const uint32_t ch = (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
-    aoff[u] = (uint32_t)(r * ldx * 2) + ch;
-    boff[u] = (uint32_t)(r * K * 2) + ch;
-  }
-  // copy u (0..7) of stage s into the stage array at base: A copies 0..3, B 4..7
-  auto copy = [&](int64_t s, const uint8_t* base, int u) {
-    const uint32_t kb = (uint32_t)(s * kCBK * 2);
-    const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(base));
-    if (u < 4) dma16(ars, lb + (4 * wv + u) * 1024, aoff[u], kb);
-    else dma16(brs, lb + kCOp + (4 * wv + u - 4) * 1024, boff[u - 4], kb);
-  };
-  auto issue = [&](int64_t s, const uint8_t* base) {
-#pragma unroll
-    for (int u = 0; u < kCCopies; ++u) copy(s, base, u);
-  };
   f32x16 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -231,88 +198,7 @@ __global__ __launch_bounds__(256) void k_err_contract(const uint16_t* __restrict
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-
-  // fragment i (0..7) of 16 k (half ks of a stage), in the order the products
-  // use them: a0 b0 b1 b2 b3 a1 a2 a3 (A lane = token row, B lane = E row,
-  // both 8 k of chunk 2 ks + lane / 32)
-  auto read1 = [&](const uint8_t* base, int ks, Frags& f, int i) {
-    const int c = 2 * ks + (lane >> 5);
-    if (i >= 1 && i <= 4) {
-      const int r = wn * 128 + (i - 1) * 32 + (lane & 31);
-      f.b[i - 1] = *reinterpret_cast<const u32x4*>(base + kCOp + r * 64 + ((c ^ ((r >> 2) & 3)) * 16));
-    } else {
-      const int mb = i == 0 ? 0 : i - 4;
-      const int r = wm * 128 + mb * 32 + (lane & 31);
-      f.a[mb] = *reinterpret_cast<const u32x4*>(base + r * 64 + ((c ^ ((r >> 2) & 3)) * 16));
-    }
-  };
-  // products 2 i and 2 i + 1 of the 16 (token block i / 2, row blocks 2 (i % 2) + 0, 1)
-  auto mma2 = [&](const Frags& f, int i) {
-    const int mb = i >> 1, nb = (i & 1) * 2;
-    acc[mb][nb] = mfma32h(f.a[mb], f.b[nb], acc[mb][nb]);
-    acc[mb][nb + 1] = mfma32h(f.a[mb], f.b[nb + 1], acc[mb][nb + 1]);
-  };
-
-  // K is a multiple of 128, so S is a multiple of 4 (and at least 4): the
-  // loop below runs whole groups of four stages and the last group is peeled,
-  // which keeps every wait count a constant.
-  Frags f0, f1;
-  // prologue: stages 0..2 in flight, stage 0 published, stage 3 issued
-  issue(0, lds0);
-  issue(1, lds1);
-  issue(2, lds2);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCCopies));
-  lds_barrier();
-  issue(3, lds3);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) read1(lds0, 0, f0, i);
-
-  // Stage s in two halves of 16 products.  First half: the products of f0
-  // (first 16 k), with the second 16 k read into f1 one fragment per two
-  // products.  Then stage s + 1 is published, once all but the `ahead` stages
-  // copied after it have landed and every LDS read of the wave has returned
-  // (so all of stage s has been read); second half: the products of f1, with
-  // one copy of stage s + 4 into stage s's array and one fragment of stage
-  // s + 1's first 16 k per two products.  Issuing copies and reads between
-  // products keeps the matrix pipe fed while they queue; scheduling barriers
-  // hold that order.
-  auto stage = [&](int64_t s, const uint8_t* cur, const uint8_t* nxt, int ahead, bool refill) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      mma2(f0, i);
-      read1(cur, 1, f1, i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kCCopies));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kCCopies));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      mma2(f1, i);
-      if (refill) copy(s + 4, cur, i);
-      read1(nxt, 0, f0, i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  int64_t s = 0;
-  for (; s < S - 4; s += 4) {
-    stage(s, lds0, lds1, 2, true);
-    stage(s + 1, lds1, lds2, 2, true);
-    stage(s + 2, lds2, lds3, 2, true);
-    stage(s + 3, lds3, lds0, 2, true);
-  }
-  stage(s, lds0, lds1, 2, false);
-  stage(s + 1, lds1, lds2, 1, false);
-  stage(s + 2, lds2, lds3, 0, false);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    mma2(f0, i);
-    read1(lds3, 1, f1, i);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) mma2(f1, i);
+  contract_tile<false>(cs, lds0, lds1, lds2, lds3, acc);
 
   // epilogue.  Lane value v of block (mb, nb) belongs to E row
   // n = n0 + wn 128 + nb 32 + lane % 32 and token
@@ -421,14 +307,31 @@ __global__ void k_select(const double* __restrict__ L, int n_alpha, const float*
 namespace awq {
 
 namespace {
+
+// The Gram form (G = X^T X once, then a 2K-long contraction per candidate, with
+// G carried as two fp16 parts) replaces the T-long contraction when it costs
+// well under half as many matrix-core operations and G (K^2 doubles) is small.
+bool search_uses_gram(int64_t N, int64_t K, int64_t T, int n_alpha) {
+  if (K > 16384) return false;
+  const double Tp = (double)gram_tokens_padded(T);
+  const double direct = (double)n_alpha * 2.0 * (double)T * (double)N * (double)K;
+  const double gram = 2.0 * Tp * (double)K * (double)K + (double)n_alpha * 4.0 * (double)N * (double)K * (double)K;
+  return gram < 0.5 * direct;
+}
+
 struct SearchWs {
   float* S;
   int* pexp;
   uint16_t* E;
   double* partial;
   double* losses;
-  uint16_t* Xh;     // bf16 tokens rounded to fp16 (bf16 input only)
+  uint16_t* Xh;     // bf16 tokens rounded to fp16 (direct form, bf16 input only)
   int* px;
+  uint16_t* Xt;     // Gram form: tokens transposed
+  double* G;
+  uint16_t* P;
+  int* sk;
+  bool gram;
   size_t bytes;
 };
 
@@ -441,16 +344,26 @@ SearchWs carve(void* ws, int dt, int64_t N, int64_t K, int64_t T, int n_alpha) {
     off += align_up(b, 256);
     return p;
   };
-  const int64_t gx = (N + awqk::kCT - 1) / awqk::kCT;
-  const int64_t gy = (T + awqk::kCT - 1) / awqk::kCT;
+  w.gram = search_uses_gram(N, K, T, n_alpha);
   w.S = (float*)take((size_t)n_alpha * K * 4);
   w.pexp = (int*)take((size_t)N * 4);
   w.E = (uint16_t*)take((size_t)N * K * 2);
-  w.partial = (double*)take((size_t)gx * gy * 8);
   w.losses = (double*)take((size_t)n_alpha * 8);
-  if (dt == awqk::DT_BF16) {
-    w.Xh = (uint16_t*)take((size_t)T * K * 2);
-    w.px = (int*)take((size_t)T * 4);
+  if (w.gram) {
+    const int64_t Tp = gram_tokens_padded(T);
+    w.partial = (double*)take((size_t)gram_loss_tiles(N, K) * 8);
+    w.Xt = (uint16_t*)take((size_t)K * Tp * 2);
+    w.G = (double*)take((size_t)K * K * 8);
+    w.P = (uint16_t*)take((size_t)K * K * 4);
+    w.sk = (int*)take((size_t)K * 4);
+  } else {
+    const int64_t gx = (N + awqk::kCT - 1) / awqk::kCT;
+    const int64_t gy = (T + awqk::kCT - 1) / awqk::kCT;
+    w.partial = (double*)take((size_t)gx * gy * 8);
+    if (dt == awqk::DT_BF16) {
+      w.Xh = (uint16_t*)take((size_t)T * K * 2);
+      w.px = (int*)take((size_t)T * 4);
+    }
   }
   w.bytes = off;
   return w;
@@ -470,31 +383,45 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
   const int64_t nS = (int64_t)n_alpha * K;
   hipLaunchKernelGGL(k_cand_scales, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, mean_abs,
                      alphas, n_alpha, K, sw.S);
-  const uint16_t* Xop = (const uint16_t*)x;
-  int64_t ldop = ldx;
-  const int* px = nullptr;
-  if (dt == DT_BF16) {
-    hipLaunchKernelGGL((k_rows_f16<DT_BF16, false, false>), dim3((unsigned)T), dim3(256), 0, st,
-                       (const uint16_t*)x, K, ldx, (const float*)nullptr, sw.Xh, sw.px);
-    Xop = sw.Xh;
-    ldop = K;
-    px = sw.px;
-  }
-  const int64_t gx = (N + kCT - 1) / kCT;
-  const int64_t gy = (T + kCT - 1) / kCT;
   const double tn = (double)T * (double)N;
-  for (int i = 0; i < n_alpha; ++i) {
-    const float* s_i = sw.S + (int64_t)i * K;
+  auto err_gen = [&](const float* s_i) {
     if (dt == DT_F16)
       hipLaunchKernelGGL(k_err_gen<DT_F16>, dim3((unsigned)N), dim3(256), 0, st,
                          (const uint16_t*)w, N, K, s_i, sw.E, sw.pexp);
     else
       hipLaunchKernelGGL(k_err_gen<DT_BF16>, dim3((unsigned)N), dim3(256), 0, st,
                          (const uint16_t*)w, N, K, s_i, sw.E, sw.pexp);
-    hipLaunchKernelGGL(k_err_contract, dim3((unsigned)contract_blocks(T, N)), dim3(256), 0, st, Xop, T,
-                       ldop, px, sw.E, N, K, sw.pexp, sw.partial);
-    hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial, gx * gy, tn,
-                       sw.losses + i);
+  };
+  if (sw.gram) {
+    const hipError_t e = launch_gram_prepare(x, dt, T, K, ldx, sw.Xt, sw.G, sw.P, sw.sk, st);
+    if (e != hipSuccess) return e;
+    const int64_t nt = gram_loss_tiles(N, K);
+    for (int i = 0; i < n_alpha; ++i) {
+      err_gen(sw.S + (int64_t)i * K);
+      const hipError_t el = launch_gram_loss(sw.E, N, K, sw.pexp, sw.P, sw.sk, sw.partial, st);
+      if (el != hipSuccess) return el;
+      hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial, nt, tn, sw.losses + i);
+    }
+  } else {
+    const uint16_t* Xop = (const uint16_t*)x;
+    int64_t ldop = ldx;
+    const int* px = nullptr;
+    if (dt == DT_BF16) {
+      hipLaunchKernelGGL((k_rows_f16<DT_BF16, false, false>), dim3((unsigned)T), dim3(256), 0, st,
+                         (const uint16_t*)x, K, ldx, (const float*)nullptr, sw.Xh, sw.px);
+      Xop = sw.Xh;
+      ldop = K;
+      px = sw.px;
+    }
+    const int64_t gx = (N + kCT - 1) / kCT;
+    const int64_t gy = (T + kCT - 1) / kCT;
+    for (int i = 0; i < n_alpha; ++i) {
+      err_gen(sw.S + (int64_t)i * K);
+      hipLaunchKernelGGL(k_err_contract, dim3((unsigned)contract_blocks(T, N)), dim3(256), 0, st, Xop, T,
+                         ldop, px, sw.E, N, K, sw.pexp, sw.partial);
+      hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial, gx * gy, tn,
+                         sw.losses + i);
+    }
   }
   hipLaunchKernelGGL(k_select, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, sw.losses,
                      n_alpha, sw.S, K, s_out, inv_s_out, loss_out, best_out);

@@ -165,13 +165,21 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
   // C: waves 0 and 1 copy 128 columns each (two columns per lane)
   const uint32_t coff = (uint32_t)((wv * 128 + lane * 2) * 8);
 
-  auto issue = [&](int64_t s, const uint8_t* base) {
+  // copy u of stage s into the stage array at base: u 0..3 the wave's A rows,
+  // 4 its B columns and (waves 0, 1) its constants
+  auto copy = [&](int64_t s, const uint8_t* base, int u) {
     const uint32_t k0 = (uint32_t)(s * kBK);
     const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(base));
+    if (u < 4) {
+      dma16(ars, lb + (4 * wv + u) * 1024, aoff[u], k0 * 2);
+    } else {
+      dma16_nt(brs, lb + kAStage + wv * 1024, boff, k0 >> 1);
+      if (wv < 2) dma16(crs, lb + kAStage + kBStage + wv * 1024, coff, (uint32_t)((k0 / kGroup) * N * 8));
+    }
+  };
+  auto issue = [&](int64_t s, const uint8_t* base) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dma16(ars, lb + (4 * wv + u) * 1024, aoff[u], k0 * 2);
-    dma16_nt(brs, lb + kAStage + wv * 1024, boff, k0 >> 1);
-    if (wv < 2) dma16(crs, lb + kAStage + kBStage + wv * 1024, coff, (uint32_t)((k0 / kGroup) * N * 8));
+    for (int u = 0; u < 5; ++u) copy(s, base, u);
   };
 
   f32x16 acc[4][2];
@@ -182,7 +190,9 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  auto compute = [&](const uint8_t* base) {
+  // products of the stage at base; the copies of stage s2 (if s2 >= 0) go out
+  // one per 16 k between them, so the matrix pipe stays fed while they queue
+  auto compute = [&](const uint8_t* base, int64_t s2, const uint8_t* nxt2) {
     f16x2 c24[2], c20[2], nzd[2];
     u32x4 bw[2];
 #pragma unroll
@@ -200,6 +210,10 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
     }
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
+      if (s2 >= 0) {
+        copy(s2, nxt2, ks);
+        if (ks == 3) copy(s2, nxt2, 4);
+      }
       u32x4 a[4], b[2];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
@@ -212,6 +226,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32h(a[mb], b[nb], acc[mb][nb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -227,9 +242,8 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
     } else {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    __builtin_amdgcn_s_barrier();
-    if (s + 2 < S) issue(s + 2, nxt2);
-    compute(cur);
+    lds_barrier();
+    compute(cur, s + 2 < S ? s + 2 : -1, nxt2);
   };
   for (int64_t s = 0; s < S; s += 3) {
     step(s, lds0, lds2);
