@@ -140,8 +140,15 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
  *   best_idx_out  int32; may be NULL; -1 if every loss is NaN
  * The error products run on fp16/bf16 matrix cores with fp32 accumulation;
  * the per-row error is scaled by an exact power of two before rounding to
- * fp16 so that it stays in the normal range.  Linears that read the same input
- * may be searched together by passing their row-concatenated W.
+ * fp16 so that it stays in the normal range.  Two equivalent forms of the
+ * loss: the direct one contracts E_i with the tokens (2 T N K operations per
+ * candidate); the Gram one uses sum_t ||E_i x_t||^2 = sum_n e_n^T (X^T X) e_n,
+ * forms G = X^T X once (2 Tp K^2, Tp = T rounded up to 256; fp32 per chunk of
+ * 8192 tokens, fp64 across chunks) and carries each row of G as two fp16
+ * parts (22 significant bits), so a candidate costs 4 N K^2.  The Gram form
+ * is taken when K <= 16384 and its total is under half of the direct one's.
+ * Linears that read the same input may be searched together by passing their
+ * row-concatenated W.
  */
 awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
                              const void* x_calib, int64_t T, int64_t ldx,
