@@ -203,11 +203,6 @@ __device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, uint32_t vof
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
                : "=&s"(keep) : "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
 }
-__device__ __forceinline__ void dma16_nt(const i32x4& r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  uint32_t keep;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen nt lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(keep) : "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
-}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }

@@ -13,6 +13,8 @@ __device__ __forceinline__ int pow2_exp_for(float amax) {
   return 14 - e;
 }
 
+constexpr int kRowsKeep = 8;   // 8-element chunks per thread kept in registers (K <= 16384)
+
 // Activation rows -> fp16: y_row = fp16(x_row * r * 2^p_row), p_row from the
 // row's max so the row sits in fp16's normal range.  One block per row.  With
 // PERMUTE each 8-element chunk is stored as (k0,k4,k2,k6,k1,k5,k3,k7), the
@@ -42,24 +44,8 @@ __global__ __launch_bounds__(256) void k_rows_f16(const uint16_t* __restrict__ s
       }
     }
   };
-  float amax = 0.0f;
-  for (int64_t c = threadIdx.x; c < nch; c += 256) {
-    float v[8];
-    load8(c, v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  __shared__ float wmax[4];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  const int p = pow2_exp_for(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
-  if (threadIdx.x == 0) pexp[row] = p;
   uint16_t* d = dst + row * K;
-  for (int64_t c = threadIdx.x; c < nch; c += 256) {
-    float v[8];
-    load8(c, v);
+  auto store8 = [&](int64_t c, const float v[8], int p) {
     uint32_t h[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) h[j] = f32_to_f16_bits(ldexpf(v[j], p));
@@ -74,7 +60,49 @@ __global__ __launch_bounds__(256) void k_rows_f16(const uint16_t* __restrict__ s
       for (int j = 0; j < 4; ++j) o[j] = h[2 * j] | (h[2 * j + 1] << 16);
     }
     *reinterpret_cast<u32x4*>(d + c * 8) = o;
+  };
+  __shared__ float wmax[4];
+  auto row_exp = [&](float amax) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    const int p = pow2_exp_for(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+    if (threadIdx.x == 0) pexp[row] = p;
+    return p;
+  };
+  float amax = 0.0f;
+  if (nch <= 256 * kRowsKeep) {
+    // the row stays in registers between the max and the conversion
+    float v[kRowsKeep][8];
+#pragma unroll
+    for (int i = 0; i < kRowsKeep; ++i) {
+      const int64_t c = threadIdx.x + 256 * i;
+      if (c < nch) {
+        load8(c, v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+      }
+    }
+    const int p = row_exp(amax);
+#pragma unroll
+    for (int i = 0; i < kRowsKeep; ++i) {
+      const int64_t c = threadIdx.x + 256 * i;
+      if (c < nch) store8(c, v[i], p);
+    }
+    return;
+  }
+  for (int64_t c = threadIdx.x; c < nch; c += 256) {
+    float v[8];
+    load8(c, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  }
+  const int p = row_exp(amax);
+  for (int64_t c = threadIdx.x; c < nch; c += 256) {
+    float v[8];
+    load8(c, v);
+    store8(c, v, p);
   }
 }
-
 }  // namespace awqk

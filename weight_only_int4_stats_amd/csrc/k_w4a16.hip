@@ -35,7 +35,7 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
 // matrix-core GEMM
 // ===========================================================================
 
-// Per weight row n (one wave): e_n with max_g step[n][g] 2^e_n in [2^-10, 2^-9),
+// Per weight row n: e_n with max_g step[n][g] 2^e_n in [2^-10, 2^-9),
 // so that D' = step 2^e_n times 2^24 is a finite fp16 and D' (q - z) a normal
 // fp16; then, for every group g, the fp16 constants of the packed-fma
 // dequantization, group-major so a block's columns are contiguous:
@@ -44,27 +44,62 @@ __global__ __launch_bounds__(256) void k_gemm_consts(const uint16_t* __restrict_
                                                      const uint8_t* __restrict__ zeros, int64_t N,
                                                      int64_t G, int* __restrict__ en,
                                                      uint32_t* __restrict__ ctab) {
-  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (n >= N) return;
-  float mx = 0.0f;
-  for (int64_t g = lane; g < G; g += 64) mx = fmaxf(mx, f16_to_f32(scales[n * G + g]));
+  // A block takes 64 rows; 64 groups at a time are staged in LDS (reads along
+  // the groups, all issued together).  Thread r < 64 takes row r's maximum
+  // from LDS; the constants are written with the rows fastest, so that every
+  // group's 64 entries form one 512-byte run.  With G <= 64 the one staged
+  // chunk serves both passes.
+  __shared__ float step_s[64][65];
+  __shared__ uint8_t zero_s[64][65];
+  __shared__ int e_s[64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  const int rows = (int)(N - n0 < 64 ? N - n0 : 64);
+  auto stage = [&](int64_t g0, int gc) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  int e = 0;
-  if (mx > 0.0f) {
-    int ex;
-    frexpf(mx, &ex);        // mx < 2^ex
-    e = -9 - ex;            // mx 2^e in [2^-10, 2^-9)
+    for (int u = 0; u < 16; ++u) {
+      const int i = wv + 4 * u;
+      if (i < rows && lane < gc) {
+        step_s[i][lane] = f16_to_f32(scales[(n0 + i) * G + g0 + lane]);
+        zero_s[i][lane] = zeros[(n0 + i) * G + g0 + lane];
+      }
+    }
+  };
+  float mx = 0.0f;
+  for (int64_t g0 = 0; g0 < G; g0 += 64) {
+    const int gc = (int)(G - g0 < 64 ? G - g0 : 64);
+    __syncthreads();
+    stage(g0, gc);
+    __syncthreads();
+    if (tid < rows)
+      for (int gl = 0; gl < gc; ++gl) mx = fmaxf(mx, step_s[tid][gl]);
   }
-  if (lane == 0) en[n] = e;
-  for (int64_t g = lane; g < G; g += 64) {
-    const float D = ldexpf(f16_to_f32(scales[n * G + g]), e);   // exact: power-of-two scaling
-    const uint32_t h24 = f32_to_f16_bits(D * 16777216.0f);
-    const uint32_t h20 = f32_to_f16_bits(D * 1048576.0f);
-    const uint32_t hz = f32_to_f16_bits(-(D * (float)zeros[n * G + g]));
-    ctab[(g * N + n) * 2] = h24 | (h20 << 16);
-    ctab[(g * N + n) * 2 + 1] = hz | (hz << 16);
+  if (tid < rows) {
+    int e = 0;
+    if (mx > 0.0f) {
+      int ex;
+      frexpf(mx, &ex);        // mx < 2^ex
+      e = -9 - ex;            // mx 2^e in [2^-10, 2^-9)
+    }
+    en[n0 + tid] = e;
+    e_s[tid] = e;
+  }
+  for (int64_t g0 = 0; g0 < G; g0 += 64) {
+    const int gc = (int)(G - g0 < 64 ? G - g0 : 64);
+    if (G > 64) {
+      __syncthreads();
+      stage(g0, gc);
+    }
+    __syncthreads();
+    if (lane < rows)
+      for (int gl = wv; gl < gc; gl += 4) {
+        const float D = ldexpf(step_s[lane][gl], e_s[lane]);   // exact: power-of-two scaling
+        const uint32_t h24 = f32_to_f16_bits(D * 16777216.0f);
+        const uint32_t h20 = f32_to_f16_bits(D * 1048576.0f);
+        const uint32_t hz = f32_to_f16_bits(-(D * (float)zero_s[lane][gl]));
+        *reinterpret_cast<uint2*>(ctab + ((g0 + gl) * N + n0 + lane) * 2) =
+            make_uint2(h24 | (h20 << 16), hz | (hz << 16));
+      }
   }
 }
 
@@ -99,9 +134,15 @@ __device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 c24, f16x2 c
 //   B  256 columns x 8 packed words; per 32 columns the first 16 bytes of
 //      each column, then the last 16 (again 16 lanes -> 16 bank slots)
 //   C  256 columns of dequantization constants (8 bytes each)
-// Tiles are ordered for the chip's eight L2 slices: block i runs on slice
-// i mod 8, so slice x takes the x-th eighth of the tiles in m-major order and
-// its concurrent blocks share activation stages in its L2.
+// Operand k order: in k16 step ks, lane half h (lanes 32 h .. 32 h + 31) holds
+// packed word 4 h + ks of its column (8 k), so that its four words are one
+// 16-byte LDS read per stage, and reads A chunk 4 h + ks to match.
+// All three are plain (temporal) copies: a packed column's 128-byte line
+// serves four consecutive stages, and the activation and weight stages are
+// shared by the blocks that run on one L2 slice at the same time.  Tiles are
+// ordered for the chip's eight L2 slices: block i runs on slice i mod 8, and
+// slice x takes the x-th eighth of the tiles in a grouped order (4 m-tiles,
+// m fastest, then n), so its ~32 concurrent blocks cover about 4 x 8 tiles.
 constexpr int kMT = 256;                // tile rows (m)
 constexpr int kNT = 256;                // tile columns (n)
 constexpr int kBK = 64;                 // k per stage
@@ -118,11 +159,11 @@ inline int64_t gemm_blocks(int64_t M, int64_t N) {
 
 template <int YDT>
 __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, int64_t M, int64_t K,
-                                              const int* __restrict__ pm,
-                                              const uint32_t* __restrict__ qw,
-                                              const uint32_t* __restrict__ ctab,
-                                              const int* __restrict__ en, int64_t N,
-                                              void* __restrict__ y, int64_t ldy) {
+                                             const int* __restrict__ pm,
+                                             const uint32_t* __restrict__ qw,
+                                             const uint32_t* __restrict__ ctab,
+                                             const int* __restrict__ en, int64_t N,
+                                             void* __restrict__ y, int64_t ldy) {
   // three LDS arrays, the loop unrolled by three: each stage is a known array
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kStage];
@@ -134,9 +175,15 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
   const int64_t slot = blockIdx.x / kXcds;
   const int64_t t = (int64_t)(blockIdx.x % kXcds) * per + slot;
   if (slot >= per || t >= T) return;
-  const int64_t mt = t / ntile;
+  // tile t in grouped order: 4 m-tiles at a time, m fastest, so the ~32
+  // blocks a slice runs at once cover about 4 x 8 tiles and share both
+  // operands in its L2
+  const int64_t g = t / (4 * ntile);
+  const int64_t rr = t - g * 4 * ntile;
+  const int64_t gm = mtile - g * 4 < 4 ? mtile - g * 4 : 4;
+  const int64_t mt = g * 4 + rr % gm;
   const int64_t m0 = mt * kMT;
-  const int64_t n0 = (t - mt * ntile) * kNT;
+  const int64_t n0 = (rr / gm) * kNT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,7 +220,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
     if (u < 4) {
       dma16(ars, lb + (4 * wv + u) * 1024, aoff[u], k0 * 2);
     } else {
-      dma16_nt(brs, lb + kAStage + wv * 1024, boff, k0 >> 1);
+      dma16(brs, lb + kAStage + wv * 1024, boff, k0 >> 1);
       if (wv < 2) dma16(crs, lb + kAStage + kBStage + wv * 1024, coff, (uint32_t)((k0 / kGroup) * N * 8));
     }
   };
@@ -190,38 +237,86 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  // products of the stage at base; the copies of stage s2 (if s2 >= 0) go out
-  // one per 16 k between them, so the matrix pipe stays fed while they queue
-  auto compute = [&](const uint8_t* base, int64_t s2, const uint8_t* nxt2) {
-    f16x2 c24[2], c20[2], nzd[2];
-    u32x4 bw[2];
+  // Per wave and stage: the dequantization constants and packed words of its
+  // two column blocks, then per k16 step the four A fragments.  The A
+  // fragments of step ks + 1 are read while the products of step ks run; the
+  // wait for the next stage and the block barrier sit in step 3, before its
+  // products, so the next stage's first reads overlap them too.  The
+  // constants are unpacked at the next stage's step 0, away from that wait.
+  struct Frag { f16x2 c24[2], c20[2], nzd[2]; u32x4 bw[2]; };
+  struct Raw { uint2 c[2]; u32x4 lo[2]; };
+  auto load_raw = [&](const uint8_t* base, Raw& w) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int col = wn * 64 + nb * 32 + (lane & 31);
-      const uint2 c = *reinterpret_cast<const uint2*>(base + kAStage + kBStage + col * 8);
-      c24[nb] = as_f16x2((c.x & 0xFFFFu) | (c.x << 16));
-      c20[nb] = as_f16x2((c.x >> 16) | (c.x & 0xFFFF0000u));
-      nzd[nb] = as_f16x2(c.y);
-      // words 0..7 of the column; this lane half takes words (lane / 32) + 2 ks, ks = 0..3
+      w.c[nb] = *reinterpret_cast<const uint2*>(base + kAStage + kBStage + col * 8);
       const uint8_t* bp = base + kAStage + (col >> 5) * 1024 + (col & 31) * 16;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(bp);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(bp + 512);
-      bw[nb] = (lane >> 5) ? u32x4{lo[1], lo[3], hi[1], hi[3]} : u32x4{lo[0], lo[2], hi[0], hi[2]};
+      w.lo[nb] = *reinterpret_cast<const u32x4*>(bp + (lane >> 5) * 512);
     }
+  };
+  auto decode = [&](const Raw& w, Frag& f) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const f16x2 cx = as_f16x2(w.c[nb].x);
+      f.c24[nb] = __builtin_shufflevector(cx, cx, 0, 0);
+      f.c20[nb] = __builtin_shufflevector(cx, cx, 1, 1);
+      f.nzd[nb] = as_f16x2(w.c[nb].y);
+      f.bw[nb] = w.lo[nb];
+    }
+  };
+  auto load_a = [&](const uint8_t* base, int ks, u32x4 (&a)[4]) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int r = wm * 128 + mb * 32 + (lane & 31);
+      a[mb] = *reinterpret_cast<const u32x4*>(base + r * 128 + (((4 * (lane >> 5) + ks) ^ ((r >> 1) & 7)) * 16));
+    }
+  };
+  const bool six = wv < 2;
+
+  Frag F;
+  Raw R;
+  u32x4 aE[4], aO[4];   // fragments of even and odd k16 steps
+  issue(0, lds0);
+  issue(1, lds1);
+  if (six) __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
+  lds_barrier();
+  load_a(lds0, 0, aE);
+  load_raw(lds0, R);
+
+  auto stage = [&](int64_t s, const uint8_t* cur, const uint8_t* nxt, const uint8_t* nxt2) {
+    const bool cp = s + 2 < S;
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      if (s2 >= 0) {
-        copy(s2, nxt2, ks);
-        if (ks == 3) copy(s2, nxt2, 4);
+      if (cp) {
+        copy(s + 2, nxt2, ks);
+        if (ks == 3) copy(s + 2, nxt2, 4);
       }
-      u32x4 a[4], b[2];
+      if (ks == 0) decode(R, F);
+      u32x4 b[2];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int r = wm * 128 + mb * 32 + (lane & 31);
-        a[mb] = *reinterpret_cast<const u32x4*>(base + r * 128 + (((2 * ks + (lane >> 5)) ^ ((r >> 1) & 7)) * 16));
+      for (int nb = 0; nb < 2; ++nb) b[nb] = dequant_word_f16(F.bw[nb][ks], F.c24[nb], F.c20[nb], F.nzd[nb]);
+      if (ks < 3) {
+        load_a(cur, ks + 1, (ks & 1) ? aE : aO);
+      } else {
+        // stage s + 1 landed (all copies but stage s + 2's) and every wave
+        // done reading the buffer the next copies overwrite; the last stage
+        // waits too, so that both paths reach the products with no read
+        // outstanding but the next stage's
+        if (cp) {
+          if (six) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(6));
+          else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(5));
+        } else {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        }
+        // unconditional: after the last stage these reads are of a stale
+        // buffer and unused, and every path reaches the products alike
+        lds_barrier();
+        load_a(nxt, 0, aE);
+        load_raw(nxt, R);
       }
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) b[nb] = dequant_word_f16(bw[nb][ks], c24[nb], c20[nb], nzd[nb]);
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4 (&a)[4] = (ks & 1) ? aO : aE;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -229,26 +324,10 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-
-  // stages 0 and 1 in flight; copies per wave and stage: 5 (6 for waves 0, 1)
-  issue(0, lds0);
-  issue(1, lds1);
-  const bool six = wv < 2;
-  auto step = [&](int64_t s, const uint8_t* cur, const uint8_t* nxt2) {
-    // stage s landed: all copies but stage s + 1's
-    if (s + 1 < S) {
-      if (six) __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    lds_barrier();
-    compute(cur, s + 2 < S ? s + 2 : -1, nxt2);
-  };
   for (int64_t s = 0; s < S; s += 3) {
-    step(s, lds0, lds2);
-    if (s + 1 < S) step(s + 1, lds1, lds0);
-    if (s + 2 < S) step(s + 2, lds2, lds1);
+    stage(s, lds0, lds1, lds2);
+    if (s + 1 < S) stage(s + 1, lds1, lds2, lds0);
+    if (s + 2 < S) stage(s + 2, lds2, lds0, lds1);
   }
 
   // 32x32 accumulator layout: column = lane % 32, row = 8 (v / 4) + 4 (lane / 32) + v % 4
@@ -433,7 +512,7 @@ hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
   const GemmWs w = gemm_ws(ws, M, N, K);
   hipLaunchKernelGGL((k_rows_f16<DT, HAS_R, true>), dim3((unsigned)M), dim3(256), 0, st, x, K, ldx,
                      r, w.xq, w.pm);
-  hipLaunchKernelGGL(k_gemm_consts, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, scales, zeros, N,
+  hipLaunchKernelGGL(k_gemm_consts, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st, scales, zeros, N,
                      K / kGroup, w.en, w.ctab);
   hipLaunchKernelGGL((k_gemm<YDT>), dim3((unsigned)gemm_blocks(M, N)), dim3(512), 0, st, w.xq, M, K, w.pm,
                      qw, w.ctab, w.en, N, y, ldy);
