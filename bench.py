@@ -226,10 +226,12 @@ def main() -> int:
     # matrix-core operations the search executes: the direct form contracts
     # over the tokens per candidate; the Gram form (taken by the library when
     # it needs under half of those, see awq_search_scales in include/awq.h)
-    # forms X^T X once and contracts over 2K per candidate
+    # forms X^T X once and per candidate contracts with the 256 x 256 blocks
+    # of it on and below the diagonal, each as two fp16 parts
     Tp = (wa.T + 255) // 256 * 256
+    gblk = (KA + 255) // 256
     direct_flop = 2.0 * wa.T * NA * KA * 20
-    gram_flop = 2.0 * Tp * KA * KA + 20 * 4.0 * NA * KA * KA
+    gram_flop = 2.0 * Tp * KA * KA + 20 * 2.0 * NA * 256 * 256 * gblk * (gblk + 1)
     search_gram = KA <= 16384 and gram_flop < 0.5 * direct_flop
     search_flop = gram_flop if search_gram else direct_flop
     stats_bytes = wa.T * KA * 2

@@ -143,10 +143,14 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
  * fp16 so that it stays in the normal range.  Two equivalent forms of the
  * loss: the direct one contracts E_i with the tokens (2 T N K operations per
  * candidate); the Gram one uses sum_t ||E_i x_t||^2 = sum_n e_n^T (X^T X) e_n,
- * forms G = X^T X once (2 Tp K^2, Tp = T rounded up to 256; fp32 per chunk of
- * 8192 tokens, fp64 across chunks) and carries each row of G as two fp16
- * parts (22 significant bits), so a candidate costs 4 N K^2.  The Gram form
- * is taken when K <= 16384 and its total is under half of the direct one's.
+ * forms G = X^T X once (its tiles on and above the diagonal; Tp = T rounded
+ * up to 256; fp32 per chunk of at most 8192 tokens, fp64 across chunks in
+ * chunk order) and carries each row of G as two fp16
+ * parts (22 significant bits); with G symmetric, a candidate contracts only
+ * over the 256 x 256 blocks of G on and below the diagonal (off-diagonal
+ * blocks counted twice), 2 N 256^2 g (g + 1) operations for g = ceil(K / 256),
+ * about 2 N K^2.  The Gram form is taken when K <= 16384 and its total is
+ * under half of the direct one's.
  * Linears that read the same input may be searched together by passing their
  * row-concatenated W.
  */

@@ -25,12 +25,16 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
                          float* s_out, float* inv_s_out, double* loss_out, int32_t* best_out,
                          void* ws, hipStream_t st);
 
-// Gram form of the search loss (k_gram.hip): Xt [K][Tp] 16-bit, G [K][K] fp64,
-// P [K][2K] fp16 (high and low parts of each row of G scaled by 2^-sk[k]).
+// Gram form of the search loss (k_gram.hip): Xt [K][Tp] 16-bit, fp32 partial
+// tiles of G (gram_partial_floats), G [K][K] fp64, P [K][2 Kp] fp16 (Kp = K
+// rounded up to 256; per 256-wide block the high then the low parts of each
+// row of G scaled by 2^-sk[k]).
 int64_t gram_tokens_padded(int64_t T);
 int64_t gram_loss_tiles(int64_t N, int64_t K);
+int64_t gram_partial_floats(int64_t T, int64_t K);
 hipError_t launch_gram_prepare(const void* x, int dt, int64_t T, int64_t K, int64_t ldx,
-                               uint16_t* Xt, double* G, uint16_t* P, int* sk, hipStream_t st);
+                               uint16_t* Xt, float* Gp, double* G, uint16_t* P, int* sk,
+                               hipStream_t st);
 hipError_t launch_gram_loss(const uint16_t* E, int64_t N, int64_t K, const int* pexp,
                             const uint16_t* P, const int* sk, double* partial, hipStream_t st);
 

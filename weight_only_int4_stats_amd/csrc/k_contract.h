@@ -38,7 +38,8 @@ struct ContractSrc {
   i32x4 brs;          // B rows
   uint32_t b_ld;      // B row stride in bytes
   uint32_t k0;        // first k, in bytes from each row's start
-  uint32_t a_wrap;    // A's k offset is taken modulo a_wrap bytes (0: no wrap)
+  uint32_t a_dup_sh;  // > 0: every 2^a_dup_sh-byte block of A's k range serves two
+                      // consecutive such blocks of k (B's range is twice A's)
   int64_t S;          // stages of 32 k; a multiple of 4, at least 4
 };
 
@@ -72,7 +73,8 @@ __device__ __forceinline__ void contract_tile(const ContractSrc& cs, uint8_t* ld
   // copy u (0..7) of stage s into the stage array at base: A copies 0..3, B 4..7
   auto copy = [&](int64_t s, const uint8_t* base, int u) {
     const uint32_t kb = cs.k0 + (uint32_t)(s * kCBK * 2);
-    const uint32_t ka = cs.a_wrap ? kb % cs.a_wrap : kb;
+    const uint32_t ka =
+        cs.a_dup_sh ? ((kb >> (cs.a_dup_sh + 1)) << cs.a_dup_sh) | (kb & ((1u << cs.a_dup_sh) - 1u)) : kb;
     const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(base));
     if (u < 4) dma16(cs.ars, lb + (4 * wv + u) * 1024, aoff[u], ka);
     else dma16(cs.brs, lb + kCOp + (4 * wv + u - 4) * 1024, boff[u - 4], kb);

@@ -7,26 +7,56 @@
 // uses this form when the calibration set is much longer than a row.
 //   1. k_transpose16  X [T][ldx] -> Xt [K][Tp] (tokens along rows, zero padded
 //                     to Tp, a multiple of 256; the 16-bit values are copied)
-//   2. k_gram         G (fp64) += Xt[:, chunk] Xt[:, chunk]^T on the matrix
-//                     cores (shared contraction core): fp32 within a chunk of
-//                     kGramChunk tokens, fp64 across chunks in a fixed order
-//                     (one launch per chunk)
+//   2. k_gram         one item per (tile of G on or above the diagonal, chunk
+//                     of at most kGramChunk tokens): Xt[:, chunk] Xt[:, chunk]^T
+//                     on the matrix cores (shared contraction core) in fp32,
+//                     written as an fp32 partial tile; the chunk length is
+//                     chosen so that the items fill kGramCUs compute units
+//                     evenly.  k_gram_reduce adds a tile's chunks in fp64 in
+//                     chunk order and writes it and its mirror image into G
+//                     (chunks are taken in groups whose partials fit
+//                     kGramPartialMax; later groups add to G in the same order).
 //   3. k_gram_split   per row k of G a power of two 2^s_k with
-//                     max_j |G_kj| 2^-s_k in [2^14, 2^15), and
-//                     P[k][j] = fp16(G_kj 2^-s_k), P[k][K + j] = fp16(G_kj 2^-s_k - P[k][j])
-//                     (22 significant bits of each row relative to its largest entry)
-//   4. k_gram_loss    per candidate: C = [E' E'] P^T (contraction over 2K, so
-//                     C_nk = sum_j E'_nj G_kj 2^-s_k to 22 bits), E' = E 2^p_n as
-//                     stored by the error generator; the epilogue adds
-//                     E'_nk C_nk 2^(s_k - 2 p_n) over the tile in fp64 -> one
-//                     partial per tile (summed in a fixed order afterwards).
+//                     max_j |G_kj| 2^-s_k in [2^14, 2^15), and the fp16 pair
+//                     hi = fp16(g), lo = fp16(g - hi) of g = G_kj 2^-s_k (22
+//                     significant bits of each row relative to its largest
+//                     entry), halved when j and k fall in the same 256-wide
+//                     block.  Row k of P holds, per 256-wide block b of j,
+//                     the 256 hi values then the 256 lo values (zeros past K).
+//   4. k_gram_loss    per candidate, with the symmetry of G:
+//                        e^T G e = sum_J sum_{I <= J} w_IJ e_I^T G_IJ e_J,
+//                     w = 1 off the diagonal blocks counted once each way
+//                     (doubling the sum, halving the diagonal blocks).  Output
+//                     tile (row tile of E', channel block J) contracts over
+//                     the blocks I <= J only: C_nk = sum_{j in blocks <= J}
+//                     E'_nj P'_kj (hi and lo, A's block read twice), about half
+//                     the work of the full product.  E' = E 2^p_n as stored by
+//                     the error generator; the epilogue adds
+//                     E'_nk C_nk 2^(s_k + 1 - 2 p_n) over the tile in fp64 ->
+//                     one partial per tile (summed in a fixed order afterwards).
 #include "awq_device.h"
 #include "awq_internal.h"
 #include "k_contract.h"
 
 namespace awqk {
 
-constexpr int64_t kGramChunk = 8192;     // tokens per fp32 accumulation chunk
+constexpr int64_t kGramChunk = 8192;     // most tokens per fp32 accumulation chunk
+constexpr int64_t kGramCUs = 256;        // compute units the chunking is planned for
+constexpr int64_t kGramPartialMax = int64_t(1) << 30;   // bytes of fp32 partial tiles per launch
+constexpr int64_t kGramTile = (int64_t)kCT * kCT;   // floats per partial tile
+
+// Tile u (0 .. g (g + 1) / 2 - 1) of G on or above the diagonal, row-major
+// over the upper triangle: (tj, tk) with tj <= tk.
+__device__ __forceinline__ void gram_upper_tile(int64_t u, int64_t g, int64_t& tj, int64_t& tk) {
+  int64_t r = 0, len = g;
+  while (u >= len) {
+    u -= len;
+    ++r;
+    --len;
+  }
+  tj = r;
+  tk = r + u;
+}
 
 // 64 tokens x 64 channels per block of 256 threads; tokens past T are zeros.
 __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ X, int64_t T,
@@ -66,29 +96,33 @@ __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict_
   }
 }
 
-// One 256 x 256 tile of G per block (row tile gy = blockIdx / gx, column tile
-// blockIdx % gx), tokens [c0, c0 + len) of Xt; G tile = (first ? 0 : G) + chunk.
+// Item b: chunk cfirst + c of len tokens (c = b / nup; the last chunk may be
+// shorter), upper tile u = b mod nup.  The fp32 tile goes to Gp[(c nup + u)] in the
+// register order of the contraction core (value i of thread t at i 256 + t),
+// which k_gram_reduce reads back with the same order.
 template <int DT>
 __global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ Xt, int64_t K, int64_t Tp,
-                                              int64_t c0, int64_t len, int first,
-                                              double* __restrict__ G) {
+                                              int64_t len, int64_t cfirst, float* __restrict__ Gp) {
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kCStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kCStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds2[kCStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds3[kCStage];
-  const int64_t gx = (K + kCT - 1) / kCT;
-  const int64_t tj = blockIdx.x / gx, tk = blockIdx.x - tj * gx;
+  const int64_t g = (K + kCT - 1) / kCT, nup = g * (g + 1) / 2;
+  const int64_t c = blockIdx.x / nup, u = blockIdx.x - c * nup;
+  int64_t tj, tk;
+  gram_upper_tile(u, g, tj, tk);
   const int64_t j0 = tj * kCT, k0 = tk * kCT;
   const int64_t rj = K - j0 < kCT ? K - j0 : kCT;
   const int64_t rk = K - k0 < kCT ? K - k0 : kCT;
+  const int64_t t0 = (cfirst + c) * len;
   ContractSrc cs;
   cs.ars = rsrc4(Xt + j0 * Tp, (uint32_t)(rj * Tp * 2));
   cs.a_ld = (uint32_t)(Tp * 2);
   cs.brs = rsrc4(Xt + k0 * Tp, (uint32_t)(rk * Tp * 2));
   cs.b_ld = (uint32_t)(Tp * 2);
-  cs.k0 = (uint32_t)(c0 * 2);
-  cs.a_wrap = 0;
-  cs.S = len / kCBK;
+  cs.k0 = (uint32_t)(t0 * 2);
+  cs.a_dup_sh = 0;
+  cs.S = (Tp - t0 < len ? Tp - t0 : len) / kCBK;
   f32x16 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -97,30 +131,58 @@ __global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ Xt, i
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
   contract_tile<DT == DT_BF16>(cs, lds0, lds1, lds2, lds3, acc);
+  float* out = Gp + (c * nup + u) * kGramTile + threadIdx.x;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) out[((mb * 4 + nb) * 16 + v) * 256] = acc[mb][nb][v];
+}
 
+// Block (u, q): upper tile u, 32 x 32 sub-block q = 4 mb + nb of every
+// wave's quarter.  G_jk = (first ? 0 : G_jk) + the fp32 partials of the
+// group's nch chunks, added in fp64 in chunk order; an off-diagonal tile also
+// fills its mirror G_kj.
+__global__ __launch_bounds__(256) void k_gram_reduce(const float* __restrict__ Gp, int64_t K,
+                                                     int64_t nch, int first, double* __restrict__ G) {
+  const int64_t g = (K + kCT - 1) / kCT, nup = g * (g + 1) / 2;
+  const int64_t u = blockIdx.x >> 4;
+  const int q = blockIdx.x & 15, mb = q >> 2, nb = q & 3;
+  int64_t tj, tk;
+  gram_upper_tile(u, g, tj, tk);
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int wm = wv >> 1, wn = wv & 1;
+  const int64_t k = tk * kCT + wn * 128 + nb * 32 + (lane & 31);
+  const int64_t jb = tj * kCT + wm * 128 + mb * 32 + 4 * (lane >> 5);
+  const float* in = Gp + u * kGramTile + q * 16 * 256 + threadIdx.x;
+  double sum[16];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int64_t k = k0 + wn * 128 + nb * 32 + (lane & 31);
-    if (k >= K) continue;
+  for (int v = 0; v < 16; ++v) {
+    const int64_t j = jb + 8 * (v >> 2) + (v & 3);
+    sum[v] = first || j >= K || k >= K ? 0.0 : G[j * K + k];
+  }
+  for (int64_t c = 0; c < nch; ++c) {
+    const float* pc = in + c * nup * kGramTile;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int v = 0; v < 16; ++v) sum[v] += (double)pc[v * 256];
+  }
+  if (k >= K) return;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t j = j0 + wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (j < K) {
-          double* g = G + j * K + k;
-          *g = (first ? 0.0 : *g) + (double)acc[mb][nb][v];
-        }
-      }
+  for (int v = 0; v < 16; ++v) {
+    const int64_t j = jb + 8 * (v >> 2) + (v & 3);
+    if (j < K) {
+      G[j * K + k] = sum[v];
+      if (tj != tk) G[k * K + j] = sum[v];
+    }
   }
 }
 
-// One block per row k of G.
+// One block per row k of G; Kp = K rounded up to a multiple of 256.
 __global__ __launch_bounds__(256) void k_gram_split(const double* __restrict__ G, int64_t K,
-                                                    uint16_t* __restrict__ P, int* __restrict__ sk) {
+                                                    int64_t Kp, uint16_t* __restrict__ P,
+                                                    int* __restrict__ sk) {
   const int64_t k = blockIdx.x;
   const double* row = G + k * K;
   double mx = 0.0;
@@ -144,24 +206,23 @@ __global__ __launch_bounds__(256) void k_gram_split(const double* __restrict__ G
   }
   __syncthreads();
   const int s = s_sh;
-  uint16_t* prow = P + k * 2 * K;
-  for (int64_t j = threadIdx.x; j < K; j += 256) {
-    const double g = ldexp(row[j], -s);
+  const int64_t kb = k / kCT;
+  uint16_t* prow = P + k * 2 * Kp;
+  for (int64_t j = threadIdx.x; j < Kp; j += 256) {
+    const int64_t b = j / kCT, c = j - b * kCT;
+    // exact: a power-of-two scaling (halving for the diagonal block)
+    const double g = j < K ? ldexp(row[j], -s - (b == kb ? 1 : 0)) : 0.0;
     const uint32_t hi = f32_to_f16_bits((float)g);
     const double rest = g - (double)f16_to_f32(hi);
-    prow[j] = (uint16_t)hi;
-    prow[K + j] = (uint16_t)f32_to_f16_bits((float)rest);
+    prow[b * 2 * kCT + c] = (uint16_t)hi;
+    prow[b * 2 * kCT + kCT + c] = (uint16_t)f32_to_f16_bits((float)rest);
   }
 }
 
-// Tile order as the direct contraction: L2 slice i mod 8 takes the x-th eighth
-// of the tiles in band order (bands of 8 column tiles of k).
-constexpr int kGBand = 8;
-constexpr int kGXcds = 8;
-
+// Tiles longest first: block o takes channel block J = gx - 1 - o / gy and
+// row tile o mod gy (consecutive blocks share J's rows of P).
 inline int64_t gram_loss_blocks(int64_t N, int64_t K) {
-  const int64_t tiles = ((N + kCT - 1) / kCT) * ((K + kCT - 1) / kCT);
-  return kGXcds * ((tiles + kGXcds - 1) / kGXcds);
+  return ((N + kCT - 1) / kCT) * ((K + kCT - 1) / kCT);
 }
 
 // partial[ty * gx + tx] for tile (row tile ty of E, column tile tx of k).
@@ -176,16 +237,11 @@ __global__ __launch_bounds__(256) void k_gram_loss(const uint16_t* __restrict__ 
   __shared__ __attribute__((aligned(16))) uint8_t lds3[kCStage];
   __shared__ double wsum[kCWaves];
 
-  const int64_t gx = (K + kCT - 1) / kCT, gy = (N + kCT - 1) / kCT, tiles = gx * gy;
-  const int64_t per = (tiles + kGXcds - 1) / kGXcds;
-  const int64_t slot = blockIdx.x / kGXcds;
-  const int64_t o = (int64_t)(blockIdx.x % kGXcds) * per + slot;
-  if (slot >= per || o >= tiles) return;
-  const int64_t band = o / (gy * kGBand);
-  const int64_t rb = o - band * gy * kGBand;
-  const int64_t bw = gx - band * kGBand < kGBand ? gx - band * kGBand : kGBand;
-  const int64_t ty = rb / bw;
-  const int64_t tx = band * kGBand + (rb - ty * bw);
+  const int64_t gx = (K + kCT - 1) / kCT, gy = (N + kCT - 1) / kCT;
+  const int64_t o = blockIdx.x;
+  const int64_t tx = gx - 1 - o / gy;
+  const int64_t ty = o - (gx - 1 - tx) * gy;
+  const int64_t Kp = gx * kCT;
   const int64_t n0 = ty * kCT;   // rows of E (MFMA A rows)
   const int64_t k0 = tx * kCT;   // rows of P (MFMA B rows) = output channels
 
@@ -194,11 +250,11 @@ __global__ __launch_bounds__(256) void k_gram_loss(const uint16_t* __restrict__ 
   ContractSrc cs;
   cs.ars = rsrc4(E + n0 * K, (uint32_t)(rn * K * 2));
   cs.a_ld = (uint32_t)(K * 2);
-  cs.brs = rsrc4(P + k0 * 2 * K, (uint32_t)(rk * K * 4));
-  cs.b_ld = (uint32_t)(K * 4);
+  cs.brs = rsrc4(P + k0 * 2 * Kp, (uint32_t)(rk * Kp * 4));
+  cs.b_ld = (uint32_t)(Kp * 4);
   cs.k0 = 0;
-  cs.a_wrap = (uint32_t)(K * 2);
-  cs.S = 2 * K / kCBK;
+  cs.a_dup_sh = 9;                       // 256 fp16 of E serve a hi and a lo block
+  cs.S = (tx + 1) * 2 * kCT / kCBK;      // blocks 0..J, hi and lo
   f32x16 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -237,7 +293,7 @@ __global__ __launch_bounds__(256) void k_gram_loss(const uint16_t* __restrict__ 
           part += ldexp(e * (double)acc[mb][nb][v], -2 * pn[v]);
         }
       }
-      tot += ldexp(part, s);
+      tot += ldexp(part, s + 1);   // the diagonal blocks were halved
     }
   }
 #pragma unroll
@@ -261,23 +317,66 @@ int64_t gram_loss_tiles(int64_t N, int64_t K) {
   return ((N + awqk::kCT - 1) / awqk::kCT) * ((K + awqk::kCT - 1) / awqk::kCT);
 }
 
+// Chunk plan of the Gram build: the chunk length (a multiple of 128 tokens, at
+// most kGramChunk) whose items, upper tiles x chunks, take the fewest
+// rounds x length on kGramCUs compute units; chunks go in groups of cg per
+// launch so that a group's partial tiles fit kGramPartialMax.
+struct GramPlan {
+  int64_t len, nch, cg, nup;
+};
+
+GramPlan gram_plan(int64_t T, int64_t K) {
+  using namespace awqk;
+  const int64_t Tp = gram_tokens_padded(T);
+  const int64_t g = (K + kCT - 1) / kCT, nup = g * (g + 1) / 2;
+  const int64_t tile_bytes = kGramTile * 4;
+  int64_t cg_max = kGramPartialMax / (nup * tile_bytes);
+  if (cg_max < 1) cg_max = 1;
+  const int64_t n0 = (Tp + kGramChunk - 1) / kGramChunk;
+  GramPlan best{0, 0, 0, nup};
+  int64_t best_cost = 0;
+  for (int64_t n = n0; n <= 2 * n0; ++n) {
+    const int64_t len = ((Tp + n - 1) / n + 127) / 128 * 128;
+    const int64_t nch = (Tp + len - 1) / len;
+    const int64_t cg = nch < cg_max ? nch : cg_max;
+    int64_t rounds = 0;
+    for (int64_t c = 0; c < nch; c += cg) {
+      const int64_t m = nch - c < cg ? nch - c : cg;
+      rounds += (nup * m + kGramCUs - 1) / kGramCUs;
+    }
+    const int64_t cost = rounds * (len + 128);     // + per-item fill and store
+    if (best.nch == 0 || cost < best_cost) {
+      best = GramPlan{len, nch, cg, nup};
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+int64_t gram_partial_floats(int64_t T, int64_t K) {
+  const GramPlan pl = gram_plan(T, K);
+  return pl.nup * pl.cg * awqk::kGramTile;
+}
+
 hipError_t launch_gram_prepare(const void* x, int dt, int64_t T, int64_t K, int64_t ldx,
-                               uint16_t* Xt, double* G, uint16_t* P, int* sk, hipStream_t st) {
+                               uint16_t* Xt, float* Gp, double* G, uint16_t* P, int* sk,
+                               hipStream_t st) {
   using namespace awqk;
   const int64_t Tp = gram_tokens_padded(T);
   hipLaunchKernelGGL(k_transpose16, dim3((unsigned)(Tp / 64), (unsigned)(K / 64)), dim3(256), 0, st,
                      (const uint16_t*)x, T, K, ldx, Xt, Tp);
   const int64_t g = (K + kCT - 1) / kCT;
-  for (int64_t c0 = 0; c0 < Tp; c0 += kGramChunk) {
-    const int64_t len = Tp - c0 < kGramChunk ? Tp - c0 : kGramChunk;
+  const GramPlan pl = gram_plan(T, K);
+  for (int64_t c = 0; c < pl.nch; c += pl.cg) {
+    const int64_t m = pl.nch - c < pl.cg ? pl.nch - c : pl.cg;
+    const dim3 grid((unsigned)(pl.nup * m));
     if (dt == DT_BF16)
-      hipLaunchKernelGGL(k_gram<DT_BF16>, dim3((unsigned)(g * g)), dim3(256), 0, st, Xt, K, Tp, c0, len,
-                         (int)(c0 == 0), G);
+      hipLaunchKernelGGL(k_gram<DT_BF16>, grid, dim3(256), 0, st, Xt, K, Tp, pl.len, c, Gp);
     else
-      hipLaunchKernelGGL(k_gram<DT_F16>, dim3((unsigned)(g * g)), dim3(256), 0, st, Xt, K, Tp, c0, len,
-                         (int)(c0 == 0), G);
+      hipLaunchKernelGGL(k_gram<DT_F16>, grid, dim3(256), 0, st, Xt, K, Tp, pl.len, c, Gp);
+    hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)(pl.nup * 16)), dim3(256), 0, st, Gp, K, m, (int)(c == 0), G);
   }
-  hipLaunchKernelGGL(k_gram_split, dim3((unsigned)K), dim3(256), 0, st, G, K, P, sk);
+  hipLaunchKernelGGL(k_gram_split, dim3((unsigned)K), dim3(256), 0, st, G, K, g * kCT, P, sk);
   return hipGetLastError();
 }
 

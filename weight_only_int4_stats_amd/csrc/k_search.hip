@@ -9,9 +9,10 @@
 // the matrix cores.  Three steps per candidate:
 //   1. k_err_gen    one block per row: the row's groups are quantized exactly
 //                   as awq_quantize_pack does, E = W - D (q - z) / s in float;
-//                   a first pass finds max|E| of the row, a second writes
-//                   E * 2^p (p chosen so the row fits fp16's normal range) as
-//                   fp16 into the workspace, with p per row.
+//                   the row's max|E| fixes p (so the row fits fp16's normal
+//                   range), then E * 2^p is written as fp16 into the
+//                   workspace, with p per row (the errors stay in registers
+//                   in between for K <= 8192, else they are computed twice).
 //   2. k_err_contract  256x256 tiles of C = X E'^T with fp16 MFMA (fp32
 //                   accumulation); the epilogue squares and sums the tile,
 //                   undoes the powers of two in double, and writes one double
@@ -77,6 +78,8 @@ __device__ __forceinline__ void err_word(const uint16_t* __restrict__ wrow,
   }
 }
 
+constexpr int kErrKeep = 4;   // packed words per thread kept in registers (K <= 8192)
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W, int64_t N,
                                                  int64_t K, const float* __restrict__ s,
@@ -84,7 +87,57 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
   const int64_t n = blockIdx.x;
   const uint16_t* wrow = W + n * K;
   const int64_t wpr = K >> 3;
+  uint16_t* erow = E + n * K;
+  __shared__ float wmax[4];
+  __shared__ int sp;
+  auto row_exp = [&](float emax) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) emax = fmaxf(emax, __shfl_xor(emax, off));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = emax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+      int p = 0;
+      if (m > 0.0f) {
+        int ex;
+        frexpf(m, &ex);          // m < 2^ex
+        p = 14 - ex;             // m * 2^p < 2^14, well inside fp16's finite range
+      }
+      sp = p;
+      pexp[n] = p;
+    }
+    __syncthreads();
+    return sp;
+  };
+  auto store = [&](int64_t c, const float e[8], int p) {
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      out[j] = f32_to_f16_bits(ldexpf(e[2 * j], p)) | (f32_to_f16_bits(ldexpf(e[2 * j + 1], p)) << 16);
+    *reinterpret_cast<u32x4*>(erow + c * 8) = out;
+  };
   float emax = 0.0f;
+  if (wpr <= 256 * kErrKeep) {
+    // the row's errors stay in registers between the maximum and the store
+    // (whole 16-lane segments are in or out: wpr is a multiple of 16)
+    float e[kErrKeep][8];
+#pragma unroll
+    for (int i = 0; i < kErrKeep; ++i) {
+      const int64_t c = threadIdx.x + 256 * i;
+      if (c < wpr) {
+        err_word<DT>(wrow, s, c * 8, e[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) emax = fmaxf(emax, fabsf(e[i][j]));
+      }
+    }
+    const int p = row_exp(emax);
+#pragma unroll
+    for (int i = 0; i < kErrKeep; ++i) {
+      const int64_t c = threadIdx.x + 256 * i;
+      if (c < wpr) store(c, e[i], p);
+    }
+    return;
+  }
   // pass 1: largest |E| of the row (whole 16-lane segments are in or out)
   for (int64_t c0 = 0; c0 < wpr; c0 += 256) {
     const int64_t c = c0 + threadIdx.x;
@@ -95,37 +148,14 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
       for (int j = 0; j < 8; ++j) emax = fmaxf(emax, fabsf(e[j]));
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) emax = fmaxf(emax, __shfl_xor(emax, off));
-  __shared__ float wmax[4];
-  __shared__ int sp;
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = emax;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    int p = 0;
-    if (m > 0.0f) {
-      int ex;
-      frexpf(m, &ex);          // m < 2^ex
-      p = 14 - ex;             // m * 2^p < 2^14, well inside fp16's finite range
-    }
-    sp = p;
-    pexp[n] = p;
-  }
-  __syncthreads();
-  const int p = sp;
-  // pass 2: the same arithmetic again, scaled by 2^p and rounded to DT
-  uint16_t* erow = E + n * K;
+  const int p = row_exp(emax);
+  // pass 2: the same arithmetic again, scaled by 2^p and rounded to fp16
   for (int64_t c0 = 0; c0 < wpr; c0 += 256) {
     const int64_t c = c0 + threadIdx.x;
     if (c < wpr) {
       float e[8];
       err_word<DT>(wrow, s, c * 8, e);
-      u32x4 out;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        out[j] = f32_to_f16_bits(ldexpf(e[2 * j], p)) | (f32_to_f16_bits(ldexpf(e[2 * j + 1], p)) << 16);
-      *reinterpret_cast<u32x4*>(erow + c * 8) = out;
+      store(c, e, p);
     }
   }
 }
@@ -188,7 +218,7 @@ __global__ __launch_bounds__(256) void k_err_contract(const uint16_t* __restrict
   cs.brs = rsrc4(E + n0 * K, (uint32_t)(cols * K * 2));
   cs.b_ld = (uint32_t)(K * 2);
   cs.k0 = 0;
-  cs.a_wrap = 0;
+  cs.a_dup_sh = 0;
   cs.S = K / kCBK;
 
   f32x16 acc[4][4];
@@ -308,14 +338,17 @@ namespace awq {
 
 namespace {
 
-// The Gram form (G = X^T X once, then a 2K-long contraction per candidate, with
-// G carried as two fp16 parts) replaces the T-long contraction when it costs
-// well under half as many matrix-core operations and G (K^2 doubles) is small.
+// The Gram form (G = X^T X once, then per candidate a contraction with G
+// carried as two fp16 parts, over the blocks on and below the diagonal only)
+// replaces the T-long contraction when it costs well under half as many
+// matrix-core operations and G (K^2 doubles) is small.
 bool search_uses_gram(int64_t N, int64_t K, int64_t T, int n_alpha) {
   if (K > 16384) return false;
   const double Tp = (double)gram_tokens_padded(T);
+  const double g = (double)((K + awqk::kCT - 1) / awqk::kCT);
   const double direct = (double)n_alpha * 2.0 * (double)T * (double)N * (double)K;
-  const double gram = 2.0 * Tp * (double)K * (double)K + (double)n_alpha * 4.0 * (double)N * (double)K * (double)K;
+  const double cand = 2.0 * (double)N * awqk::kCT * awqk::kCT * g * (g + 1.0);
+  const double gram = 2.0 * Tp * (double)K * (double)K + (double)n_alpha * cand;
   return gram < 0.5 * direct;
 }
 
@@ -328,6 +361,7 @@ struct SearchWs {
   uint16_t* Xh;     // bf16 tokens rounded to fp16 (direct form, bf16 input only)
   int* px;
   uint16_t* Xt;     // Gram form: tokens transposed
+  float* Gp;        // Gram form: fp32 partial tiles of G per token chunk
   double* G;
   uint16_t* P;
   int* sk;
@@ -353,8 +387,9 @@ SearchWs carve(void* ws, int dt, int64_t N, int64_t K, int64_t T, int n_alpha) {
     const int64_t Tp = gram_tokens_padded(T);
     w.partial = (double*)take((size_t)gram_loss_tiles(N, K) * 8);
     w.Xt = (uint16_t*)take((size_t)K * Tp * 2);
+    w.Gp = (float*)take((size_t)gram_partial_floats(T, K) * 4);
     w.G = (double*)take((size_t)K * K * 8);
-    w.P = (uint16_t*)take((size_t)K * K * 4);
+    w.P = (uint16_t*)take((size_t)K * ((K + awqk::kCT - 1) / awqk::kCT * awqk::kCT) * 4);
     w.sk = (int*)take((size_t)K * 4);
   } else {
     const int64_t gx = (N + awqk::kCT - 1) / awqk::kCT;
@@ -393,7 +428,7 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
                          (const uint16_t*)w, N, K, s_i, sw.E, sw.pexp);
   };
   if (sw.gram) {
-    const hipError_t e = launch_gram_prepare(x, dt, T, K, ldx, sw.Xt, sw.G, sw.P, sw.sk, st);
+    const hipError_t e = launch_gram_prepare(x, dt, T, K, ldx, sw.Xt, sw.Gp, sw.G, sw.P, sw.sk, st);
     if (e != hipSuccess) return e;
     const int64_t nt = gram_loss_tiles(N, K);
     for (int i = 0; i < n_alpha; ++i) {
