@@ -177,6 +177,10 @@ __device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const 
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma16h(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
 
 // Raw buffer descriptor: base address, stride 0, size in bytes, untyped dwords.
 // The arguments must be the same in every lane; the words are taken from the

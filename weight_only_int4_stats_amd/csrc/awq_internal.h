@@ -36,7 +36,8 @@ hipError_t launch_gram_prepare(const void* x, int dt, int64_t T, int64_t K, int6
                                uint16_t* Xt, float* Gp, double* G, uint16_t* P, int* sk,
                                hipStream_t st);
 hipError_t launch_gram_loss(const uint16_t* E, int64_t N, int64_t K, const int* pexp,
-                            const uint16_t* P, const int* sk, double* partial, hipStream_t st);
+                            const uint16_t* P, const int* sk, double* partial, int nc,
+                            hipStream_t st);
 
 // ---- W4A16 product ----------------------------------------------------------
 bool gemv1_supported(int64_t K, int64_t N);   // batch-1 GEMV kernels cover this shape

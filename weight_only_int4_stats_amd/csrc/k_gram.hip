@@ -219,18 +219,22 @@ __global__ __launch_bounds__(256) void k_gram_split(const double* __restrict__ G
   }
 }
 
-// Tiles longest first: block o takes channel block J = gx - 1 - o / gy and
-// row tile o mod gy (consecutive blocks share J's rows of P).
-inline int64_t gram_loss_blocks(int64_t N, int64_t K) {
-  return ((N + kCT - 1) / kCT) * ((K + kCT - 1) / kCT);
+// nc candidates per launch (error rows of candidate c at E + c N K, row
+// exponents at pexp + c N, tile partials at partial + c gx gy), so that the
+// uneven tiles of the triangle fill the compute units.  Tiles longest first:
+// block o takes channel block J = gx - 1 - o / (nc gy), then candidate and
+// row tile (consecutive blocks share J's rows of P).
+inline int64_t gram_loss_blocks(int64_t N, int64_t K, int nc) {
+  return ((N + kCT - 1) / kCT) * ((K + kCT - 1) / kCT) * nc;
 }
 
-// partial[ty * gx + tx] for tile (row tile ty of E, column tile tx of k).
+// partial[c gx gy + ty gx + tx] for tile (row tile ty of E, column tile tx of k)
+// of candidate c.
 __global__ __launch_bounds__(256) void k_gram_loss(const uint16_t* __restrict__ E, int64_t N, int64_t K,
                                                    const int* __restrict__ pexp,
                                                    const uint16_t* __restrict__ P,
                                                    const int* __restrict__ sk,
-                                                   double* __restrict__ partial) {
+                                                   double* __restrict__ partial, int nc) {
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kCStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kCStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds2[kCStage];
@@ -239,9 +243,14 @@ __global__ __launch_bounds__(256) void k_gram_loss(const uint16_t* __restrict__ 
 
   const int64_t gx = (K + kCT - 1) / kCT, gy = (N + kCT - 1) / kCT;
   const int64_t o = blockIdx.x;
-  const int64_t tx = gx - 1 - o / gy;
-  const int64_t ty = o - (gx - 1 - tx) * gy;
+  const int64_t tx = gx - 1 - o / (nc * gy);
+  const int64_t rest = o - (gx - 1 - tx) * nc * gy;
+  const int64_t cand = rest / gy;
+  const int64_t ty = rest - cand * gy;
   const int64_t Kp = gx * kCT;
+  E += cand * N * K;
+  pexp += cand * N;
+  partial += cand * gx * gy;
   const int64_t n0 = ty * kCT;   // rows of E (MFMA A rows)
   const int64_t k0 = tx * kCT;   // rows of P (MFMA B rows) = output channels
 
@@ -381,10 +390,11 @@ hipError_t launch_gram_prepare(const void* x, int dt, int64_t T, int64_t K, int6
 }
 
 hipError_t launch_gram_loss(const uint16_t* E, int64_t N, int64_t K, const int* pexp,
-                            const uint16_t* P, const int* sk, double* partial, hipStream_t st) {
+                            const uint16_t* P, const int* sk, double* partial, int nc,
+                            hipStream_t st) {
   using namespace awqk;
-  hipLaunchKernelGGL(k_gram_loss, dim3((unsigned)gram_loss_blocks(N, K)), dim3(256), 0, st, E, N, K,
-                     pexp, P, sk, partial);
+  hipLaunchKernelGGL(k_gram_loss, dim3((unsigned)gram_loss_blocks(N, K, nc)), dim3(256), 0, st, E, N, K,
+                     pexp, P, sk, partial, nc);
   return hipGetLastError();
 }
 

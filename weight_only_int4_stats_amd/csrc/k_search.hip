@@ -338,6 +338,11 @@ namespace awq {
 
 namespace {
 
+// Candidates whose Gram-form losses one launch computes (error rows of each
+// kept in the workspace): the uneven tiles of the triangle then fill the
+// compute units better.
+constexpr int kGramBatch = 4;
+
 // The Gram form (G = X^T X once, then per candidate a contraction with G
 // carried as two fp16 parts, over the blocks on and below the diagonal only)
 // replaces the T-long contraction when it costs well under half as many
@@ -366,6 +371,7 @@ struct SearchWs {
   uint16_t* P;
   int* sk;
   bool gram;
+  int nc;           // Gram form: candidates scored per loss launch
   size_t bytes;
 };
 
@@ -379,13 +385,14 @@ SearchWs carve(void* ws, int dt, int64_t N, int64_t K, int64_t T, int n_alpha) {
     return p;
   };
   w.gram = search_uses_gram(N, K, T, n_alpha);
+  w.nc = w.gram ? (n_alpha < kGramBatch ? n_alpha : kGramBatch) : 1;
   w.S = (float*)take((size_t)n_alpha * K * 4);
-  w.pexp = (int*)take((size_t)N * 4);
-  w.E = (uint16_t*)take((size_t)N * K * 2);
+  w.pexp = (int*)take((size_t)w.nc * N * 4);
+  w.E = (uint16_t*)take((size_t)w.nc * N * K * 2);
   w.losses = (double*)take((size_t)n_alpha * 8);
   if (w.gram) {
     const int64_t Tp = gram_tokens_padded(T);
-    w.partial = (double*)take((size_t)gram_loss_tiles(N, K) * 8);
+    w.partial = (double*)take((size_t)w.nc * gram_loss_tiles(N, K) * 8);
     w.Xt = (uint16_t*)take((size_t)K * Tp * 2);
     w.Gp = (float*)take((size_t)gram_partial_floats(T, K) * 4);
     w.G = (double*)take((size_t)K * K * 8);
@@ -419,23 +426,29 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
   hipLaunchKernelGGL(k_cand_scales, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, mean_abs,
                      alphas, n_alpha, K, sw.S);
   const double tn = (double)T * (double)N;
-  auto err_gen = [&](const float* s_i) {
+  // error rows of candidate i into slot c of the workspace
+  auto err_gen = [&](const float* s_i, int c) {
+    uint16_t* E = sw.E + (int64_t)c * N * K;
+    int* pe = sw.pexp + (int64_t)c * N;
     if (dt == DT_F16)
       hipLaunchKernelGGL(k_err_gen<DT_F16>, dim3((unsigned)N), dim3(256), 0, st,
-                         (const uint16_t*)w, N, K, s_i, sw.E, sw.pexp);
+                         (const uint16_t*)w, N, K, s_i, E, pe);
     else
       hipLaunchKernelGGL(k_err_gen<DT_BF16>, dim3((unsigned)N), dim3(256), 0, st,
-                         (const uint16_t*)w, N, K, s_i, sw.E, sw.pexp);
+                         (const uint16_t*)w, N, K, s_i, E, pe);
   };
   if (sw.gram) {
     const hipError_t e = launch_gram_prepare(x, dt, T, K, ldx, sw.Xt, sw.Gp, sw.G, sw.P, sw.sk, st);
     if (e != hipSuccess) return e;
     const int64_t nt = gram_loss_tiles(N, K);
-    for (int i = 0; i < n_alpha; ++i) {
-      err_gen(sw.S + (int64_t)i * K);
-      const hipError_t el = launch_gram_loss(sw.E, N, K, sw.pexp, sw.P, sw.sk, sw.partial, st);
+    for (int i0 = 0; i0 < n_alpha; i0 += sw.nc) {
+      const int nc = n_alpha - i0 < sw.nc ? n_alpha - i0 : sw.nc;
+      for (int c = 0; c < nc; ++c) err_gen(sw.S + (int64_t)(i0 + c) * K, c);
+      const hipError_t el = launch_gram_loss(sw.E, N, K, sw.pexp, sw.P, sw.sk, sw.partial, nc, st);
       if (el != hipSuccess) return el;
-      hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial, nt, tn, sw.losses + i);
+      for (int c = 0; c < nc; ++c)
+        hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial + (int64_t)c * nt, nt, tn,
+                           sw.losses + i0 + c);
     }
   } else {
     const uint16_t* Xop = (const uint16_t*)x;
@@ -451,7 +464,7 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
     const int64_t gx = (N + kCT - 1) / kCT;
     const int64_t gy = (T + kCT - 1) / kCT;
     for (int i = 0; i < n_alpha; ++i) {
-      err_gen(sw.S + (int64_t)i * K);
+      err_gen(sw.S + (int64_t)i * K, 0);
       hipLaunchKernelGGL(k_err_contract, dim3((unsigned)contract_blocks(T, N)), dim3(256), 0, st, Xop, T,
                          ldop, px, sw.E, N, K, sw.pexp, sw.partial);
       hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial, gx * gy, tn,

@@ -17,7 +17,7 @@
 //   two, to fp16 (exact for bf16 input without 1/s) in the order the nibble
 //   unpack produces; a second pre-pass picks a power of two per weight row so
 //   that step * 15 stays inside fp16.  Each lane dequantizes its packed word
-//   to step * (q - z) rounded once to fp16 and feeds v_mfma_f32_32x32x16_f16;
+//   to step * (q - z) rounded once to fp16 and feeds v_mfma_f32_16x16x32_f16;
 //   the epilogue undoes both powers of two exactly.
 #include "awq_device.h"
 #include "awq_internal.h"
@@ -124,7 +124,9 @@ __device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 c24, f16x2 c
 }
 
 // 256 x 256 output tile per block of 8 waves (2 along m x 4 along n, each wave
-// 128 x 64 = 4 x 2 blocks of 32 x 32), 64 k per stage, three LDS stages
+// 128 x 64 = 8 x 4 blocks of 16 x 16: the 16 x 16 x 32 product moves half the
+// accumulator data per flop of the 32 x 32 x 16 one and runs at a higher clock
+// under the chip's power limit), 64 k per stage, three LDS stages
 // filled by LDS DMA (buffer_load ... lds) two stages ahead of the matrix-core
 // work:
 //   A  256 rows x 64 k of fp16 activations, row r's 16-byte chunk c stored at
@@ -134,9 +136,9 @@ __device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 c24, f16x2 c
 //   B  256 columns x 8 packed words; per 32 columns the first 16 bytes of
 //      each column, then the last 16 (again 16 lanes -> 16 bank slots)
 //   C  256 columns of dequantization constants (8 bytes each)
-// Operand k order: in k16 step ks, lane half h (lanes 32 h .. 32 h + 31) holds
-// packed word 4 h + ks of its column (8 k), so that its four words are one
-// 16-byte LDS read per stage, and reads A chunk 4 h + ks to match.
+// Operand k order: in k32 step st, lane group h (lanes 16 h .. 16 h + 15) holds
+// packed word 2 h + st of its column (8 k), so that its two words are one
+// 8-byte LDS read per stage, and reads A chunk 2 h + st to match.
 // All three are plain (temporal) copies: a packed column's 128-byte line
 // serves four consecutive stages, and the activation and weight stages are
 // shared by the blocks that run on one L2 slice at the same time.  Tiles are
@@ -229,53 +231,55 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
     for (int u = 0; u < 5; ++u) copy(s, base, u);
   };
 
-  f32x16 acc[4][2];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+      for (int v = 0; v < 4; ++v) acc[a][b][v] = 0.0f;
 
-  // Per wave and stage: the dequantization constants and packed words of its
-  // two column blocks, then per k16 step the four A fragments.  The A
-  // fragments of step ks + 1 are read while the products of step ks run; the
-  // wait for the next stage and the block barrier sit in step 3, before its
-  // products, so the next stage's first reads overlap them too.  The
-  // constants are unpacked at the next stage's step 0, away from that wait.
-  struct Frag { f16x2 c24[2], c20[2], nzd[2]; u32x4 bw[2]; };
-  struct Raw { uint2 c[2]; u32x4 lo[2]; };
+  // 16 x 16 x 32 products.  Operand k order: lane group h = lane / 16 holds
+  // packed words 2 h (step 0) and 2 h + 1 (step 1) of its column, one 8-byte
+  // LDS read per stage, and A chunk 2 h + st to match.  Sub-step q = 2 st + hh
+  // multiplies the row blocks 4 hh .. 4 hh + 3 with the four column blocks; the
+  // next sub-step's four A fragments are read meanwhile.
+  struct Frag { f16x2 c24[4], c20[4], nzd[4]; uint2 bw[4]; };
+  struct Raw { uint2 c[4]; uint2 w[4]; };
   auto load_raw = [&](const uint8_t* base, Raw& w) {
+    const int h = lane >> 4;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int col = wn * 64 + nb * 32 + (lane & 31);
+    for (int nb = 0; nb < 4; ++nb) {
+      const int col = wn * 64 + nb * 16 + (lane & 15);
       w.c[nb] = *reinterpret_cast<const uint2*>(base + kAStage + kBStage + col * 8);
-      const uint8_t* bp = base + kAStage + (col >> 5) * 1024 + (col & 31) * 16;
-      w.lo[nb] = *reinterpret_cast<const u32x4*>(bp + (lane >> 5) * 512);
+      w.w[nb] = *reinterpret_cast<const uint2*>(base + kAStage + (col >> 5) * 1024 + (h >> 1) * 512 +
+                                                (col & 31) * 16 + (h & 1) * 8);
     }
   };
   auto decode = [&](const Raw& w, Frag& f) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < 4; ++nb) {
       const f16x2 cx = as_f16x2(w.c[nb].x);
       f.c24[nb] = __builtin_shufflevector(cx, cx, 0, 0);
       f.c20[nb] = __builtin_shufflevector(cx, cx, 1, 1);
       f.nzd[nb] = as_f16x2(w.c[nb].y);
-      f.bw[nb] = w.lo[nb];
+      f.bw[nb] = w.w[nb];
     }
   };
-  auto load_a = [&](const uint8_t* base, int ks, u32x4 (&a)[4]) {
+  auto load_a = [&](const uint8_t* base, int q, u32x4 (&a)[4]) {
+    const int st = q >> 1, hh = q & 1;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int r = wm * 128 + mb * 32 + (lane & 31);
-      a[mb] = *reinterpret_cast<const u32x4*>(base + r * 128 + (((4 * (lane >> 5) + ks) ^ ((r >> 1) & 7)) * 16));
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + (hh * 4 + i) * 16 + (lane & 15);
+      a[i] = *reinterpret_cast<const u32x4*>(base + r * 128 + (((2 * (lane >> 4) + st) ^ ((r >> 1) & 7)) * 16));
     }
   };
   const bool six = wv < 2;
 
   Frag F;
   Raw R;
-  u32x4 aE[4], aO[4];   // fragments of even and odd k16 steps
+  u32x4 aE[4], aO[4];   // fragments of even and odd sub-steps
+  u32x4 bq[4];          // dequantized column blocks of the current k32 step
   issue(0, lds0);
   issue(1, lds1);
   if (six) __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));
@@ -287,40 +291,37 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
   auto stage = [&](int64_t s, const uint8_t* cur, const uint8_t* nxt, const uint8_t* nxt2) {
     const bool cp = s + 2 < S;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
+    for (int q = 0; q < 4; ++q) {
       if (cp) {
-        copy(s + 2, nxt2, ks);
-        if (ks == 3) copy(s + 2, nxt2, 4);
+        copy(s + 2, nxt2, q);
+        if (q == 3) copy(s + 2, nxt2, 4);
       }
-      if (ks == 0) decode(R, F);
-      u32x4 b[2];
+      if (q == 0) decode(R, F);
+      if ((q & 1) == 0) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) b[nb] = dequant_word_f16(F.bw[nb][ks], F.c24[nb], F.c20[nb], F.nzd[nb]);
-      if (ks < 3) {
-        load_a(cur, ks + 1, (ks & 1) ? aE : aO);
+        for (int nb = 0; nb < 4; ++nb)
+          bq[nb] = dequant_word_f16(q ? F.bw[nb].y : F.bw[nb].x, F.c24[nb], F.c20[nb], F.nzd[nb]);
+      }
+      if (q < 3) {
+        load_a(cur, q + 1, (q & 1) ? aE : aO);
       } else {
-        // stage s + 1 landed (all copies but stage s + 2's) and every wave
-        // done reading the buffer the next copies overwrite; the last stage
-        // waits too, so that both paths reach the products with no read
-        // outstanding but the next stage's
         if (cp) {
           if (six) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(6));
           else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(5));
         } else {
           __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
         }
-        // unconditional: after the last stage these reads are of a stale
-        // buffer and unused, and every path reaches the products alike
         lds_barrier();
         load_a(nxt, 0, aE);
         load_raw(nxt, R);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const u32x4 (&a)[4] = (ks & 1) ? aO : aE;
+      const u32x4 (&a)[4] = (q & 1) ? aO : aE;
+      const int hh = q & 1;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32h(a[mb], b[nb], acc[mb][nb]);
+        for (int nb = 0; nb < 4; ++nb) acc[hh * 4 + i][nb] = mfma16h(a[i], bq[nb], acc[hh * 4 + i][nb]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -330,17 +331,17 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
     if (s + 2 < S) stage(s + 2, lds2, lds0, lds1);
   }
 
-  // 32x32 accumulator layout: column = lane % 32, row = 8 (v / 4) + 4 (lane / 32) + v % 4
+  // 16x16 accumulator layout: column = lane % 16, row = 4 (lane / 16) + v
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int64_t n = n0 + wn * 64 + nb * 32 + (lane & 31);
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t n = n0 + wn * 64 + nb * 16 + (lane & 15);
     if (n >= N) continue;
     const int e = en[n];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = m0 + wm * 128 + mb * 16 + 4 * (lane >> 4) + v;
         if (m < M) store_y<YDT>(y, m * ldy + n, ldexpf(acc[mb][nb][v], -(pm[m] + e)));
       }
   }
@@ -363,10 +364,6 @@ constexpr int kSkW = 4;                 // waves per block (K quarters)
 constexpr int kSkP = 2;                 // groups in flight per wave
 constexpr int64_t kSkMaxM = 16;         // tokens per B tile
 
-__device__ __forceinline__ f32x4 mfma16h(const u32x4& a, const u32x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
 
 template <int YDT, int P>
 __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict__ xq, int M, int64_t K,
