@@ -16,6 +16,12 @@
  *                      one uint8 zero point per group
  *   awq_w4a16_gemm     y = x (dequant W)^T fused: unpack, apply the group step
  *                      and zero point, optionally the per-channel 1/s
+ * and one helper that moves the per-channel 1/s out of the product:
+ *   awq_fold_scales    divides the producer of x (a LayerNorm's gain and bias,
+ *                      a preceding linear's rows) by s
+ * Linears that read the same input (q, k and v; gate and up) are searched
+ * together by passing their row-concatenated W to awq_search_scales: they then
+ * share s, and one fold serves them all.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -200,15 +206,39 @@ awq_status awq_quantize_pack(const void* w, awq_dtype dt, int64_t N, int64_t K, 
  *   inv_s    [K] float or NULL
  *   y        [M][ldy] of ydt (F16, BF16 or F32)
  *   ws       >= awq_workspace_bytes(AWQ_OP_GEMM, M, N, K, 0, 0)
- * M <= 8 runs the split-K GEMV kernel (fp32 accumulation of exact
- * int4 x activation products); larger M runs the matrix-core kernel, whose
- * operands are the dequantized weights rounded to xdt.  M == 0 or N == 0 is a
- * no-op.
+ * M == 1 runs the batch-1 GEMV (fp32 accumulation of exact int4 x fp16
+ * products of x r); larger M runs matrix-core products on fp16 operands: x r
+ * scaled by exact powers of two (per token and group for M <= 16, per token
+ * above) and the dequantized weights step (q - z) rounded once to fp16.  M == 0
+ * or N == 0 is a no-op.
  */
 awq_status awq_w4a16_gemm(const void* x, awq_dtype xdt, int64_t M, int64_t K, int64_t ldx,
                           const int32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                           int64_t N, int group_size, const float* inv_s, void* y, awq_dtype ydt,
                           int64_t ldy, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Folds the activation scaling into the operation that produces x, so that
+ * the product runs with inv_s == NULL.  "AWQ Math", section "The equivalent
+ * transform: scale up W, scale down x": the division of x_j by s_j can be
+ * moved backward into the previous layer, for example the preceding LayerNorm
+ * or linear; "AWQ > Benefits and Practical Considerations": the product applies
+ * the inverse scale only when it is not already fused into the preceding layer.
+ * In place, on v [rows][ld] (cols used):
+ *   axis 1: v[i][j] <- v[i][j] / s[j]   s has cols entries: a LayerNorm's gain
+ *           and bias, a preceding linear's bias (1 x K rows)
+ *   axis 0: v[i][j] <- v[i][j] / s[i]   s has rows entries: a preceding
+ *           linear's weight [K][C_in], whose row i produces x_i
+ * Each value becomes dt(float(v) / s) with IEEE binary32 division and
+ * round-to-nearest-even to dt.
+ *
+ *   v       device, dt F16, BF16 or F32, aligned to its element size
+ *   rows, cols  >= 0 (an empty array is a no-op); ld >= cols
+ *   s       device float, finite and nonzero
+ *   axis    0 or 1
+ */
+awq_status awq_fold_scales(void* v, awq_dtype dt, int64_t rows, int64_t cols, int64_t ld, const float* s,
+                           int axis, void* stream);
 
 #ifdef __cplusplus
 }

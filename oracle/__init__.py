@@ -32,5 +32,6 @@ from .awq import (  # noqa: F401
     quantize_layer, pack_codes, unpack_codes,
     search_losses, search_losses_operand_model, choose_candidate, search_scales,
     w4a16_matmul, w4a16_matmul_rows,
+    round_bf16, round_storage, fold_scales,
     symmetric_rtn,
 )

@@ -343,6 +343,48 @@ def w4a16_matmul_rows(x, words, step, zeros, rows, inv_s=None, group: int = GROU
 
 
 # --------------------------------------------------------------------------
+# O8  folding the activation scaling into the producer of x
+#     "AWQ Math", "The equivalent transform: scale up W, scale down x": the
+#     division of x_j by s_j can be folded backward into the previous layer,
+#     for example the preceding LayerNorm or linear; "AWQ > Benefits and
+#     Practical Considerations": the product applies 1/s only when it is not
+#     already fused into the preceding layer.
+#     READING: each folded value is dt(float32(v) / float32(s)) -- one IEEE
+#     binary32 division, then round-to-nearest-even to the storage type.
+# --------------------------------------------------------------------------
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Finite float32 values rounded to bfloat16 (8 significant bits),
+    nearest with ties to even, returned as float32: add half of the dropped
+    low 16 bits of the binary32 pattern, plus one when the kept part is odd,
+    then clear them."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    odd = (b >> 16) & 1
+    r = ((b + 0x7FFF + odd) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).reshape(np.shape(a))
+
+
+def round_storage(a32: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values rounded to the storage type ('f16', 'bf16', 'f32')."""
+    a32 = np.asarray(a32, dtype=np.float32)
+    if dtype == "f16":
+        return a32.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        return round_bf16(a32)
+    return a32
+
+
+def fold_scales(v: np.ndarray, s: np.ndarray, axis: int = 1, dtype: str = "f16") -> np.ndarray:
+    """v [rows, cols] float32 holding dtype values.  axis 1: column j divided
+    by s[j] (a LayerNorm's gain and bias, a bias: 1 x K rows); axis 0: row i
+    divided by s[i] (a preceding linear's weight [K, C_in], whose row i
+    produces x_i).  Returns the folded values as float32."""
+    v32 = np.asarray(v, dtype=np.float32)
+    s32 = np.asarray(s, dtype=np.float32)
+    q = v32 / (s32[None, :] if axis == 1 else s32[:, None])   # IEEE binary32 division
+    return round_storage(q, dtype)
+
+
+# --------------------------------------------------------------------------
 # The pages' textbook lead-in quantizer, used only to reproduce their worked
 # example: "AWQ Math", "Weight-only quantization and where it breaks"
 # (Q(w) = step * round(w / step), step = max|w| / 2^(N-1)).

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_four_calls_and_helpers():
     names = declared_functions()
     for n in ("awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_w4a16_gemm",
-              "awq_workspace_bytes", "awq_status_str", "awq_abi_version"):
+              "awq_fold_scales", "awq_workspace_bytes", "awq_status_str", "awq_abi_version"):
         assert n in names
 
 
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.awq_abi_version() == 1
+    assert lib.awq_abi_version() == 2
     for code in range(8):
         assert lib.awq_status_str(code).decode()
     assert lib.awq_status_str(0).decode() == "ok"
@@ -145,3 +145,22 @@ def test_gemm_validation():
     assert call(x=BAD) == 4
     assert call(ldx=4100) == 4
     assert call(r=BAD) == 4
+
+
+def test_fold_validation():
+    lib = _lib()
+    E = abi
+    f = lib.awq_fold_scales
+    NULL = None
+    A = ctypes.c_void_p(1 << 20)          # never dereferenced: every case fails on the host
+    S = ctypes.c_void_p(1 << 21)
+    assert f(A, 7, 4, 8, 8, S, 1, NULL) == 3                 # dtype
+    assert f(A, E.AWQ_F16, 4, 8, 7, S, 1, NULL) == 2         # ld < cols
+    assert f(A, E.AWQ_F16, -1, 8, 8, S, 1, NULL) == 2        # negative rows
+    assert f(A, E.AWQ_F16, 4, 8, 8, S, 2, NULL) == 2         # axis
+    assert f(NULL, E.AWQ_F16, 4, 8, 8, S, 1, NULL) == 1
+    assert f(A, E.AWQ_F16, 4, 8, 8, NULL, 0, NULL) == 1
+    assert f(ctypes.c_void_p((1 << 20) + 1), E.AWQ_F16, 4, 8, 8, S, 1, NULL) == 4   # odd address
+    assert f(ctypes.c_void_p((1 << 20) + 2), E.AWQ_F32, 4, 8, 8, S, 1, NULL) == 4
+    assert f(NULL, E.AWQ_F16, 0, 8, 8, NULL, 1, NULL) == 0   # empty: no-op
+

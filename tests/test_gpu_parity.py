@@ -337,3 +337,66 @@ def test_determinism():
         outs.append([t.cpu().clone() for t in (m, s, L, q, sc, z, y, y1)])
     for a, b in zip(*outs):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+# ---------------------------------------------------------------------------
+# folding 1/s into the producer of x ("AWQ Math", "The equivalent transform:
+# scale up W, scale down x") and the shared-input search of q, k and v
+# ---------------------------------------------------------------------------
+_FOLD_DT = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,cols,ld,axis", [(1, 4096, 4096, 1), (37, 300, 304, 1), (37, 300, 304, 0),
+                                               (1000, 513, 513, 0), (3, 1, 1, 1)])
+def test_fold_scales_bit_exact(dtype, rows, cols, ld, axis):
+    g = np.random.Generator(np.random.PCG64(rows * 7 + cols + axis))
+    full = torch.from_numpy(g.uniform(-3, 3, (rows, ld)).astype(np.float32)).to(dtype)
+    s = np.exp(g.uniform(-3, 3, cols if axis == 1 else rows)).astype(np.float32)
+    v = gpu(full)
+    awq.awq_fold_scales(v[:, :cols], gpu(torch.from_numpy(s)), axis=axis)
+    torch.cuda.synchronize()
+    want = O.fold_scales(f32(full)[:, :cols], s, axis, _FOLD_DT[dtype])
+    got = f32(v.cpu())
+    assert np.array_equal(got[:, :cols].view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(got[:, cols:], f32(full)[:, cols:])      # padding untouched
+
+
+def test_shared_input_search_and_fold_c3():
+    """q, k and v of a decoder layer read one input: one search on their
+    row-concatenated W gives one s for all three; 1/s folded into the
+    preceding LayerNorm's gain and bias leaves the products without inv_s, and
+    they match the unfolded layer."""
+    X = WL.calibration(WL.workload(3, "q"))
+    assert torch.equal(X, WL.calibration(WL.workload(3, "v")))          # the shared input
+    W = torch.cat([WL.weight(WL.workload(3, "q"))[:256], WL.weight(WL.workload(3, "k"))[:128],
+                   WL.weight(WL.workload(3, "v"))[:128]])
+    _check_search(W, X, F16)                                                 # search parity
+    m = awq.awq_act_stats(gpu(X))
+    al = gpu(torch.from_numpy(WL.alpha_grid(20)))
+    s, inv, _, _ = awq.awq_search_scales(gpu(W), gpu(X), m, al)
+    q, sc, z = awq.awq_quantize_pack(gpu(W), s)
+    g = np.random.Generator(np.random.PCG64(33))
+    K = W.shape[1]
+    gamma = torch.from_numpy(g.uniform(0.5, 1.5, K).astype(np.float16))
+    beta = torch.from_numpy(g.uniform(-0.1, 0.1, K).astype(np.float16))
+    gf, bf = gpu(gamma.clone()), gpu(beta.clone())
+    awq.awq_fold_scales(gf, s)
+    awq.awq_fold_scales(bf, s)
+    torch.cuda.synchronize()
+    s_np = s.cpu().numpy()
+    assert np.array_equal(f32(gf.cpu()), O.fold_scales(f32(gamma)[None, :], s_np, 1, "f16")[0])
+    assert np.array_equal(f32(bf.cpu()), O.fold_scales(f32(beta)[None, :], s_np, 1, "f16")[0])
+    # a normalized decode batch through the LayerNorm's affine part, folded and not
+    n = g.standard_normal((8, K)).astype(np.float32)
+    x = torch.from_numpy((n * f32(gamma) + f32(beta)).astype(np.float16))
+    xf = torch.from_numpy((n * f32(gf.cpu()) + f32(bf.cpu())).astype(np.float16))
+    words, step, zeros = q.cpu().numpy(), sc.cpu().numpy(), z.cpu().numpy()
+    inv_np = inv.cpu().numpy()
+    ref = O.w4a16_matmul(f32(x), words, step, zeros, inv_np)                # the unfolded layer
+    for M in (1, 8):
+        y = awq.awq_w4a16_gemm(gpu(xf[:M]), q, sc, z, None, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert rel_max_err(f32(y), O.w4a16_matmul(f32(xf[:M]), words, step, zeros, None)) <= GEMM_TOL
+        assert rel_max_err(f32(y), ref[:M]) <= GEMM_TOL
+

@@ -558,3 +558,62 @@ def test_operand_model_row_exponent():
             assert pi == 0
         else:
             assert 2.0 ** 13 <= mx * 2.0 ** pi < 2.0 ** 14
+
+
+# ---------------------------------------------------------------------------
+# O8  folding 1/s into the producer of x ("AWQ Math", "The equivalent
+# transform: scale up W, scale down x")
+# ---------------------------------------------------------------------------
+def test_round_bf16_matches_library_cast_including_ties():
+    """bfloat16 rounding against torch's float -> bfloat16 cast (a library
+    routine the oracle does not use), with exact ties in both directions."""
+    torch = pytest.importorskip("torch")
+    g = np.random.Generator(np.random.PCG64(80))
+    a = (g.standard_normal(20000) * np.exp(g.uniform(-20, 20, 20000))).astype(np.float32)
+    bits = g.integers(0, 1 << 16, 2000).astype(np.uint32) << 16
+    ties = (bits | 0x8000).view(np.float32)                       # exactly halfway
+    ties = ties[np.isfinite(ties)]
+    for v in (a, ties):
+        want = torch.from_numpy(v.copy()).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(O.round_bf16(v).view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_fold_by_powers_of_two_and_one_is_exact(dtype):
+    g = np.random.Generator(np.random.PCG64(81))
+    v = O.round_storage(g.uniform(-4, 4, (3, 256)).astype(np.float32), dtype)
+    s = (2.0 ** g.integers(-3, 4, 256)).astype(np.float32)
+    assert np.array_equal(O.fold_scales(v, s, 1, dtype), (v / s[None, :]).astype(np.float32))
+    assert np.array_equal(O.fold_scales(v, np.ones(256, np.float32), 1, dtype), v)
+    s0 = (2.0 ** g.integers(-3, 4, 3)).astype(np.float32)
+    assert np.array_equal(O.fold_scales(v, s0, 0, dtype), (v / s0[:, None]).astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype,u", [("f16", 2.0 ** -11), ("bf16", 2.0 ** -8), ("f32", 2.0 ** -24)])
+def test_fold_gives_the_scaled_activation(dtype, u):
+    """The fold reproduces x / s through the producer of x, in fp64 up to the
+    rounding of the folded values: a LayerNorm x = n * gamma + beta (gain and
+    bias folded along axis 1) and a preceding linear x = W_prev u (rows of
+    W_prev folded along axis 0)."""
+    g = np.random.Generator(np.random.PCG64(82))
+    K, C = 384, 200
+    s = np.exp(g.uniform(-2, 2, K)).astype(np.float32)
+    n = g.standard_normal(K)
+    gamma = O.round_storage(g.uniform(0.5, 1.5, K).astype(np.float32), dtype)
+    beta = O.round_storage(g.uniform(-0.2, 0.2, K).astype(np.float32), dtype)
+    gf = O.fold_scales(gamma[None, :], s, 1, dtype)[0].astype(np.float64)
+    bf = O.fold_scales(beta[None, :], s, 1, dtype)[0].astype(np.float64)
+    x = n * gamma + beta
+    xf = n * gf + bf
+    bound = (u + 2.0 ** -24) * 1.01 * (np.abs(n * gamma) + np.abs(beta)) / s
+    assert np.all(np.abs(xf - x / s) <= bound)
+    W = O.round_storage(g.standard_normal((K, C)).astype(np.float32) * 0.05, dtype)
+    uu = g.standard_normal(C)
+    Wf = O.fold_scales(W, s, 0, dtype).astype(np.float64)
+    y = W.astype(np.float64) @ uu
+    yf = Wf @ uu
+    bound = (u + 2.0 ** -24) * 1.01 * (np.abs(W.astype(np.float64)) @ np.abs(uu)) / s
+    assert np.all(np.abs(yf - y / s) <= bound)
+    # dividing columns instead of rows gives something else
+    assert not np.allclose(O.fold_scales(W, s[:C], 1, dtype), Wf)
+

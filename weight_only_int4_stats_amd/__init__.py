@@ -18,7 +18,7 @@ from ._abi import (AWQ_BF16, AWQ_F16, AWQ_F32, AWQ_GROUP, AWQ_OP_ACT_STATS, AWQ_
                    AWQ_OP_QUANTIZE, AWQ_OP_SEARCH, AwqError, lib)
 
 __all__ = ["awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_w4a16_gemm",
-           "awq_workspace_bytes", "AwqError", "lib"]
+           "awq_fold_scales", "awq_workspace_bytes", "AwqError", "lib"]
 
 _DT = {torch.float16: AWQ_F16, torch.bfloat16: AWQ_BF16, torch.float32: AWQ_F32}
 
@@ -143,3 +143,19 @@ def awq_w4a16_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
                               ldy, _ptr(ws), wsb, _stream(dev, stream))
     _abi.check("awq_w4a16_gemm", st)
     return y
+
+
+def awq_fold_scales(v: torch.Tensor, s: torch.Tensor, axis: int = 1, stream=None) -> torch.Tensor:
+    """In place: v[i][j] /= s[j] (axis 1) or s[i] (axis 0); a 1-D v is one row."""
+    _dev(v, "v")
+    _dev(s, "s")
+    if s.dtype != torch.float32 or s.dim() != 1 or not s.is_contiguous():
+        raise ValueError("s must be a contiguous float32 vector")
+    v2 = v.view(1, -1) if v.dim() == 1 else v
+    rows, cols, ld = _rows(v2, "v")
+    if s.numel() != (cols if axis == 1 else rows):
+        raise ValueError("s must have one entry per column (axis 1) or per row (axis 0)")
+    st = lib().awq_fold_scales(_ptr(v2), _DT.get(v.dtype, -1), rows, cols, ld, _ptr(s), axis,
+                               _stream(v.device, stream))
+    _abi.check("awq_fold_scales", st)
+    return v

@@ -32,6 +32,7 @@ SIGNATURES = {
     "awq_quantize_pack": (_i, [_p, _i, _i64, _i64, _p, _i, _p, _p, _p, _p, _p]),
     "awq_w4a16_gemm": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _i64, _i, _p, _p, _i, _i64, _p,
                             _sz, _p]),
+    "awq_fold_scales": (_i, [_p, _i, _i64, _i64, _i64, _p, _i, _p]),
 }
 
 _lib = None

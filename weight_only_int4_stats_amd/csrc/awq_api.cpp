@@ -18,7 +18,7 @@ awq_status from_hip(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_HI
 
 extern "C" {
 
-int awq_abi_version(void) { return 1; }
+int awq_abi_version(void) { return 2; }
 
 const char* awq_status_str(awq_status st) {
   switch (st) {
@@ -107,6 +107,17 @@ awq_status awq_w4a16_gemm(const void* x, awq_dtype xdt, int64_t M, int64_t K, in
   if (need && (!ws || ws_bytes < need || !aligned256(ws))) return AWQ_ERR_WORKSPACE;
   return from_hip(awq::launch_w4a16(x, (int)xdt, M, K, ldx, (const uint32_t*)qweight, scales,
                                     zeros, N, inv_s, y, (int)ydt, ldy, ws, (hipStream_t)stream));
+}
+
+awq_status awq_fold_scales(void* v, awq_dtype dt, int64_t rows, int64_t cols, int64_t ld, const float* s,
+                           int axis, void* stream) {
+  if (dt != AWQ_F16 && dt != AWQ_BF16 && dt != AWQ_F32) return AWQ_ERR_DTYPE;
+  if (rows < 0 || cols < 0 || ld < cols || (axis != 0 && axis != 1)) return AWQ_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return AWQ_OK;
+  if (!v || !s) return AWQ_ERR_NULL;
+  const uintptr_t el = dt == AWQ_F32 ? 4u : 2u;
+  if (((uintptr_t)v & (el - 1)) != 0 || ((uintptr_t)s & 3u) != 0) return AWQ_ERR_ALIGN;
+  return from_hip(awq::launch_fold_scales(v, (int)dt, rows, cols, ld, s, axis, (hipStream_t)stream));
 }
 
 }  // extern "C"

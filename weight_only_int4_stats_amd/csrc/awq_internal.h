@@ -39,6 +39,10 @@ hipError_t launch_gram_loss(const uint16_t* E, int64_t N, int64_t K, const int* 
                             const uint16_t* P, const int* sk, double* partial, int nc,
                             hipStream_t st);
 
+// ---- folding 1/s into the producer of x (k_fold.hip) ---------------------------
+hipError_t launch_fold_scales(void* v, int dt, int64_t rows, int64_t cols, int64_t ld, const float* s,
+                              int axis, hipStream_t st);
+
 // ---- W4A16 product ----------------------------------------------------------
 bool gemv1_supported(int64_t K, int64_t N);   // batch-1 GEMV kernels cover this shape
 hipError_t launch_gemv1(const void* x, int xdt, int64_t K, const uint32_t* qw,
