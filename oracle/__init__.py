@@ -28,7 +28,7 @@ from .awq import (  # noqa: F401
     act_mean_abs, act_fixed_point_sums,
     candidate_scales,
     fp16_round_up, scale_columns, unscale_activation,
-    group_quant_params, quantize_codes, dequantize,
+    code_max, group_quant_params, quantize_codes, dequantize,
     quantize_layer, pack_codes, unpack_codes,
     search_losses, search_losses_operand_model, choose_candidate, search_scales,
     w4a16_matmul, w4a16_matmul_rows,

@@ -1,4 +1,4 @@
-"""AWQ oracle: statistics, scale search, group-128 asymmetric INT4, W4A16 product.
+"""AWQ oracle: statistics, scale search, group-wise INT4 (and its variants), W4A16 product.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).  Plain NumPy; float64
 unless a step is defined in float32 / float16.
@@ -83,6 +83,8 @@ def candidate_scales(m: np.ndarray, alphas: np.ndarray) -> np.ndarray:
 #     granularity, and complexity": groups of 128 input channels, each with
 #     its own step and zero point; "AWQ > Benefits and Practical
 #     Considerations": one scale and one zero point per 128 weights.
+#     Variants the same passages name: other group sizes (64, 256), other bit
+#     widths N, and the symmetric step max|w| / 2^(N-1) of the lead-in.
 # --------------------------------------------------------------------------
 def fp16_round_up(d: np.ndarray) -> np.ndarray:
     """Smallest float16 >= d (d float32, d >= 0), as float16.
@@ -98,33 +100,54 @@ def fp16_round_up(d: np.ndarray) -> np.ndarray:
     return h.astype(np.float16)
 
 
-def group_quant_params(wg: np.ndarray):
-    """Step and zero point of each group.  ``wg`` float32 [..., G, 128].
+def code_max(bits: int = NBITS, symmetric: bool = False) -> int:
+    """Largest stored code: 2^N - 1 for the asymmetric grid (2^N levels); 2^N
+    for the symmetric one, whose codes run over -2^(N-1) .. 2^(N-1) (2^N + 1
+    levels) and are stored shifted up by the zero point 2^(N-1)."""
+    return (1 << bits) if symmetric else (1 << bits) - 1
 
-    lo = min(0, min w'), hi = max(0, max w')          READING: range holds 0
-    d  = fp32( fp32(hi - lo) / 15 )                    2^N - 1 = 15 intervals
-    step (fp16) = round-up(d), at least 2^-24;  D = fp32(step)
-    z  = clamp( rint( fp32(-lo / D) ), 0, 15 )         integer zero point
+
+def group_quant_params(wg: np.ndarray, bits: int = NBITS, symmetric: bool = False):
+    """Step and zero point of each group.  ``wg`` float32 [..., G, group].
+
+    Asymmetric (the default; scale and zero point per group, "AWQ > Benefits
+    and Practical Considerations"):
+      lo = min(0, min w'), hi = max(0, max w')          READING: range holds 0
+      d  = fp32( fp32(hi - lo) / (2^N - 1) )             2^N levels, 15 intervals at N = 4
+      z  = clamp( rint( fp32(-lo / D) ), 0, 2^N - 1 )    integer zero point
+    Symmetric ("AWQ Math", "Weight-only quantization and where it breaks":
+    step = max|w| / 2^(N-1), Q(w) = step * round(w / step)):
+      d  = fp32( max|w'| / 2^(N-1) )                     exact: a power-of-two divisor
+      z  = 2^(N-1)                                       codes stored shifted by z
+    Both: step (fp16) = round-up(d), at least 2^-24; D = fp32(step).
     Returns (D float32, step float16, z float32, d float32).
     """
     wg = np.asarray(wg, dtype=np.float32)
     assert np.all(np.isfinite(wg)), "non-finite weights are outside the method's domain"
-    lo = np.minimum(wg.min(axis=-1), np.float32(0))
-    hi = np.maximum(wg.max(axis=-1), np.float32(0))
-    d = (hi - lo) / np.float32(QMAX)
+    assert 2 <= bits <= (7 if symmetric else 8), "codes must fit one byte"
+    if symmetric:
+        amax = np.max(np.abs(wg), axis=-1)
+        d = amax / np.float32(1 << (bits - 1))
+    else:
+        lo = np.minimum(wg.min(axis=-1), np.float32(0))
+        hi = np.maximum(wg.max(axis=-1), np.float32(0))
+        d = (hi - lo) / np.float32((1 << bits) - 1)
     step = fp16_round_up(np.maximum(d, np.float32(FP16_TINY)))
     assert np.all(np.isfinite(step)), "group range exceeds the float16 step range"
     D = step.astype(np.float32)
-    z = np.clip(np.rint((-lo) / D), 0, QMAX).astype(np.float32)
+    if symmetric:
+        z = np.full(D.shape, 1 << (bits - 1), dtype=np.float32)
+    else:
+        z = np.clip(np.rint((-lo) / D), 0, (1 << bits) - 1).astype(np.float32)
     return D, step, z, d
 
 
-def quantize_codes(wg: np.ndarray, D: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """q = clamp( rint( fp32(w' / D) ) + z, 0, 15 ) as uint8.  round() is
-    round-half-to-even (READING)."""
+def quantize_codes(wg: np.ndarray, D: np.ndarray, z: np.ndarray, cmax: int = QMAX) -> np.ndarray:
+    """q = clamp( rint( fp32(w' / D) ) + z, 0, cmax ) as uint8 (cmax from
+    ``code_max``).  round() is round-half-to-even (READING)."""
     wg = np.asarray(wg, dtype=np.float32)
     q = np.rint(wg / D[..., None]) + z[..., None]
-    return np.clip(q, 0, QMAX).astype(np.uint8)
+    return np.clip(q, 0, cmax).astype(np.uint8)
 
 
 def dequantize(q: np.ndarray, D: np.ndarray, z: np.ndarray) -> np.ndarray:
@@ -144,21 +167,25 @@ def unscale_activation(x: np.ndarray, s: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64) / np.asarray(s).astype(np.float64)
 
 
-def quantize_layer(W: np.ndarray, s: np.ndarray | None = None, group: int = GROUP):
+def quantize_layer(W: np.ndarray, s: np.ndarray | None = None, group: int = GROUP,
+                   bits: int = NBITS, symmetric: bool = False):
     """Quantize W' = W * diag(s) ("AWQ Math", "The equivalent transform").
 
     W float32 [N, K] holding fp16/bf16 values; s float32 [K] or None (s = 1,
-    plain round-to-nearest).  Returns dict with codes q uint8 [N, K], step
-    float16 [N, G], D float32 [N, G], z uint8 [N, G], d float32 [N, G]
-    (pre-rounding step), wp float32 [N, K] (the scaled weights).
+    plain round-to-nearest).  Groups are ``group`` consecutive input channels
+    of one row ("AWQ Math", "Shapes, granularity, and complexity"); ``bits`` and
+    ``symmetric`` select the grid (``group_quant_params``).  Returns dict with
+    codes q uint8 [N, K], step float16 [N, G], D float32 [N, G], z uint8
+    [N, G], d float32 [N, G] (pre-rounding step), wp float32 [N, K] (the
+    scaled weights).
     """
     W = np.asarray(W, dtype=np.float32)
     N, K = W.shape
     assert K % group == 0, "K must be a multiple of the group size"
     wp = W if s is None else scale_columns(W, np.asarray(s, dtype=np.float32))
     wg = wp.reshape(N, K // group, group)
-    D, step, z, d = group_quant_params(wg)
-    q = quantize_codes(wg, D, z).reshape(N, K)
+    D, step, z, d = group_quant_params(wg, bits, symmetric)
+    q = quantize_codes(wg, D, z, code_max(bits, symmetric)).reshape(N, K)
     return {"q": q, "step": step, "D": D, "z": z.astype(np.uint8), "d": d, "wp": wp}
 
 
@@ -189,9 +216,10 @@ def unpack_codes(words: np.ndarray) -> np.ndarray:
 #     Q(W diag(s)) diag(s)^-1 x ||, measured as the mean squared error over
 #     the calibration activations; a small grid of alpha; forward passes only.
 # --------------------------------------------------------------------------
-def _dequantized_weight(W: np.ndarray, s: np.ndarray, group: int = GROUP) -> np.ndarray:
+def _dequantized_weight(W: np.ndarray, s: np.ndarray, group: int = GROUP,
+                        bits: int = NBITS, symmetric: bool = False) -> np.ndarray:
     """W_hat = Q(W diag(s)) diag(s)^-1 in float64."""
-    r = quantize_layer(W, s, group)
+    r = quantize_layer(W, s, group, bits, symmetric)
     N, K = W.shape
     G = K // group
     grid = dequantize(r["q"].reshape(N, G, group), r["D"], r["z"].astype(np.float32))
@@ -199,13 +227,14 @@ def _dequantized_weight(W: np.ndarray, s: np.ndarray, group: int = GROUP) -> np.
 
 
 def search_losses(W: np.ndarray, X: np.ndarray, S: np.ndarray, group: int = GROUP,
-                  t_chunk: int = 4096) -> np.ndarray:
+                  t_chunk: int = 4096, *, bits: int = NBITS, symmetric: bool = False) -> np.ndarray:
     """L_i = (1 / (T N)) * sum_t sum_n ( sum_k (W - W_hat_i)[n, k] x_t[k] )^2.
 
     READING: the objective is the mean squared error (same argmin as the norm);
     the target is the unrounded W x; W_hat_i uses the stored fp16 step, so the
     loss scores exactly what is deployed.  W float32 [N, K], X float32 [T, K],
-    S float32 [n_alpha, K].  float64 throughout.
+    S float32 [n_alpha, K]; ``bits`` / ``symmetric`` select the quantizer's
+    grid.  float64 throughout.
     """
     W = np.asarray(W, dtype=np.float32)
     X = np.asarray(X, dtype=np.float32)
@@ -214,7 +243,7 @@ def search_losses(W: np.ndarray, X: np.ndarray, S: np.ndarray, group: int = GROU
     out = np.empty(S.shape[0], dtype=np.float64)
     W64 = W.astype(np.float64)
     for i in range(S.shape[0]):
-        E = W64 - _dequantized_weight(W, S[i], group)
+        E = W64 - _dequantized_weight(W, S[i], group, bits, symmetric)
         acc = 0.0
         for t0 in range(0, T, t_chunk):
             P = X[t0:t0 + t_chunk].astype(np.float64) @ E.T
@@ -241,7 +270,8 @@ def _round_rows_fp16(a32: np.ndarray):
 
 def search_losses_operand_model(W: np.ndarray, X: np.ndarray, S: np.ndarray,
                                 x_is_fp16: bool = True, group: int = GROUP,
-                                t_chunk: int = 4096) -> np.ndarray:
+                                t_chunk: int = 4096, *, bits: int = NBITS,
+                                symmetric: bool = False) -> np.ndarray:
     """The same losses as ``search_losses``, scored in the precision of a
     matrix-core evaluation, so that the chosen index -- an integer decided by
     floating point -- is taken in the precision that evaluation uses.
@@ -266,7 +296,7 @@ def search_losses_operand_model(W: np.ndarray, X: np.ndarray, S: np.ndarray,
     out = np.empty(S.shape[0], dtype=np.float64)
     for i in range(S.shape[0]):
         s = np.asarray(S[i], dtype=np.float32)
-        r = quantize_layer(W, s, group)
+        r = quantize_layer(W, s, group, bits, symmetric)
         Dk = np.repeat(r["D"], group, axis=1)                       # float32 [N, K]
         zk = np.repeat(r["z"].astype(np.float32), group, axis=1)
         grid = Dk * (r["q"].astype(np.float32) - zk)                # exact in float32
@@ -293,7 +323,8 @@ def choose_candidate(losses: np.ndarray) -> int:
 
 
 def search_scales(W: np.ndarray, X: np.ndarray, m: np.ndarray, alphas: np.ndarray,
-                  group: int = GROUP, operand_model: str | None = None):
+                  group: int = GROUP, operand_model: str | None = None, *,
+                  bits: int = NBITS, symmetric: bool = False):
     """Full search: candidate scales, losses, argmin.  Returns
     (best index, s* float32 [K], 1/s* float32 [K], losses float64 [n]).
     operand_model: None scores exactly (float64); "fp16" / "fp16-scaled-x"
@@ -301,9 +332,10 @@ def search_scales(W: np.ndarray, X: np.ndarray, m: np.ndarray, alphas: np.ndarra
     float16, or rounded to float16 per token)."""
     S = candidate_scales(m, alphas)
     if operand_model is None:
-        L = search_losses(W, X, S, group)
+        L = search_losses(W, X, S, group, bits=bits, symmetric=symmetric)
     else:
-        L = search_losses_operand_model(W, X, S, operand_model == "fp16", group)
+        L = search_losses_operand_model(W, X, S, operand_model == "fp16", group,
+                                        bits=bits, symmetric=symmetric)
     i = choose_candidate(L)
     s = S[i]
     return i, s, (np.float32(1.0) / s).astype(np.float32), L

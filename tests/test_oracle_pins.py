@@ -617,3 +617,161 @@ def test_fold_gives_the_scaled_activation(dtype, u):
     # dividing columns instead of rows gives something else
     assert not np.allclose(O.fold_scales(W, s[:C], 1, dtype), Wf)
 
+
+
+# ------------------------------------------------------- quantizer variants
+def _nearest_code_brute(quo, zz, cmax):
+    """Code c in 0..cmax whose level c - z is nearest to the rational quo,
+    ties to the even integer c - z."""
+    best = None
+    for c in range(cmax + 1):
+        key = (abs(quo - (c - zz)), (c - zz) % 2)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def test_symmetric_step_is_the_worked_example():
+    """The symmetric variant reproduces the pages' worked example: 4 bits and a
+    group whose largest magnitude is 1.0 give the step 1/8 (zero point 8,
+    codes -8 .. 8 around it); through the whole layer quantizer, a channel with
+    |x| = 10 then carries output error 0.3125, and scaling it by 2 (group
+    maximum unchanged) gives 0.15625 ("AWQ Math", "A worked numeric example";
+    fixture worked_example.json)."""
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    g = _rng(60)
+    R, grp = 4000, 128
+    W = g.uniform(-0.25, 0.25, (R, 2 * grp)).astype(np.float32)
+    W[:, 0] = ex["group_max_abs"]                 # each group's largest magnitude
+    W[:, grp] = -ex["group_max_abs"]
+    for sc, want in [(1.0, ex["err_before"]), (ex["scale"], ex["err_after"])]:
+        s = np.full(2 * grp, sc, np.float32)
+        s[0] = s[grp] = 1.0                        # the maxima stay where they are
+        r = O.quantize_layer(W, s, grp, bits=ex["bits"], symmetric=True)
+        assert np.all(r["D"] == ex["step"]) and np.all(r["z"] == 8)
+        assert np.all(r["q"][:, 0] == 16) and np.all(r["q"][:, grp] == 0)
+        Wh = O.dequantize(r["q"].reshape(R, 2, grp), r["D"], r["z"].astype(np.float32)).reshape(R, -1)
+        e = np.abs(Wh - r["wp"].astype(np.float64))[:, np.r_[1:grp, grp + 1:2 * grp]]
+        got = e.mean() * ex["mean_abs_activation"] / sc
+        assert abs(got - want) / want < 0.01
+
+
+@pytest.mark.parametrize("bits", [2, 3, 5, 7])
+def test_symmetric_levels_brute_force(bits):
+    """Symmetric grid: 2^N + 1 levels D (q - 2^(N-1)), the group's extreme
+    magnitude maps to the end code when max|w| / 2^(N-1) is an fp16 value, and
+    every code is the nearest level (exhaustive, exact rationals)."""
+    g = _rng(61 + bits)
+    half = 1 << (bits - 1)
+    cmax = O.code_max(bits, True)
+    assert cmax == 2 * half
+    wp = _fp16_values(g.standard_normal((30, 128)) * g.uniform(0.01, 2, (30, 1)))
+    D, _, z, d = O.group_quant_params(wp, bits, True)
+    assert np.all(z == half) and np.all(D >= d)
+    q = O.quantize_codes(wp, D, z, cmax)
+    assert q.max() <= cmax
+    ok, _ = _bound_ok(wp, D, q, z)
+    assert ok
+    for gi in range(wp.shape[0]):
+        for k in range(0, 128, 5):
+            quo = Fraction(float(np.float32(wp[gi, k]) / np.float32(D[gi])))
+            assert q[gi, k] == _nearest_code_brute(quo, half, cmax)
+    # a power-of-two maximum: the step is exact and the extremes use both ends
+    v = np.linspace(-1, 1, 1025).astype(np.float32)[None, :]
+    Dv, _, zv, _ = O.group_quant_params(v, bits, True)
+    qv = O.quantize_codes(v, Dv, zv, cmax)
+    assert Dv[0] == np.float32(1.0 / half) and qv[0, 0] == 0 and qv[0, -1] == cmax
+    assert np.unique(qv).size == cmax + 1
+
+
+@pytest.mark.parametrize("bits", [2, 3, 5, 8])
+def test_asymmetric_bits_levels_bound_and_nearest(bits):
+    """N-bit asymmetric grid: 2^N levels, a dense sweep reaches both end codes,
+    the half-step bound holds, and codes are the nearest level."""
+    g = _rng(70 + bits)
+    cmax = O.code_max(bits, False)
+    assert cmax == (1 << bits) - 1
+    for _ in range(20):
+        lo, hi = -g.uniform(0.1, 3), g.uniform(0.1, 3)
+        wp = _fp16_values(np.linspace(lo, hi, 128))[None, :]
+        D, _, z, _ = O.group_quant_params(wp, bits)
+        q = O.quantize_codes(wp, D, z, cmax)
+        assert q[0, 0] == 0 and q.max() <= cmax and q.max() >= cmax - 1
+        levels = np.unique(O.dequantize(np.arange(cmax + 1, dtype=np.uint8)[None, :], D, z))
+        assert levels.size == cmax + 1
+    wp = _fp16_values(g.standard_normal((40, 128)) * g.uniform(0.001, 2, (40, 1)))
+    D, _, z, d = O.group_quant_params(wp, bits)
+    assert np.all(D >= d) and np.all(z <= cmax)
+    q = O.quantize_codes(wp, D, z, cmax)
+    ok, _ = _bound_ok(wp, D, q, z)
+    assert ok
+    for gi in range(0, 40, 3):
+        for k in range(0, 128, 7):
+            quo = Fraction(float(np.float32(wp[gi, k]) / np.float32(D[gi])))
+            assert q[gi, k] == _nearest_code_brute(quo, int(z[gi]), cmax)
+
+
+@pytest.mark.parametrize("group", [64, 256])
+def test_group_size_slices_and_wider_step(group):
+    """Group g of row n is input channels [g * group, (g + 1) * group) of that
+    row, quantized on its own ("AWQ Math", "Shapes, granularity, and
+    complexity"); checked slice by slice with explicit indexing.  A group of
+    256 never has a smaller step than either of its 128-halves, and the same
+    step when both halves span the same range ("CPU-SLM implications and
+    common pitfalls": larger groups widen the step)."""
+    g = _rng(80 + group)
+    N, K = 5, 1024
+    W = _fp16_values(g.standard_normal((N, K)) * 0.03)
+    W[:, 7] *= 30
+    s = np.exp(g.uniform(-1, 1, K)).astype(np.float32)
+    r = O.quantize_layer(W, s, group)
+    wp = O.scale_columns(W, s)
+    for n in range(N):
+        for gi in range(K // group):
+            sl = wp[n, gi * group:(gi + 1) * group][None, :]
+            D, step, z, _ = O.group_quant_params(sl)
+            assert r["D"][n, gi] == D[0] and r["z"][n, gi] == z[0]
+            assert np.array_equal(r["q"][n, gi * group:(gi + 1) * group], O.quantize_codes(sl, D, z)[0])
+    if group == 256:
+        r128 = O.quantize_layer(W, s, 128)
+        assert np.all(r["D"] >= np.maximum(r128["D"][:, 0::2], r128["D"][:, 1::2]))
+        V = W.copy()
+        V[:, 128:256] = V[:, 0:128][:, ::-1]       # second half: same values, same range
+        ra, rb = O.quantize_layer(V, None, 256), O.quantize_layer(V, None, 128)
+        assert np.array_equal(ra["D"][:, 0], rb["D"][:, 0]) and np.array_equal(rb["D"][:, 0], rb["D"][:, 1])
+
+
+def _loss_by_loops_q(W, X, s, group, bits, symmetric):
+    """Like the loop loss above, for any group size and grid."""
+    N, K = W.shape
+    r = O.quantize_layer(W, s, group, bits, symmetric)
+    q, D, z = r["q"], r["D"], r["z"]
+    tot = 0.0
+    for t in range(X.shape[0]):
+        xs = [float(X[t, k]) / float(s[k]) for k in range(K)]
+        for n in range(N):
+            y = math.fsum(float(W[n, k]) * float(X[t, k]) for k in range(K))
+            yq = math.fsum(float(D[n, k // group]) * (int(q[n, k]) - int(z[n, k // group])) * xs[k]
+                           for k in range(K))
+            tot += (y - yq) ** 2
+    return tot / (X.shape[0] * N)
+
+
+@pytest.mark.parametrize("group,bits,symmetric", [(64, 4, False), (256, 3, False), (128, 4, True),
+                                                  (64, 8, False), (128, 2, True)])
+def test_search_loss_variants_against_loops(group, bits, symmetric):
+    g = _rng(90 + group + bits)
+    N, K, T = 3, 256, 5
+    W = _fp16_values(g.standard_normal((N, K)) * 0.02)
+    X = _fp16_values(g.standard_normal((T, K)) * np.where(np.arange(K) % 50 == 3, 20, 1))
+    S = O.candidate_scales(O.act_mean_abs(X), np.arange(20) / 19.0)
+    L = O.search_losses(W, X, S, group, bits=bits, symmetric=symmetric)
+    for i in (0, 9, 19):
+        ref = _loss_by_loops_q(W, X, S[i], group, bits, symmetric)
+        assert abs(L[i] - ref) <= 1e-9 * ref
+    # more bits never give a coarser grid: the plain (s = 1) loss falls with N
+    if not symmetric and bits < 8:
+        L8 = O.search_losses(W, X, S[:1], group, bits=8)
+        assert L8[0] < L[0]
+    Lm = O.search_losses_operand_model(W, X, S, True, group, bits=bits, symmetric=symmetric)
+    assert np.all(np.abs(Lm - L) <= 2e-3 * L)
