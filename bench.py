@@ -33,6 +33,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 N_ROT = 32          # decode GEMVs per step (distinct resident weight copies)
+# quantizer variants reported beside the timed path: (group, bits, symmetric)
+VARIANTS = ((64, 4, False), (128, 4, False), (256, 4, False), (128, 3, False), (128, 8, False),
+            (128, 4, True), (128, 3, True))
 METRIC = "W4A16 GEMV effective HBM GB/s (M=1) + prefill GEMM TFLOP/s; % of roofline"
 
 
@@ -234,6 +237,19 @@ def main() -> int:
     gram_flop = 2.0 * Tp * KA * KA + 20 * 2.0 * NA * 256 * 256 * gblk * (gblk + 1)
     search_gram = KA <= 16384 and gram_flop < 0.5 * direct_flop
     search_flop = gram_flop if search_gram else direct_flop
+    loss_h = [float(v) for v in loss.cpu()]
+    best_h = int(best.cpu()[0])
+    alphas_h = alphas.cpu().numpy()
+    # Output MSE of plain round-to-nearest (alpha = 0, s = 1) and of the
+    # searched scale for the quantizer variants, on the same layer and
+    # calibration tokens: one untimed search each, after the timed steps.
+    variants = []
+    for g, bits, sym in VARIANTS:
+        _, _, Lv, bv = awq.awq_search_scales(WA, XA, m, alphas, g, ws=ws_search, bits=bits, symmetric=sym)
+        Lv, iv = [float(v) for v in Lv.cpu()], int(bv.cpu()[0])
+        variants.append({"group": g, "bits": bits, "grid": "symmetric" if sym else "asymmetric",
+                         "loss_rtn": Lv[0], "loss_awq": Lv[iv], "alpha": float(alphas_h[iv]),
+                         "rtn_over_awq": Lv[0] / Lv[iv]})
     stats_bytes = wa.T * KA * 2
     quant_bytes = NA * KA * 2 + bytes_a
     stages = {
@@ -241,7 +257,11 @@ def main() -> int:
         "search": {"ms": avg["search"], "form": "gram" if search_gram else "direct",
                    "TFLOP/s": search_flop / (avg["search"] * 1e-3) / 1e12,
                    "frac_fp16_mfma": search_flop / (avg["search"] * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
-                   "direct_form_equivalent_TFLOP/s": direct_flop / (avg["search"] * 1e-3) / 1e12},
+                   "direct_form_equivalent_TFLOP/s": direct_flop / (avg["search"] * 1e-3) / 1e12,
+                   # output MSE over the calibration tokens: alpha = 0 is s = 1, plain
+                   # round-to-nearest; the chosen alpha is the searched scale
+                   "loss_rtn": loss_h[0], "loss_awq": loss_h[best_h], "alpha": float(alphas_h[best_h]),
+                   "rtn_over_awq": loss_h[0] / loss_h[best_h]},
         "quantize": {"ms": avg["quantize"], "GB/s": quant_bytes / (avg["quantize"] * 1e-3) / 1e9},
         "gemv_m1": {"us_per_launch": gemv1_us, "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS},
         "gemv_m8": {"us_per_launch": gemv8_us, "GB/s": gemv8_gbs, "frac_hbm": gemv8_gbs / HBM_PEAK_GBS},
@@ -276,6 +296,7 @@ def main() -> int:
                          "unit": "TFLOP/s", "frac": gemm_tflops / FP16_MFMA_PEAK_TFLOPS,
                          "flop_per_launch": gemm_flop, "kernel": "k_gemm"},
         "stages": stages,
+        "quantizer_variants": variants,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(WA, qs[0], scs[0], zs[0], xa1)

@@ -11,14 +11,18 @@
  *   awq_act_stats      per-input-channel mean |x_j| over calibration tokens
  *   awq_search_scales  s_j = (mean|x_j|)^alpha, alpha chosen on a grid by the
  *                      layer-output MSE of Q(W diag(s)) diag(s)^-1 x
- *   awq_quantize_pack  group-128 asymmetric 4-bit round-to-nearest of
+ *   awq_quantize_pack  group-wise asymmetric 4-bit round-to-nearest of
  *                      W diag(s): codes packed 8 per int32, one fp16 step and
- *                      one uint8 zero point per group
+ *                      one uint8 zero point per group (of 64, 128 or 256)
  *   awq_w4a16_gemm     y = x (dequant W)^T fused: unpack, apply the group step
  *                      and zero point, optionally the per-channel 1/s
- * and one helper that moves the per-channel 1/s out of the product:
+ * and two helpers:
  *   awq_fold_scales    divides the producer of x (a LayerNorm's gain and bias,
- *                      a preceding linear's rows) by s
+ *                      a preceding linear's rows) by s, which moves the
+ *                      per-channel 1/s out of the product
+ *   awq_quantize_codes the quantizer's variants (N bits, asymmetric or
+ *                      symmetric grid), one unpacked code per byte; the search
+ *                      scores the same variants
  * Linears that read the same input (q, k and v; gate and up) are searched
  * together by passing their row-concatenated W to awq_search_scales: they then
  * share s, and one fold serves them all.
@@ -27,8 +31,8 @@
  * --------------------------------
  *  Shapes.  W is [N][K] row-major (N = output channels C_out, K = input
  *    channels C_in); activations are [rows][ldx] row-major with K used
- *    columns.  The group size is 128 input channels and K must be a multiple
- *    of it.
+ *    columns.  A quantization group is 64, 128 (the usual choice) or 256
+ *    consecutive input channels of one row, and K must be a multiple of it.
  *  Memory.  Every array argument is a DEVICE pointer on the current HIP device,
  *    allocated and owned by the caller; the library allocates nothing and keeps
  *    no state between calls.  Scratch memory is the caller's workspace `ws` of
@@ -45,8 +49,10 @@
  *  Determinism.  The same inputs give bit-identical outputs on every run: no
  *    floating-point atomics, fixed reduction orders.
  *  Numerical domain.  Inputs are finite.  Calibration column sums satisfy
- *    sum_t |x_tj| < 2^29 (fixed-point range of the statistic).  The group range
- *    of W diag(s) divided by 15 is below 65504 (the step is stored in fp16).
+ *    sum_t |x_tj| < 2^29 (fixed-point range of the statistic).  The step of
+ *    every group of W diag(s) before rounding (its range over 2^N - 1, or
+ *    max|w| over 2^(N-1) for the symmetric grid) is below 65504 (the step is
+ *    stored in fp16).
  *    Outside this domain results are unspecified.
  */
 #ifndef AWQ_H
@@ -65,7 +71,7 @@ typedef enum awq_status {
   AWQ_ERR_SHAPE = 2,        /* K % group != 0, a size < 0 (or 0 where > 0 needed), ld < K */
   AWQ_ERR_DTYPE = 3,        /* element type not accepted by this call               */
   AWQ_ERR_ALIGN = 4,        /* pointer not 16-byte aligned or ld % 8 != 0            */
-  AWQ_ERR_UNSUPPORTED = 5,  /* group_size != 128, n_alpha outside [1, 64], K too big */
+  AWQ_ERR_UNSUPPORTED = 5,  /* group size, bits, n_alpha outside [1, 64], K too big */
   AWQ_ERR_WORKSPACE = 6,    /* ws NULL or smaller than awq_workspace_bytes(...)      */
   AWQ_ERR_HIP = 7           /* a HIP launch failed                                   */
 } awq_status;
@@ -83,7 +89,7 @@ typedef enum awq_op {
   AWQ_OP_GEMM = 3
 } awq_op;
 
-#define AWQ_GROUP 128
+#define AWQ_GROUP 128           /* the usual group size; 64 and 256 are accepted too */
 #define AWQ_MAX_ALPHA 64
 #define AWQ_MAX_K 131072
 /* Largest calibration row stride (elements) of awq_search_scales: 256 rows of
@@ -97,8 +103,8 @@ int awq_abi_version(void);
 /* Human-readable name of a status value (static storage). */
 const char* awq_status_str(awq_status st);
 
-/* Workspace bytes a call needs for the given sizes (0 if it needs none).
- * Arguments that an op does not use are ignored. */
+/* Workspace bytes a call needs for the given sizes (0 if it needs none), for
+ * every group size.  Arguments that an op does not use are ignored. */
 size_t awq_workspace_bytes(awq_op op, int64_t M, int64_t N, int64_t K, int64_t T, int n_alpha);
 
 /*
@@ -128,7 +134,9 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
  * required": s_j = (s_X,j)^alpha with s_X,j = mean |x_j|, alpha on a small grid
  * in [0, 1], and the alpha that minimises the mean squared error between the
  * layer output W x and Q(W diag(s)) diag(s)^-1 x over the calibration tokens
- * wins.  Q is the quantizer of awq_quantize_pack (fp16 step as stored).
+ * wins.  Q is the quantizer of awq_quantize_pack (fp16 step as stored) or,
+ * for other bit widths and the symmetric grid, of awq_quantize_codes; with
+ * alpha = 0 (s = 1) the loss is that of plain round-to-nearest.
  *
  *   candidate i: s_ij = float( pow( max(double(mean_abs[j]), 2^-14), alphas[i] ) )
  *   loss_i      = (1 / (T N)) sum_t sum_n ( ((W - W_hat_i) x_t)_n )^2
@@ -139,7 +147,9 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
  *   mean_abs    [K] float (output of awq_act_stats)
  *   alphas      [n_alpha] double, device memory
  *   n_alpha     1..AWQ_MAX_ALPHA
- *   group_size  must be 128
+ *   group_size  64, 128 or 256; K a multiple of it and of 128
+ *   bits, symmetric  the grid, as for awq_quantize_codes (4 and 0: the grid
+ *               of awq_quantize_pack)
  *   s_out       [K] float: s of the best candidate
  *   inv_s_out   [K] float: 1.0f / s (IEEE division); may be NULL
  *   loss_out    [n_alpha] double; may be NULL
@@ -163,16 +173,18 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
 awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
                              const void* x_calib, int64_t T, int64_t ldx,
                              const float* mean_abs, const double* alphas, int n_alpha,
-                             int group_size, float* s_out, float* inv_s_out, double* loss_out,
-                             int32_t* best_idx_out, void* ws, size_t ws_bytes, void* stream);
+                             int group_size, int bits, int symmetric, float* s_out,
+                             float* inv_s_out, double* loss_out, int32_t* best_idx_out, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /*
  * Group-wise asymmetric 4-bit round-to-nearest of W' = W diag(s).
  * "AWQ Math", sections "Weight-only quantization and where it breaks"
  * (Q(w) = step * round(w / step)) and "Shapes, granularity, and complexity"
- * (groups of 128 input channels, each with its own step and zero point);
- * "AWQ > Benefits and Practical Considerations" (one scale and one zero point
- * per 128 weights).  Per group of 128 consecutive k of one row n:
+ * (groups of commonly 128 input channels, each with its own step and zero
+ * point); "AWQ > Benefits and Practical Considerations" (one scale and one
+ * zero point per 128 weights).  Per group of g = group_size (64, 128 or 256)
+ * consecutive k of one row n:
  *   w'  = float(w) * s_k                      (s == NULL: s = 1, plain RTN)
  *   lo  = min(0, min w'),  hi = max(0, max w')
  *   d   = (hi - lo) / 15                      (float, IEEE division)
@@ -183,9 +195,9 @@ awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
  *   w         [N][K] fp16 or bf16 (dt), contiguous
  *   s         [K] float or NULL
  *   qweight   [N][K/8] int32: code of k = 8c + j in bits [4j, 4j+4) of word c
- *   scales    [N][K/128] fp16 bit patterns (step)
- *   zeros     [N][K/128] uint8 (z)
- *   scales_f32_dbg [N][K/128] float (d, before rounding); may be NULL
+ *   scales    [N][K/g] fp16 bit patterns (step)
+ *   zeros     [N][K/g] uint8 (z)
+ *   scales_f32_dbg [N][K/g] float (d, before rounding); may be NULL
  * N == 0 is a no-op.
  */
 awq_status awq_quantize_pack(const void* w, awq_dtype dt, int64_t N, int64_t K, const float* s,
@@ -193,13 +205,44 @@ awq_status awq_quantize_pack(const void* w, awq_dtype dt, int64_t N, int64_t K, 
                              float* scales_f32_dbg, void* stream);
 
 /*
+ * The quantizer's variants, one code per byte: N = bits, asymmetric or
+ * symmetric grid, groups of g = group_size.  "AWQ Math", section
+ * "Weight-only quantization and where it breaks" (N-bit weights; the
+ * symmetric step max|w| / 2^(N-1), Q(w) = step * round(w / step)) and
+ * "Shapes, granularity, and complexity" (groups, each with its own step and
+ * zero point); "CPU-SLM implications and common pitfalls" (larger groups
+ * widen the step).  Per group, with w' = float(w) * s_k (s == NULL: s = 1):
+ *   asymmetric (symmetric == 0), bits 2..8:
+ *     d = (max(0, max w') - min(0, min w')) / (2^N - 1)        (IEEE division)
+ *     z = clamp(rint(-min(0, min w') / D), 0, 2^N - 1),  C = 2^N - 1
+ *   symmetric (symmetric == 1), bits 2..7:
+ *     d = max|w'| / 2^(N-1)                                     (exact)
+ *     z = 2^(N-1),  C = 2^N: codes -2^(N-1) .. 2^(N-1) are stored shifted up by
+ *     z, 2^N + 1 levels as the formula gives (so not packable into N bits)
+ *   both: step = smallest fp16 >= max(d, 2^-24), D = float(step),
+ *     q_k = clamp(rint(w'_k / D) + z, 0, C); the grid value is D (q_k - z).
+ * bits 4 and symmetric 0 give the codes awq_quantize_pack packs (same g).
+ *
+ *   w        [N][K] fp16 or bf16 (dt), contiguous
+ *   s        [K] float or NULL
+ *   codes    [N][K] uint8, 16-byte aligned
+ *   scales   [N][K/g] fp16 bit patterns (step)
+ *   zeros    [N][K/g] uint8 (z)
+ * N == 0 is a no-op.
+ */
+awq_status awq_quantize_codes(const void* w, awq_dtype dt, int64_t N, int64_t K, const float* s,
+                              int group_size, int bits, int symmetric, uint8_t* codes,
+                              uint16_t* scales, uint8_t* zeros, void* stream);
+
+/*
  * Fused W4A16 product.  "AWQ > Benefits and Practical Considerations": the
  * dequantization unpacks 4-bit integers, applies the group scale and zero
  * point and optionally the per-channel inverse scale (when it is not folded
  * into the preceding layer), fused with the matrix multiply so that the fp16
  * weight matrix is never materialised.
- *   y[m][n] = sum_k step[n][k/128] * (q[n][k] - z[n][k/128]) * x[m][k] * r[k]
- * with r = inv_s (or 1 when inv_s == NULL).
+ *   y[m][n] = sum_k step[n][k/g] * (q[n][k] - z[n][k/g]) * x[m][k] * r[k]
+ * with r = inv_s (or 1 when inv_s == NULL) and g = group_size (64, 128 or
+ * 256, as quantized).
  *
  *   x        [M][ldx] fp16 or bf16 (xdt)
  *   qweight, scales, zeros  as written by awq_quantize_pack
@@ -208,9 +251,9 @@ awq_status awq_quantize_pack(const void* w, awq_dtype dt, int64_t N, int64_t K, 
  *   ws       >= awq_workspace_bytes(AWQ_OP_GEMM, M, N, K, 0, 0)
  * M == 1 runs the batch-1 GEMV (fp32 accumulation of exact int4 x fp16
  * products of x r); larger M runs matrix-core products on fp16 operands: x r
- * scaled by exact powers of two (per token and group for M <= 16, per token
- * above) and the dequantized weights step (q - z) rounded once to fp16.  M == 0
- * or N == 0 is a no-op.
+ * scaled by exact powers of two (per token and 128 channels for M <= 16 when
+ * K is a multiple of 128, per token otherwise) and the dequantized weights
+ * step (q - z) rounded once to fp16.  M == 0 or N == 0 is a no-op.
  */
 awq_status awq_w4a16_gemm(const void* x, awq_dtype xdt, int64_t M, int64_t K, int64_t ldx,
                           const int32_t* qweight, const uint16_t* scales, const uint8_t* zeros,

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_four_calls_and_helpers():
     names = declared_functions()
     for n in ("awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_w4a16_gemm",
-              "awq_fold_scales", "awq_workspace_bytes", "awq_status_str", "awq_abi_version"):
+              "awq_fold_scales", "awq_quantize_codes", "awq_workspace_bytes", "awq_status_str",
+              "awq_abi_version"):
         assert n in names
 
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.awq_abi_version() == 2
+    assert lib.awq_abi_version() == 3
     for code in range(8):
         assert lib.awq_status_str(code).decode()
     assert lib.awq_status_str(0).decode() == "ok"
@@ -87,15 +88,23 @@ def test_search_validation():
 
     def call(**kw):
         a = dict(w=A, dt=E.AWQ_F16, N=512, K=512, x=A2, T=64, ldx=512, m=A3, al=A3, na=20, g=128,
-                 s=A2, inv=NULL, loss=NULL, best=NULL, ws=A3, wsb=ws)
+                 bits=4, sym=0, s=A2, inv=NULL, loss=NULL, best=NULL, ws=A3, wsb=ws)
         a.update(kw)
         return f(a["w"], a["dt"], a["N"], a["K"], a["x"], a["T"], a["ldx"], a["m"], a["al"], a["na"],
-                 a["g"], a["s"], a["inv"], a["loss"], a["best"], a["ws"], a["wsb"], NULL)
+                 a["g"], a["bits"], a["sym"], a["s"], a["inv"], a["loss"], a["best"], a["ws"], a["wsb"],
+                 NULL)
 
     assert call(w=NULL) == 1
     assert call(s=NULL) == 1
     assert call(dt=E.AWQ_F32) == 3
-    assert call(g=64) == 5
+    assert call(g=32) == 5
+    assert call(g=512) == 5
+    assert call(bits=1) == 5
+    assert call(bits=9) == 5
+    assert call(bits=8, sym=1) == 5          # 2^8 + 1 symmetric levels do not fit a byte
+    assert call(sym=2) == 5
+    assert call(g=256, K=384, ldx=384) == 2  # K % group
+    assert call(g=64, K=576, ldx=576) == 2   # K % 128
     assert call(na=0) == 5
     assert call(na=65) == 5
     assert call(K=500, ldx=504) == 2
@@ -116,9 +125,35 @@ def test_quantize_validation():
     assert f(A, E.AWQ_F32, 4, 512, NULL, 128, A2, A3, A3, NULL, NULL) == 3
     assert f(A, E.AWQ_F16, 4, 500, NULL, 128, A2, A3, A3, NULL, NULL) == 2
     assert f(A, E.AWQ_F16, -1, 512, NULL, 128, A2, A3, A3, NULL, NULL) == 2
-    assert f(A, E.AWQ_F16, 4, 512, NULL, 256, A2, A3, A3, NULL, NULL) == 5
+    assert f(A, E.AWQ_F16, 4, 512, NULL, 96, A2, A3, A3, NULL, NULL) == 5
+    assert f(A, E.AWQ_F16, 4, 384, NULL, 256, A2, A3, A3, NULL, NULL) == 2
     assert f(BAD, E.AWQ_F16, 4, 512, NULL, 128, A2, A3, A3, NULL, NULL) == 4
     assert f(A, E.AWQ_F16, 4, 512, BAD, 128, A2, A3, A3, NULL, NULL) == 4
+
+
+def test_quantize_codes_validation():
+    lib = _lib()
+    f = lib.awq_quantize_codes
+
+    def call(**kw):
+        a = dict(w=A, dt=E.AWQ_F16, N=4, K=512, s=NULL, g=128, bits=3, sym=0, q=A2, sc=A3, z=A3)
+        a.update(kw)
+        return f(a["w"], a["dt"], a["N"], a["K"], a["s"], a["g"], a["bits"], a["sym"], a["q"], a["sc"],
+                 a["z"], NULL)
+
+    assert call(N=0, w=NULL, q=NULL) == 0        # no-op
+    assert call(w=NULL) == 1
+    assert call(z=NULL) == 1
+    assert call(dt=E.AWQ_F32) == 3
+    assert call(K=448) == 2
+    assert call(N=-1) == 2
+    assert call(g=96) == 5
+    assert call(bits=1) == 5
+    assert call(bits=8, sym=1) == 5
+    assert call(bits=9) == 5
+    assert call(q=ctypes.c_void_p(0x20008)) == 4  # codes 16-byte aligned
+    assert call(w=BAD) == 4
+    assert call(s=BAD) == 4
 
 
 def test_gemm_validation():
@@ -142,6 +177,7 @@ def test_gemm_validation():
     assert call(ldy=100) == 2
     assert call(M=-1) == 2
     assert call(g=32) == 5
+    assert call(g=256, K=4224, ldx=4224) == 2   # K % group
     assert call(x=BAD) == 4
     assert call(ldx=4100) == 4
     assert call(r=BAD) == 4

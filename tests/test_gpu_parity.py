@@ -223,35 +223,38 @@ def test_product_special_cases():
 SEARCH_MODEL_RTOL = 1e-5   # GPU loss vs the oracle scored in the same operand precision
 
 
-def _check_search(W, X, dtype, n_alpha=20):
+def _check_search(W, X, dtype, n_alpha=20, group=128, bits=4, sym=False):
     """Statistic bit-exact; chosen index, s and 1/s bit-exact against the
     oracle scored in the matrix-core operand precision (the decision is taken
     in the same precision on both sides); every loss within SEARCH_MODEL_RTOL
     of that oracle and within the rigorous rounding bound of the exact fp64
-    losses."""
+    losses.  group / bits / sym select the quantizer variant."""
     alphas = WL.alpha_grid(n_alpha)
     m = awq.awq_act_stats(gpu(X))
-    s, inv, L, best = awq.awq_search_scales(gpu(W), gpu(X), m, gpu(torch.from_numpy(alphas)))
+    s, inv, L, best = awq.awq_search_scales(gpu(W), gpu(X), m, gpu(torch.from_numpy(alphas)), group,
+                                            bits=bits, symmetric=sym)
     torch.cuda.synchronize()
     s, inv, L, best = s.cpu().numpy(), inv.cpu().numpy(), L.cpu().numpy(), int(best.cpu()[0])
     m_ref = O.act_mean_abs(f32(X))
     assert np.array_equal(m.cpu().numpy().view(np.uint32), m_ref.view(np.uint32))
     model = "fp16" if dtype == F16 else "fp16-scaled-x"
-    i_mod, s_mod, inv_mod, L_mod = O.search_scales(f32(W), f32(X), m_ref, alphas, operand_model=model)
+    i_mod, s_mod, inv_mod, L_mod = O.search_scales(f32(W), f32(X), m_ref, alphas, group,
+                                                   operand_model=model, bits=bits, symmetric=sym)
     S = O.candidate_scales(m_ref, alphas)
-    L_ex = O.search_losses(f32(W), f32(X), S)
+    L_ex = O.search_losses(f32(W), f32(X), S, group, bits=bits, symmetric=sym)
     W64, X64 = f32(W).astype(np.float64), f32(X).astype(np.float64)
     N, K = W64.shape
     for i in range(n_alpha):
         assert abs(L[i] - L_mod[i]) <= SEARCH_MODEL_RTOL * L_mod[i], (i, L[i], L_mod[i])
-        r = O.quantize_layer(f32(W), S[i])
-        grid = O.dequantize(r["q"].reshape(N, K // 128, 128), r["D"],
+        r = O.quantize_layer(f32(W), S[i], group, bits, sym)
+        grid = O.dequantize(r["q"].reshape(N, K // group, group), r["D"],
                             r["z"].astype(np.float32)).reshape(N, K)
         b, _ = loss_error_bound(W64, X64, O.unscale_activation(grid, S[i]), FP16_U)
         assert abs(L[i] - L_ex[i]) <= b + 1e-6 * L_ex[i], (i, L[i], L_ex[i], b)
     order = np.argsort(L_mod)
     gap = (L_mod[order[1]] - L_mod[order[0]]) / L_mod[order[0]]
-    print(f"search N={N} K={K}: best {i_mod} (exact-scoring best {O.choose_candidate(L_ex)}), "
+    print(f"search N={N} K={K} g={group} bits={bits} sym={sym}: best {i_mod} "
+          f"(exact-scoring best {O.choose_candidate(L_ex)}), "
           f"gap {gap:.2e}, max loss diff vs model {np.max(np.abs(L - L_mod) / L_mod):.2e}")
     if gap <= 2 * SEARCH_MODEL_RTOL:
         pytest.skip(f"ill-posed seed: best and runner-up {gap:.2e} apart (relative)")
@@ -400,3 +403,145 @@ def test_shared_input_search_and_fold_c3():
         assert rel_max_err(f32(y), O.w4a16_matmul(f32(xf[:M]), words, step, zeros, None)) <= GEMM_TOL
         assert rel_max_err(f32(y), ref[:M]) <= GEMM_TOL
 
+
+
+# ------------------------------------------------------------- quantizer variants
+def _variant_layer(N, K, dtype, seed, with_s):
+    W = WL.random_matrix((N, K), torch.float32, seed=seed, scale=0.02)
+    W[:, 3::101] *= 30.0                      # outliers inside some groups
+    W[0, :64] = 0.0                           # an all-zero group (every group size starts it)
+    W[1, :] = -0.4                            # a constant negative row
+    W = W.to(dtype)
+    s = None
+    if with_s:
+        g = np.random.Generator(np.random.PCG64(seed + 5))
+        s = torch.from_numpy(np.exp(g.uniform(-2.5, 2.5, K)).astype(np.float32))
+    return W, s
+
+
+@pytest.mark.parametrize("group", [64, 256])
+@pytest.mark.parametrize("N,K,dtype,with_s", [
+    (37, 4096, F16, True), (300, 11008 - 11008 % 256, BF16, True), (129, 1024, BF16, False),
+    (5, 256, F16, True), (64, 768, F16, False),
+])
+def test_quantize_pack_groups_bit_exact(group, N, K, dtype, with_s):
+    """awq_quantize_pack with groups of 64 and 256: packed words, steps, zero
+    points and the unrounded steps bit-exact."""
+    W, s = _variant_layer(N, K, dtype, N + K + group, with_s)
+    dbg = torch.empty((N, K // group), dtype=torch.float32, device="cuda")
+    q, sc, z = awq.awq_quantize_pack(gpu(W), None if s is None else gpu(s), group, scales_f32_dbg=dbg)
+    torch.cuda.synchronize()
+    r = O.quantize_layer(f32(W), None if s is None else s.numpy(), group)
+    assert sc.shape == (N, K // group)
+    assert np.array_equal(dbg.cpu().numpy().view(np.uint32), r["d"].view(np.uint32))
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), r["step"].view(np.uint16))
+    assert np.array_equal(z.cpu().numpy(), r["z"])
+    assert np.array_equal(q.cpu().numpy(), O.pack_codes(r["q"]))
+
+
+VARIANTS = [(128, 4, False), (64, 3, False), (256, 2, False), (128, 8, False), (64, 5, False),
+            (64, 4, True), (128, 7, True), (256, 2, True), (128, 3, True)]
+
+
+@pytest.mark.parametrize("group,bits,sym", VARIANTS)
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_quantize_codes_bit_exact(group, bits, sym, dtype):
+    """awq_quantize_codes: every grid of the family (N bits, asymmetric or
+    symmetric, groups of 64 / 128 / 256), codes, steps and zero points
+    bit-exact; for 4-bit asymmetric the codes are those awq_quantize_pack packs."""
+    N, K = 203, 1536
+    W, s = _variant_layer(N, K, dtype, 7 * bits + group + (1000 if sym else 0), True)
+    c, sc, z = awq.awq_quantize_codes(gpu(W), gpu(s), group, bits, sym)
+    torch.cuda.synchronize()
+    r = O.quantize_layer(f32(W), s.numpy(), group, bits, sym)
+    assert np.array_equal(c.cpu().numpy(), r["q"])
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), r["step"].view(np.uint16))
+    assert np.array_equal(z.cpu().numpy(), r["z"])
+    assert int(c.max()) <= O.code_max(bits, sym)
+    if bits == 4 and not sym:
+        q, _, _ = awq.awq_quantize_pack(gpu(W), gpu(s), group)
+        assert np.array_equal(q.cpu().numpy(), O.pack_codes(c.cpu().numpy()))
+
+
+@pytest.mark.parametrize("group,bits,sym", [(64, 4, False), (256, 4, False), (128, 3, False),
+                                            (64, 8, False), (128, 4, True), (256, 3, True)])
+@pytest.mark.parametrize("N,K,T,dtype", [(300, 1024, 200, F16), (130, 768, 3000, BF16)])
+def test_search_variants(group, bits, sym, N, K, T, dtype):
+    """The search scores the quantizer variant it is given: every loss, the
+    chosen index and s as for the 4-bit grid (the first shape takes the
+    direct form of the loss, the second the Gram form)."""
+    W = WL.random_matrix((N, K), torch.float32, seed=N + bits, scale=0.02).to(dtype)
+    X = _act(T, K, dtype, seed=T + group)
+    _check_search(W, X, dtype, group=group, bits=bits, sym=sym)
+
+
+def _random_packed_g(N, K, seed, group):
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = g.integers(0, 16, (N, K)).astype(np.uint8)
+    step = g.uniform(2e-4, 4e-3, (N, K // group)).astype(np.float16)
+    z = g.integers(0, 16, (N, K // group)).astype(np.uint8)
+    return O.pack_codes(q), step, z
+
+
+@pytest.mark.parametrize("group", [64, 256])
+@pytest.mark.parametrize("M,N,K,dtype,ydt,with_r", [
+    (1, 1000, 4096, F16, F16, True), (1, 11008, 4096, BF16, torch.float32, False),
+    (1, 257, 768, F16, torch.float32, True), (3, 700, 2048, F16, F16, True),
+    (8, 4096, 11008 - 11008 % 256, BF16, torch.float32, True), (16, 96, 1024, F16, torch.float32, False),
+    (40, 600, 2560, F16, F16, True), (300, 520, 1024, BF16, torch.float32, False),
+])
+def test_product_groups_parity(group, M, N, K, dtype, ydt, with_r):
+    """The fused product with groups of 64 and 256, on every path (batch-1
+    GEMV, skinny matrix-core product, tiled GEMM)."""
+    words, step, z = _random_packed_g(N, K, M * 1000 + N + K + group, group)
+    x = _act(M, K, dtype, M + K)
+    r = None
+    if with_r:
+        g = np.random.Generator(np.random.PCG64(K + group))
+        r = (np.float32(1) / np.exp(g.uniform(-1.5, 1.5, K)).astype(np.float32)).astype(np.float32)
+    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                           gpu(torch.from_numpy(z)), None if r is None else gpu(torch.from_numpy(r)),
+                           out_dtype=ydt, group_size=group)
+    torch.cuda.synchronize()
+    ref = O.w4a16_matmul(f32(x), words, step, z, r, group)
+    err = rel_max_err(f32(y), ref, ydt)
+    print(f"product g={group} M={M} N={N} K={K}: rel max err {err:.3e}")
+    assert err <= GEMM_TOL
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 40])
+def test_product_group64_odd_units(M):
+    """Groups of 64 with K = 64 * odd (not whole 128-channel units): batch 1
+    runs the GEMV, larger batches the tiled GEMM."""
+    N, K, group = 333, 64 * 23, 64
+    words, step, z = _random_packed_g(N, K, 77 + M, group)
+    x = _act(M, K, F16, 5 + M)
+    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                           gpu(torch.from_numpy(z)), out_dtype=torch.float32, group_size=group)
+    torch.cuda.synchronize()
+    ref = O.w4a16_matmul(f32(x), words, step, z, None, group)
+    assert rel_max_err(f32(y), ref) <= GEMM_TOL
+
+
+@pytest.mark.parametrize("group", [64, 256])
+def test_group_end_to_end(group):
+    """Statistics -> search -> quantize -> products with one group size: the
+    search's s, the packed layer and the product at M = 1 and 8 against the
+    oracle on the same inputs."""
+    w = WL.workload(1)
+    W, X = WL.weight(w), WL.calibration(w)
+    _check_search(W, X, F16, group=group)
+    m = awq.awq_act_stats(gpu(X))
+    al = gpu(torch.from_numpy(WL.alpha_grid(20)))
+    s, inv, _, _ = awq.awq_search_scales(gpu(W), gpu(X), m, al, group)
+    q, sc, z = awq.awq_quantize_pack(gpu(W), s, group)
+    torch.cuda.synchronize()
+    r = O.quantize_layer(f32(W), s.cpu().numpy(), group)
+    assert np.array_equal(q.cpu().numpy(), O.pack_codes(r["q"]))
+    xs = X[:8]
+    for M in (1, 8):
+        y = awq.awq_w4a16_gemm(gpu(xs[:M]), q, sc, z, inv, out_dtype=torch.float32, group_size=group)
+        torch.cuda.synchronize()
+        ref = O.w4a16_matmul(f32(xs[:M]), q.cpu().numpy(), sc.cpu().numpy(), z.cpu().numpy(),
+                             inv.cpu().numpy(), group)
+        assert rel_max_err(f32(y), ref) <= GEMM_TOL

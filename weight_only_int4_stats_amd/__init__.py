@@ -17,8 +17,8 @@ from . import _abi
 from ._abi import (AWQ_BF16, AWQ_F16, AWQ_F32, AWQ_GROUP, AWQ_OP_ACT_STATS, AWQ_OP_GEMM,  # noqa: F401
                    AWQ_OP_QUANTIZE, AWQ_OP_SEARCH, AwqError, lib)
 
-__all__ = ["awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_w4a16_gemm",
-           "awq_fold_scales", "awq_workspace_bytes", "AwqError", "lib"]
+__all__ = ["awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_quantize_codes",
+           "awq_w4a16_gemm", "awq_fold_scales", "awq_workspace_bytes", "AwqError", "lib"]
 
 _DT = {torch.float16: AWQ_F16, torch.bfloat16: AWQ_BF16, torch.float32: AWQ_F32}
 
@@ -74,8 +74,10 @@ def awq_search_scales(w: torch.Tensor, x_calib: torch.Tensor, mean_abs: torch.Te
                       alphas: torch.Tensor, group_size: int = AWQ_GROUP,
                       s_out: torch.Tensor | None = None, inv_s_out: torch.Tensor | None = None,
                       loss_out: torch.Tensor | None = None, best_idx_out: torch.Tensor | None = None,
-                      ws: torch.Tensor | None = None, stream=None):
-    """Returns (s [K] f32, inv_s [K] f32, losses [n] f64, best index int32 [1])."""
+                      ws: torch.Tensor | None = None, stream=None, *, bits: int = 4,
+                      symmetric: bool = False):
+    """Returns (s [K] f32, inv_s [K] f32, losses [n] f64, best index int32 [1]).
+    bits / symmetric select the quantizer's grid (4 / False: awq_quantize_pack's)."""
     for t, n in ((w, "w"), (x_calib, "x_calib"), (mean_abs, "mean_abs"), (alphas, "alphas")):
         _dev(t, n)
     if not w.is_contiguous() or w.dim() != 2:
@@ -94,9 +96,9 @@ def awq_search_scales(w: torch.Tensor, x_calib: torch.Tensor, mean_abs: torch.Te
     best_idx_out = torch.empty(1, dtype=torch.int32, device=dev) if best_idx_out is None else best_idx_out
     ws, wsb = _workspace(awq_workspace_bytes(AWQ_OP_SEARCH, 0, N, K, T, n_alpha), dev, ws)
     st = lib().awq_search_scales(_ptr(w), _DT.get(w.dtype, -1), N, K, _ptr(x_calib), T, ldx,
-                                 _ptr(mean_abs), _ptr(alphas), n_alpha, group_size, _ptr(s_out),
-                                 _ptr(inv_s_out), _ptr(loss_out), _ptr(best_idx_out), _ptr(ws), wsb,
-                                 _stream(dev, stream))
+                                 _ptr(mean_abs), _ptr(alphas), n_alpha, group_size, bits,
+                                 int(bool(symmetric)), _ptr(s_out), _ptr(inv_s_out), _ptr(loss_out),
+                                 _ptr(best_idx_out), _ptr(ws), wsb, _stream(dev, stream))
     _abi.check("awq_search_scales", st)
     return s_out, inv_s_out, loss_out, best_idx_out
 
@@ -105,7 +107,7 @@ def awq_quantize_pack(w: torch.Tensor, s: torch.Tensor | None = None, group_size
                       qweight: torch.Tensor | None = None, scales: torch.Tensor | None = None,
                       zeros: torch.Tensor | None = None, scales_f32_dbg: torch.Tensor | None = None,
                       stream=None):
-    """Returns (qweight int32 [N, K/8], scales fp16 [N, K/128], zeros uint8 [N, K/128])."""
+    """Returns (qweight int32 [N, K/8], scales fp16 [N, K/g], zeros uint8 [N, K/g])."""
     _dev(w, "w")
     if not w.is_contiguous() or w.dim() != 2:
         raise ValueError("w must be a contiguous [N, K] tensor")
@@ -120,6 +122,27 @@ def awq_quantize_pack(w: torch.Tensor, s: torch.Tensor | None = None, group_size
                                  _stream(dev, stream))
     _abi.check("awq_quantize_pack", st)
     return qweight, scales, zeros
+
+
+def awq_quantize_codes(w: torch.Tensor, s: torch.Tensor | None = None, group_size: int = AWQ_GROUP,
+                       bits: int = 4, symmetric: bool = False, codes: torch.Tensor | None = None,
+                       scales: torch.Tensor | None = None, zeros: torch.Tensor | None = None,
+                       stream=None):
+    """Returns (codes uint8 [N, K], scales fp16 [N, K/g], zeros uint8 [N, K/g])."""
+    _dev(w, "w")
+    if not w.is_contiguous() or w.dim() != 2:
+        raise ValueError("w must be a contiguous [N, K] tensor")
+    N, K = w.shape
+    dev = w.device
+    G = K // group_size if group_size > 0 else 0
+    codes = torch.empty((N, K), dtype=torch.uint8, device=dev) if codes is None else codes
+    scales = torch.empty((N, G), dtype=torch.float16, device=dev) if scales is None else scales
+    zeros = torch.empty((N, G), dtype=torch.uint8, device=dev) if zeros is None else zeros
+    st = lib().awq_quantize_codes(_ptr(w), _DT.get(w.dtype, -1), N, K, _ptr(s), group_size, bits,
+                                  int(bool(symmetric)), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                  _stream(dev, stream))
+    _abi.check("awq_quantize_codes", st)
+    return codes, scales, zeros
 
 
 def awq_w4a16_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,

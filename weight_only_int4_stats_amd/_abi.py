@@ -27,9 +27,10 @@ SIGNATURES = {
     "awq_status_str": (ctypes.c_char_p, [_i]),
     "awq_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i64, _i]),
     "awq_act_stats": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _sz, _p]),
-    "awq_search_scales": (_i, [_p, _i, _i64, _i64, _p, _i64, _i64, _p, _p, _i, _i, _p, _p, _p,
-                               _p, _p, _sz, _p]),
+    "awq_search_scales": (_i, [_p, _i, _i64, _i64, _p, _i64, _i64, _p, _p, _i, _i, _i, _i, _p, _p,
+                               _p, _p, _p, _sz, _p]),
     "awq_quantize_pack": (_i, [_p, _i, _i64, _i64, _p, _i, _p, _p, _p, _p, _p]),
+    "awq_quantize_codes": (_i, [_p, _i, _i64, _i64, _p, _i, _i, _i, _p, _p, _p, _p]),
     "awq_w4a16_gemm": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _i64, _i, _p, _p, _i, _i64, _p,
                             _sz, _p]),
     "awq_fold_scales": (_i, [_p, _i, _i64, _i64, _i64, _p, _i, _p]),

@@ -6,7 +6,6 @@
 
 namespace awqk {
 
-constexpr int kGroup = 128;           // input channels per quantization group
 constexpr int kWave = 64;             // CDNA wavefront width
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -72,28 +71,54 @@ __device__ __forceinline__ uint32_t f16_round_up_bits(float d) {
   return b;
 }
 
+// One quantizer grid.  Asymmetric N bits: 2^N levels, the step is the
+// group's range (holding 0) over 2^N - 1 and the zero point an integer code.
+// Symmetric N bits: the step is max|w| / 2^(N-1) and the codes run over
+// -2^(N-1) .. 2^(N-1) (2^N + 1 levels), stored shifted up by 2^(N-1).
+struct QSpec {
+  float div;     // asymmetric: 2^N - 1; symmetric: 2^(N-1)
+  float cmax;    // largest stored code: 2^N - 1, or 2^N
+  bool sym;
+};
+constexpr QSpec kQ4 = {15.0f, 15.0f, false};     // the 4-bit asymmetric grid
+__host__ __device__ constexpr QSpec qspec(int bits, bool sym) {
+  return sym ? QSpec{(float)(1 << (bits - 1)), (float)(1 << bits), true}
+             : QSpec{(float)((1 << bits) - 1), (float)((1 << bits) - 1), false};
+}
+
 // Integer zero point and step of one group, shared by the quantizer and the
 // search's error generator so both score and store the same grid.
 struct GroupGrid {
   float D;          // step as float (fp16 value)
-  float z;          // zero point 0..15 as float
+  float z;          // zero point as float
   float d;          // step before rounding
+  float cmax;       // largest stored code
   uint32_t step_bits;
 };
 
-__device__ __forceinline__ GroupGrid group_grid(float mn, float mx) {
+// SYM must equal q.sym: the grid is chosen at compile time so that each thread
+// computes only its own step.
+template <bool SYM = false>
+__device__ __forceinline__ GroupGrid group_grid(float mn, float mx, const QSpec q = kQ4) {
   GroupGrid g;
-  const float lo = fminf(mn, 0.0f);
-  const float hi = fmaxf(mx, 0.0f);
-  g.d = (hi - lo) / 15.0f;                            // IEEE division
+  float lo = 0.0f;
+  if constexpr (SYM) {
+    g.d = fmaxf(-mn, mx) / q.div;                     // max|w| / 2^(N-1): exact
+  } else {
+    lo = fminf(mn, 0.0f);
+    const float hi = fmaxf(mx, 0.0f);
+    g.d = (hi - lo) / q.div;                          // IEEE division
+  }
   g.step_bits = f16_round_up_bits(fmaxf(g.d, 0x1p-24f));
   g.D = f16_to_f32(g.step_bits);
-  g.z = fminf(fmaxf(rintf(-lo / g.D), 0.0f), 15.0f);
+  if constexpr (SYM) g.z = q.div;
+  else g.z = fminf(fmaxf(rintf(-lo / g.D), 0.0f), q.cmax);
+  g.cmax = q.cmax;
   return g;
 }
 
 __device__ __forceinline__ float quant_code(float wp, const GroupGrid& g) {
-  return fminf(fmaxf(rintf(wp / g.D) + g.z, 0.0f), 15.0f);
+  return fminf(fmaxf(rintf(wp / g.D) + g.z, 0.0f), g.cmax);
 }
 
 // Raw buffer access: the fourth descriptor word for untyped 32-bit data, an
@@ -103,12 +128,15 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr uint32_t kBufferOob = 0x80000000u;
 constexpr int kBufferNt = 2;
 
-// Min / max across the 16 lanes of an aligned 16-lane segment.
-__device__ __forceinline__ void seg16_minmax(float& mn, float& mx) {
+// Min / max across the GL lanes of an aligned GL-lane segment (one group:
+// GL threads of 8 weights each).
+template <int GL>
+__device__ __forceinline__ void seg_minmax(float& mn, float& mx) {
+  static_assert(GL == 8 || GL == 16 || GL == 32, "group of 64, 128 or 256");
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, off, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+  for (int off = GL / 2; off >= 1; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, GL));
+    mx = fmaxf(mx, __shfl_xor(mx, off, GL));
   }
 }
 

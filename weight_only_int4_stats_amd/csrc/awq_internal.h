@@ -8,22 +8,33 @@
 
 namespace awq {
 
+// Quantizer variant: input channels per group (64, 128, 256), bits per code,
+// and the grid (asymmetric with a zero point, or symmetric max|w| / 2^(N-1)).
+struct QuantVariant {
+  int group = 128;
+  int bits = 4;
+  bool sym = false;
+};
+
 // ---- calibration statistic (mean |x|) -------------------------------------
 size_t act_stats_ws_bytes(int64_t K);
 hipError_t launch_act_stats(const void* x, int dt, int64_t T, int64_t K, int64_t ldx,
                             float* mean_abs, void* ws, hipStream_t st);
 
 // ---- quantize + pack --------------------------------------------------------
-hipError_t launch_quantize_pack(const void* w, int dt, int64_t N, int64_t K, const float* s,
+hipError_t launch_quantize_pack(const void* w, int dt, int64_t N, int64_t K, const float* s, int group,
                                 uint32_t* qw, uint16_t* scales, uint8_t* zeros, float* dbg,
                                 hipStream_t st);
+hipError_t launch_quantize_codes(const void* w, int dt, int64_t N, int64_t K, const float* s,
+                                 QuantVariant qv, uint8_t* codes, uint16_t* scales, uint8_t* zeros,
+                                 hipStream_t st);
 
 // ---- scale search -----------------------------------------------------------
 size_t search_ws_bytes(int dt, int64_t N, int64_t K, int64_t T, int n_alpha);
 hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void* x, int64_t T,
                          int64_t ldx, const float* mean_abs, const double* alphas, int n_alpha,
-                         float* s_out, float* inv_s_out, double* loss_out, int32_t* best_out,
-                         void* ws, hipStream_t st);
+                         QuantVariant qv, float* s_out, float* inv_s_out, double* loss_out,
+                         int32_t* best_out, void* ws, hipStream_t st);
 
 // Gram form of the search loss (k_gram.hip): Xt [K][Tp] 16-bit, fp32 partial
 // tiles of G (gram_partial_floats), G [K][K] fp64, P [K][2 Kp] fp16 (Kp = K
@@ -44,15 +55,16 @@ hipError_t launch_fold_scales(void* v, int dt, int64_t rows, int64_t cols, int64
                               int axis, hipStream_t st);
 
 // ---- W4A16 product ----------------------------------------------------------
+// group: input channels per step / zero point (64, 128 or 256)
 bool gemv1_supported(int64_t K, int64_t N);   // batch-1 GEMV kernels cover this shape
 hipError_t launch_gemv1(const void* x, int xdt, int64_t K, const uint32_t* qw,
-                        const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
-                        void* y, int ydt, hipStream_t st);
-size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
+                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int group,
+                        const float* r, void* y, int ydt, hipStream_t st);
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int group);
 hipError_t launch_w4a16(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx,
                         const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros,
-                        int64_t N, const float* inv_s, void* y, int ydt, int64_t ldy, void* ws,
-                        hipStream_t st);
+                        int64_t N, int group, const float* inv_s, void* y, int ydt, int64_t ldy,
+                        void* ws, hipStream_t st);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

@@ -138,7 +138,7 @@ template <int DT, int YDT, bool HAS_R, int UL, int NS>
 __global__ __launch_bounds__(1024) void k_gemv1_rows(
     const uint16_t* __restrict__ x, int64_t K, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N,
-    const float* __restrict__ r, void* __restrict__ y, int nks) {
+    const float* __restrict__ r, void* __restrict__ y, int nks, int gsh) {
   extern __shared__ uint32_t lds1[];
   const int nwv = blockDim.x >> 6;
   const int nrg = nwv / nks;
@@ -150,8 +150,8 @@ __global__ __launch_bounds__(1024) void k_gemv1_rows(
   const int64_t ch = (int64_t)ks * 64 + lane;
   const bool valid = ch < CH;
   const int64_t chc = valid ? ch : 0;
-  const int64_t G = K / kGroup;
-  const int64_t gc = chc >> 2;
+  const int64_t G = K >> (gsh + 5);                              // groups per row
+  const int64_t gc = chc >> gsh;                                 // this lane's group
   const int64_t rowsb = (int64_t)nrg * UL;
   const int64_t row0 = (int64_t)blockIdx.x * rowsb + (int64_t)rg * UL;
   uint32_t* xpair = lds1;                                        // [CH][16] fp16 pairs
@@ -251,7 +251,7 @@ template <int DT, int YDT, bool HAS_R, int NS, int D, int C>
 __global__ __launch_bounds__(1024) void k_gemv1_cu(
     const uint16_t* __restrict__ x, int64_t K, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N,
-    const float* __restrict__ r, void* __restrict__ y, int nks, int nrg, int rows_max) {
+    const float* __restrict__ r, void* __restrict__ y, int nks, int nrg, int rows_max, int gsh) {
   static_assert(D >= 1 && D <= 4, "rows in flight");
   extern __shared__ uint32_t lds1[];
   const int lane = threadIdx.x & 63;
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(1024) void k_gemv1_cu(
 
   // Buffer resources over this block's rows: an offset past the end reads 0
   // without touching memory, which masks missing rows and chunks.
-  const uint32_t KW = (uint32_t)(K >> 3), G32 = (uint32_t)(K >> 7);
+  const uint32_t KW = (uint32_t)(K >> 3), G32 = (uint32_t)(K >> (gsh + 5));
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(qw + r0 * KW), (short)0, nrows * (int)KW * 4, kBufferWord3);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(1024) void k_gemv1_cu(
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const bool ok = rowok && okc[c];
-      const uint32_t g = (uint32_t)(chc[c] >> 2);
+      const uint32_t g = (uint32_t)(chc[c] >> gsh);
       wb[slot][c] = __builtin_amdgcn_raw_buffer_load_b128(
           wrs, ok ? (rl * KW + (uint32_t)chc[c] * 4) * 4 : kBufferOob, 0, kBufferNt);
       sb[slot][c] = __builtin_amdgcn_raw_buffer_load_b16(srs, ok ? (rl * G32 + g) * 2 : kBufferOob, 0, 0);
@@ -386,7 +386,7 @@ constexpr size_t kCuLdsReserve = 81 * 1024;
 
 template <int DT, int YDT, bool HAS_R, int NS, int D, int C>
 hipError_t gemv1_cu_launch(const uint16_t* x, int64_t K, const uint32_t* qw, const uint16_t* scales,
-                         const uint8_t* zeros, int64_t N, const float* r, void* y, int nblk,
+                         const uint8_t* zeros, int64_t N, int gsh, const float* r, void* y, int nblk,
                          int nrg_max, hipStream_t st) {
   const int64_t CH = K >> 5;
   const int nks = (int)((CH + 64 * C - 1) / (64 * C));
@@ -402,7 +402,7 @@ hipError_t gemv1_cu_launch(const uint16_t* x, int64_t K, const uint32_t* qw, con
   // so the grid of one block per unit spreads over all of them.
   if (lds < kCuLdsReserve) lds = kCuLdsReserve;
   hipLaunchKernelGGL((k_gemv1_cu<DT, YDT, HAS_R, NS, D, C>), dim3((unsigned)nblk), dim3((unsigned)threads),
-                     lds, st, x, K, qw, scales, zeros, N, r, y, nks, nrg, rows_max);
+                     lds, st, x, K, qw, scales, zeros, N, r, y, nks, nrg, rows_max, gsh);
   return hipGetLastError();
 }
 
@@ -410,7 +410,7 @@ hipError_t gemv1_cu_launch(const uint16_t* x, int64_t K, const uint32_t* qw, con
 // (NS chunks of 8 per thread must cover K / 8, rounded up to whole quads).
 template <int DT, int YDT, bool HAS_R, int UL, int NS>
 hipError_t gemv1_rows_launch(const uint16_t* x, int64_t K, const uint32_t* qw, const uint16_t* scales,
-                        const uint8_t* zeros, int64_t N, const float* r, void* y, int nrg,
+                        const uint8_t* zeros, int64_t N, int gsh, const float* r, void* y, int nrg,
                         hipStream_t st) {
   const int64_t CH = K >> 5;
   const int nks = (int)((CH + 63) / 64);
@@ -419,7 +419,7 @@ hipError_t gemv1_rows_launch(const uint16_t* x, int64_t K, const uint32_t* qw, c
   if (threads > 1024 || ((K >> 3) + 3) / 4 * 4 > NS * threads) return hipErrorInvalidValue;
   const size_t lds = (size_t)CH * 16 * 4 + (size_t)CH * 4 * 4 + (size_t)nks * rows * 4;
   hipLaunchKernelGGL((k_gemv1_rows<DT, YDT, HAS_R, UL, NS>), dim3((unsigned)((N + rows - 1) / rows)),
-                     dim3((unsigned)threads), lds, st, x, K, qw, scales, zeros, N, r, y, nks);
+                     dim3((unsigned)threads), lds, st, x, K, qw, scales, zeros, N, r, y, nks, gsh);
   return hipGetLastError();
 }
 
@@ -441,9 +441,11 @@ inline int gemv1_path(int64_t K, int64_t N) {
   return cu_ok ? 2 : 0;
 }
 
+// gsh: log2 of the 32-code chunks per group (1, 2, 3 for groups of 64, 128, 256)
 template <int DT, int YDT, bool HAS_R>
 hipError_t gemv1_dispatch(const uint16_t* x, int64_t K, const uint32_t* qw, const uint16_t* scales,
-                          const uint8_t* zeros, int64_t N, const float* r, void* y, hipStream_t st) {
+                          const uint8_t* zeros, int64_t N, int gsh, const float* r, void* y,
+                          hipStream_t st) {
   const int path = gemv1_path(K, N);
   const int64_t need = ((K >> 3) + 3) / 4 * 4;     // staged 8-element pieces, whole quads
   if (path == 2) {
@@ -451,10 +453,10 @@ hipError_t gemv1_dispatch(const uint16_t* x, int64_t K, const uint32_t* qw, cons
     const int64_t nks = ((K >> 5) + 127) / 128;
     const int64_t threads = nks * (16 / nks) * 64;
     if (need <= threads)
-      return gemv1_cu_launch<DT, YDT, HAS_R, 1, 1, 2>(x, K, qw, scales, zeros, N, r, y, nblk, 16, st);
+      return gemv1_cu_launch<DT, YDT, HAS_R, 1, 1, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nblk, 16, st);
     if (need <= 2 * threads)
-      return gemv1_cu_launch<DT, YDT, HAS_R, 2, 1, 2>(x, K, qw, scales, zeros, N, r, y, nblk, 16, st);
-    return gemv1_cu_launch<DT, YDT, HAS_R, 4, 1, 2>(x, K, qw, scales, zeros, N, r, y, nblk, 16, st);
+      return gemv1_cu_launch<DT, YDT, HAS_R, 2, 1, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nblk, 16, st);
+    return gemv1_cu_launch<DT, YDT, HAS_R, 4, 1, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nblk, 16, st);
   }
   if (path == 0) return hipErrorInvalidValue;
   const int64_t CH = K >> 5;
@@ -462,9 +464,9 @@ hipError_t gemv1_dispatch(const uint16_t* x, int64_t K, const uint32_t* qw, cons
   int nrg = nks >= 8 ? 1 : 8 / nks;
   if (nks * nrg > 16) nrg = 16 / nks;
   const int64_t threads = (int64_t)nks * nrg * 64;
-  if (need <= threads) return gemv1_rows_launch<DT, YDT, HAS_R, 4, 1>(x, K, qw, scales, zeros, N, r, y, nrg, st);
-  if (need <= 2 * threads) return gemv1_rows_launch<DT, YDT, HAS_R, 4, 2>(x, K, qw, scales, zeros, N, r, y, nrg, st);
-  return gemv1_rows_launch<DT, YDT, HAS_R, 4, kG1MaxStage>(x, K, qw, scales, zeros, N, r, y, nrg, st);
+  if (need <= threads) return gemv1_rows_launch<DT, YDT, HAS_R, 4, 1>(x, K, qw, scales, zeros, N, gsh, r, y, nrg, st);
+  if (need <= 2 * threads) return gemv1_rows_launch<DT, YDT, HAS_R, 4, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nrg, st);
+  return gemv1_rows_launch<DT, YDT, HAS_R, 4, kG1MaxStage>(x, K, qw, scales, zeros, N, gsh, r, y, nrg, st);
 }
 
 }  // namespace awqk
@@ -486,13 +488,15 @@ int device_cus() {
 bool gemv1_supported(int64_t K, int64_t N) { return awqk::gemv1_path(K, N) != 0; }
 
 hipError_t launch_gemv1(const void* x, int xdt, int64_t K, const uint32_t* qw,
-                        const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
-                        void* y, int ydt, hipStream_t st) {
+                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int group,
+                        const float* r, void* y, int ydt, hipStream_t st) {
   using namespace awqk;
   const uint16_t* xp = (const uint16_t*)x;
+  const int gsh = group == 64 ? 1 : group == 128 ? 2 : group == 256 ? 3 : -1;
+  if (gsh < 0) return hipErrorInvalidValue;
 #define AWQ_G1(DT, YDT)                                                                         \
-  return r ? gemv1_dispatch<DT, YDT, true>(xp, K, qw, scales, zeros, N, r, y, st)               \
-           : gemv1_dispatch<DT, YDT, false>(xp, K, qw, scales, zeros, N, r, y, st)
+  return r ? gemv1_dispatch<DT, YDT, true>(xp, K, qw, scales, zeros, N, gsh, r, y, st)          \
+           : gemv1_dispatch<DT, YDT, false>(xp, K, qw, scales, zeros, N, gsh, r, y, st)
   if (xdt == DT_F16) {
     if (ydt == DT_F16) AWQ_G1(DT_F16, DT_F16);
     if (ydt == DT_BF16) AWQ_G1(DT_F16, DT_BF16);

@@ -8,7 +8,9 @@
 // and its cost is the dense contraction E_i X^T (2 T N K flops), which runs on
 // the matrix cores.  Three steps per candidate:
 //   1. k_err_gen    one block per row: the row's groups are quantized exactly
-//                   as awq_quantize_pack does, E = W - D (q - z) / s in float;
+//                   as awq_quantize_pack (the 4-bit asymmetric grid) or
+//                   awq_quantize_codes (any grid) do, E = W - D (q - z) / s
+//                   in float;
 //                   the row's max|E| fixes p (so the row fits fp16's normal
 //                   range), then E * 2^p is written as fp16 into the
 //                   workspace, with p per row (the errors stay in registers
@@ -46,9 +48,14 @@ __global__ void k_cand_scales(const float* __restrict__ m, const double* __restr
 // ---------------------------------------------------------------------------
 // error generation
 // ---------------------------------------------------------------------------
-template <int DT>
+// Grids of the error generator: the 4-bit asymmetric one with compile-time
+// constants, any asymmetric one, any symmetric one.
+enum { kGridQ4 = 0, kGridAsym = 1, kGridSym = 2 };
+
+template <int DT, int GL, int GR>
 __device__ __forceinline__ void err_word(const uint16_t* __restrict__ wrow,
-                                         const float* __restrict__ s, int64_t k0, float e[8]) {
+                                         const float* __restrict__ s, int64_t k0, QSpec q,
+                                         float e[8]) {
   const u32x4 raw = ldg128(wrow + k0);
   const f32x4 s0 = *reinterpret_cast<const f32x4*>(s + k0);
   const f32x4 s1 = *reinterpret_cast<const f32x4*>(s + k0 + 4);
@@ -68,21 +75,22 @@ __device__ __forceinline__ void err_word(const uint16_t* __restrict__ wrow,
     mn = fminf(mn, wp[j]);
     mx = fmaxf(mx, wp[j]);
   }
-  seg16_minmax(mn, mx);
-  const GroupGrid g = group_grid(mn, mx);
+  seg_minmax<GL>(mn, mx);
+  const GroupGrid g = group_grid<GR == kGridSym>(mn, mx, GR == kGridQ4 ? kQ4 : q);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float q = quant_code(wp[j], g);
-    const float grid = g.D * (q - g.z);            // exact: fp16 step x 4-bit integer
+    const float c = quant_code(wp[j], g);
+    const float grid = g.D * (c - g.z);            // exact: fp16 step x small integer
     e[j] = w[j] - grid / sv[j];
   }
 }
 
 constexpr int kErrKeep = 4;   // packed words per thread kept in registers (K <= 8192)
 
-template <int DT>
+// GL: threads per quantization group (group / 8); q: the grid, GR its kind.
+template <int DT, int GL, int GR>
 __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W, int64_t N,
-                                                 int64_t K, const float* __restrict__ s,
+                                                 int64_t K, const float* __restrict__ s, QSpec q,
                                                  uint16_t* __restrict__ E, int* __restrict__ pexp) {
   const int64_t n = blockIdx.x;
   const uint16_t* wrow = W + n * K;
@@ -119,13 +127,13 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
   float emax = 0.0f;
   if (wpr <= 256 * kErrKeep) {
     // the row's errors stay in registers between the maximum and the store
-    // (whole 16-lane segments are in or out: wpr is a multiple of 16)
+    // (whole GL-lane segments are in or out: wpr is a multiple of GL)
     float e[kErrKeep][8];
 #pragma unroll
     for (int i = 0; i < kErrKeep; ++i) {
       const int64_t c = threadIdx.x + 256 * i;
       if (c < wpr) {
-        err_word<DT>(wrow, s, c * 8, e[i]);
+        err_word<DT, GL, GR>(wrow, s, c * 8, q, e[i]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) emax = fmaxf(emax, fabsf(e[i][j]));
       }
@@ -138,12 +146,12 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
     }
     return;
   }
-  // pass 1: largest |E| of the row (whole 16-lane segments are in or out)
+  // pass 1: largest |E| of the row (whole GL-lane segments are in or out)
   for (int64_t c0 = 0; c0 < wpr; c0 += 256) {
     const int64_t c = c0 + threadIdx.x;
     float e[8];
     if (c < wpr) {
-      err_word<DT>(wrow, s, c * 8, e);
+      err_word<DT, GL, GR>(wrow, s, c * 8, q, e);
 #pragma unroll
       for (int j = 0; j < 8; ++j) emax = fmaxf(emax, fabsf(e[j]));
     }
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
     const int64_t c = c0 + threadIdx.x;
     if (c < wpr) {
       float e[8];
-      err_word<DT>(wrow, s, c * 8, e);
+      err_word<DT, GL, GR>(wrow, s, c * 8, q, e);
       store(c, e, p);
     }
   }
@@ -418,8 +426,8 @@ size_t search_ws_bytes(int dt, int64_t N, int64_t K, int64_t T, int n_alpha) {
 
 hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void* x, int64_t T,
                          int64_t ldx, const float* mean_abs, const double* alphas, int n_alpha,
-                         float* s_out, float* inv_s_out, double* loss_out, int32_t* best_out,
-                         void* ws, hipStream_t st) {
+                         QuantVariant qv, float* s_out, float* inv_s_out, double* loss_out,
+                         int32_t* best_out, void* ws, hipStream_t st) {
   using namespace awqk;
   const SearchWs sw = carve(ws, dt, N, K, T, n_alpha);
   const int64_t nS = (int64_t)n_alpha * K;
@@ -427,16 +435,27 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
                      alphas, n_alpha, K, sw.S);
   const double tn = (double)T * (double)N;
   // error rows of candidate i into slot c of the workspace
+  const QSpec q = qspec(qv.bits, qv.sym);
   auto err_gen = [&](const float* s_i, int c) {
     uint16_t* E = sw.E + (int64_t)c * N * K;
     int* pe = sw.pexp + (int64_t)c * N;
-    if (dt == DT_F16)
-      hipLaunchKernelGGL(k_err_gen<DT_F16>, dim3((unsigned)N), dim3(256), 0, st,
-                         (const uint16_t*)w, N, K, s_i, E, pe);
-    else
-      hipLaunchKernelGGL(k_err_gen<DT_BF16>, dim3((unsigned)N), dim3(256), 0, st,
-                         (const uint16_t*)w, N, K, s_i, E, pe);
+    const uint16_t* W = (const uint16_t*)w;
+#define AWQ_EG2(GL, GR)                                                                             \
+  if (dt == DT_F16)                                                                                 \
+    hipLaunchKernelGGL((k_err_gen<DT_F16, GL, GR>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, q, E, pe); \
+  else                                                                                              \
+    hipLaunchKernelGGL((k_err_gen<DT_BF16, GL, GR>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, q, E, pe)
+#define AWQ_EG(GL)                                                                                  \
+  if (q.sym) { AWQ_EG2(GL, kGridSym); }                                                             \
+  else if (qv.bits == 4) { AWQ_EG2(GL, kGridQ4); }                                                  \
+  else { AWQ_EG2(GL, kGridAsym); }
+    if (qv.group == 64) { AWQ_EG(8); }
+    else if (qv.group == 256) { AWQ_EG(32); }
+    else { AWQ_EG(16); }
+#undef AWQ_EG2
+#undef AWQ_EG
   };
+  if (qv.group != 64 && qv.group != 128 && qv.group != 256) return hipErrorInvalidValue;
   if (sw.gram) {
     const hipError_t e = launch_gram_prepare(x, dt, T, K, ldx, sw.Xt, sw.Gp, sw.G, sw.P, sw.sk, st);
     if (e != hipSuccess) return e;

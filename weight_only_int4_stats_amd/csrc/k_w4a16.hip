@@ -165,7 +165,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
                                              const uint32_t* __restrict__ qw,
                                              const uint32_t* __restrict__ ctab,
                                              const int* __restrict__ en, int64_t N,
-                                             void* __restrict__ y, int64_t ldy) {
+                                             void* __restrict__ y, int64_t ldy, int glog) {
   // three LDS arrays, the loop unrolled by three: each stage is a known array
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kStage];
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
-  const int64_t G = K / kGroup;
+  const int64_t G = K >> glog;                 // groups of 2^glog >= kBK channels per row
   const int64_t S = K / kBK;
   const int rows = (int)(M - m0 < kMT ? M - m0 : kMT);
   const int cols = (int)(N - n0 < kNT ? N - n0 : kNT);
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
       dma16(ars, lb + (4 * wv + u) * 1024, aoff[u], k0 * 2);
     } else {
       dma16(brs, lb + kAStage + wv * 1024, boff, k0 >> 1);
-      if (wv < 2) dma16(crs, lb + kAStage + kBStage + wv * 1024, coff, (uint32_t)((k0 / kGroup) * N * 8));
+      if (wv < 2) dma16(crs, lb + kAStage + kBStage + wv * 1024, coff, (uint32_t)((k0 >> glog) * N * 8));
     }
   };
   auto issue = [&](int64_t s, const uint8_t* base) {
@@ -356,8 +356,10 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
 // (row l % 16, block b = l / 16) loads chunk 4 g + b of its row (one 128-bit
 // load per group) and feeds word i of it to the MFMA of step i; the B lane
 // (token l % 16, block b) loads the matching 8 fp16 activations of chunk
-// 4 g + b.  A group's four steps thus use one step and zero point, which turn
-// into the packed-fma constants.  The per-row power of two e_n (as in the
+// 4 g + b.  A unit g of 128 input channels is four such steps; a lane's chunk
+// lies in one weight group (a unit holds one group of 128, half of one of 256
+// or two of 64), whose step and zero point turn into the lane's packed-fma
+// constants.  The per-row power of two e_n (as in the
 // GEMM) is found from the row's steps in a prologue; the four waves' 16 x 16
 // partial tiles are added in LDS in a fixed order.
 constexpr int kSkW = 4;                 // waves per block (K quarters)
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
                                                      const uint32_t* __restrict__ qw,
                                                      const uint16_t* __restrict__ scales,
                                                      const uint8_t* __restrict__ zeros, int64_t N,
-                                                     void* __restrict__ y, int64_t ldy) {
+                                                     void* __restrict__ y, int64_t ldy, int glog) {
   __shared__ float red[kSkW][16 * 16];
   __shared__ float rmax[kSkW][16];
   const int lane = threadIdx.x & 63;
@@ -380,7 +382,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
   const int b = lane >> 4;                       // k block
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int nrows = (int)(N - n0 < 16 ? N - n0 : 16);
-  const int G = (int)(K >> 7);
+  const int G = (int)(K >> 7);                   // 128-channel units (4 MFMA steps each)
+  const int GW = (int)(K >> glog);               // weight groups per row
+  const int csh = glog - 5;                      // 32-code chunk -> weight group
   const int g0 = (int)((int64_t)wv * G / kSkW), g1 = (int)((int64_t)(wv + 1) * G / kSkW);
   const uint32_t KW = (uint32_t)(K >> 3);
   const bool rowok = rl < nrows;
@@ -388,27 +392,29 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(qw + n0 * KW), (short)0, nrows * (int)KW * 4, kBufferWord3);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(scales + n0 * G), (short)0, nrows * G * 2, kBufferWord3);
+      (void*)(scales + n0 * GW), (short)0, nrows * GW * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(zeros + n0 * G), (short)0, nrows * G, kBufferWord3);
+      (void*)(zeros + n0 * GW), (short)0, nrows * GW, kBufferWord3);
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)xq, (short)0, M * (int)K * 2, kBufferWord3);
 
   // ---- slot loads for group g (rows / tokens out of range read 0)
   // first piece of the row's steps for the power of two (issued before the
   // group loads: vector memory returns in order)
-  const int npc = (G * 2 + 15) / 16;             // 16-byte pieces of a row's steps
-  const uint32_t srow = (uint32_t)rl * (uint32_t)G * 2;
+  const int npc = (GW * 2 + 15) / 16;            // 16-byte pieces of a row's steps
+  const uint32_t srow = (uint32_t)rl * (uint32_t)GW * 2;
   const u32x4 sp0 = __builtin_amdgcn_raw_buffer_load_b128(srs, rowok && b < npc ? srow + 16 * b : kBufferOob, 0, 0);
 
   u32x4 wa[P], xb[P][4];
   uint32_t sr[P], zr[P];
+  // the lane's chunk 4 g + b lies in weight group (4 g + b) >> csh
   auto load_group = [&](int slot, int g) {
     const bool ok = g < g1;
     const uint32_t woff = (uint32_t)rl * KW * 4 + (uint32_t)(4 * g + b) * 16;
+    const uint32_t gw = (uint32_t)(rl * GW + ((4 * g + b) >> csh));
     wa[slot] = __builtin_amdgcn_raw_buffer_load_b128(wrs, ok && rowok ? woff : kBufferOob, 0, kBufferNt);
-    sr[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, ok && rowok ? (uint32_t)(rl * G + g) * 2 : kBufferOob, 0, 0);
-    zr[slot] = __builtin_amdgcn_raw_buffer_load_b8(zrs, ok && rowok ? (uint32_t)(rl * G + g) : kBufferOob, 0, 0);
+    sr[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, ok && rowok ? gw * 2 : kBufferOob, 0, 0);
+    zr[slot] = __builtin_amdgcn_raw_buffer_load_b8(zrs, ok && rowok ? gw : kBufferOob, 0, 0);
     const uint32_t xoff = ((uint32_t)rl * (uint32_t)K + (uint32_t)(128 * g + 32 * b)) * 2;
     const bool xok = ok && rl < M;
 #pragma unroll
@@ -424,7 +430,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict_
   auto piece_max = [&](const u32x4& v, int pc, float m) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (pc * 8 + j < G) m = fmaxf(m, f16_to_f32((v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu));
+      if (pc * 8 + j < GW) m = fmaxf(m, f16_to_f32((v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu));
     return m;
   };
   float mx = piece_max(sp0, b, 0.0f);
@@ -485,7 +491,7 @@ struct GemmWs {
   size_t bytes;
 };
 
-inline GemmWs gemm_ws(void* ws, int64_t M, int64_t N, int64_t K) {
+inline GemmWs gemm_ws(void* ws, int64_t M, int64_t N, int64_t K, int group) {
   GemmWs w{};
   char* base = (char*)ws;
   size_t off = 0;
@@ -497,22 +503,22 @@ inline GemmWs gemm_ws(void* ws, int64_t M, int64_t N, int64_t K) {
   w.xq = (uint16_t*)take((size_t)M * K * 2);
   w.pm = (int*)take((size_t)M * 4);
   w.en = (int*)take((size_t)N * 4);
-  w.ctab = (uint32_t*)take((size_t)N * (K / kGroup) * 8);
+  w.ctab = (uint32_t*)take((size_t)N * (K / group) * 8);
   w.bytes = off;
   return w;
 }
 
 template <int DT, int YDT, bool HAS_R>
 hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
-                         const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
-                         void* y, int64_t ldy, void* ws, hipStream_t st) {
-  const GemmWs w = gemm_ws(ws, M, N, K);
+                         const uint16_t* scales, const uint8_t* zeros, int64_t N, int glog,
+                         const float* r, void* y, int64_t ldy, void* ws, hipStream_t st) {
+  const GemmWs w = gemm_ws(ws, M, N, K, 1 << glog);
   hipLaunchKernelGGL((k_rows_f16<DT, HAS_R, true>), dim3((unsigned)M), dim3(256), 0, st, x, K, ldx,
                      r, w.xq, w.pm);
   hipLaunchKernelGGL(k_gemm_consts, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st, scales, zeros, N,
-                     K / kGroup, w.en, w.ctab);
+                     K >> glog, w.en, w.ctab);
   hipLaunchKernelGGL((k_gemm<YDT>), dim3((unsigned)gemm_blocks(M, N)), dim3(512), 0, st, w.xq, M, K, w.pm,
-                     qw, w.ctab, w.en, N, y, ldy);
+                     qw, w.ctab, w.en, N, y, ldy, glog);
   return hipGetLastError();
 }
 
@@ -544,7 +550,7 @@ template <int DT, int YDT, bool HAS_R, int NP, int P>
 __global__ __launch_bounds__(1024) void k_gemm_skinny_cu(
     const uint16_t* __restrict__ x, int M, int64_t K, int64_t ldx, const float* __restrict__ r,
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
-    const uint8_t* __restrict__ zeros, int64_t N, void* __restrict__ y, int64_t ldy) {
+    const uint8_t* __restrict__ zeros, int64_t N, void* __restrict__ y, int64_t ldy, int glog) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds_sc[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -552,7 +558,9 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_cu(
   const int rl = lane & 15;
   const int b = lane >> 4;
   const uint32_t K8 = (uint32_t)(K >> 3);
-  const int G = (int)(K >> 7);
+  const int G = (int)(K >> 7);                   // 128-channel units (4 MFMA steps each)
+  const int GW = (int)(K >> glog);               // weight groups per row
+  const int csh = glog - 5;                      // 32-code chunk -> weight group
   const uint32_t KW = (uint32_t)(K >> 3);
   const int64_t r0 = (int64_t)blockIdx.x * N / gridDim.x;
   const int nrows = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x - r0);
@@ -599,9 +607,9 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_cu(
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(qw + r0 * KW), (short)0, nrows * (int)KW * 4, kBufferWord3);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(scales + r0 * G), (short)0, nrows * G * 2, kBufferWord3);
+      (void*)(scales + r0 * GW), (short)0, nrows * GW * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(zeros + r0 * G), (short)0, nrows * G, kBufferWord3);
+      (void*)(zeros + r0 * GW), (short)0, nrows * GW, kBufferWord3);
   int it = wv;
   int tile = 0, g0 = 0, g1 = 0;
   auto set_item = [&](int item) {
@@ -616,17 +624,18 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_cu(
   auto load_group = [&](int slot, int g) {
     const int row = tile * 16 + rl;
     const bool ok = have && g < g1 && row < nrows;
+    const uint32_t gw = (uint32_t)(row * GW + ((4 * g + b) >> csh));    // the chunk's weight group
     wa[slot] = __builtin_amdgcn_raw_buffer_load_b128(
         wrs, ok ? (uint32_t)row * KW * 4 + (uint32_t)(4 * g + b) * 16 : kBufferOob, 0, kBufferNt);
-    sr[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, ok ? (uint32_t)(row * G + g) * 2 : kBufferOob, 0, 0);
-    zr[slot] = __builtin_amdgcn_raw_buffer_load_b8(zrs, ok ? (uint32_t)(row * G + g) : kBufferOob, 0, 0);
+    sr[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, ok ? gw * 2 : kBufferOob, 0, 0);
+    zr[slot] = __builtin_amdgcn_raw_buffer_load_b8(zrs, ok ? gw : kBufferOob, 0, 0);
   };
   // 16-byte pieces of the row's steps, for the row's power of two
-  const int npc = (G * 2 + 15) / 16;
+  const int npc = (GW * 2 + 15) / 16;
   auto load_piece = [&](int pc) {
     const int row = tile * 16 + rl;
     return __builtin_amdgcn_raw_buffer_load_b128(
-        srs, have && row < nrows && pc < npc ? (uint32_t)row * G * 2 + 16 * pc : kBufferOob, 0, 0);
+        srs, have && row < nrows && pc < npc ? (uint32_t)row * GW * 2 + 16 * pc : kBufferOob, 0, 0);
   };
   // branch-free (a wave without an item reads out of range): a conditional
   // block of loads here would make every later wait count all of them
@@ -698,7 +707,7 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_cu(
     auto piece_max = [&](const u32x4& pv, int pc, float m) {
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (pc * 8 + q < G) m = fmaxf(m, f16_to_f32((pv[q >> 1] >> (16 * (q & 1))) & 0xFFFFu));
+        if (pc * 8 + q < GW) m = fmaxf(m, f16_to_f32((pv[q >> 1] >> (16 * (q & 1))) & 0xFFFFu));
       return m;
     };
     float mx = piece_max(sp0, b, 0.0f);
@@ -781,9 +790,10 @@ inline int skinny_cu_pieces(int64_t M, int64_t K) {
   return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= kScMaxPieces ? 8 : 0;
 }
 
-// Blocks of the per-CU skinny product for (M, N, K); 0 if it does not apply.
+// Blocks of the per-CU skinny product for (M, N, K); 0 if it does not apply
+// (K must be whole 128-channel units).
 inline int skinny_cu_blocks(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || M > 16 || skinny_cu_pieces(M, K) == 0) return 0;
+  if (M < 1 || M > 16 || K % 128 != 0 || skinny_cu_pieces(M, K) == 0) return 0;
   const int64_t cus = awq::device_cus();
   const int64_t nblk = N < cus ? N : cus;
   const int64_t rows_max = (N + nblk - 1) / nblk;
@@ -793,19 +803,20 @@ inline int skinny_cu_blocks(int64_t M, int64_t N, int64_t K) {
 
 template <int DT, int YDT, bool HAS_R, int P = 2>
 hipError_t skinny_cu_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
-                              const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
-                              void* y, int64_t ldy, int nblk, hipStream_t st) {
+                              const uint16_t* scales, const uint8_t* zeros, int64_t N, int glog,
+                              const float* r, void* y, int64_t ldy, int nblk, hipStream_t st) {
   if (nblk > N) nblk = (int)N;
   const int64_t rows_max = (N + nblk - 1) / nblk;
   size_t lds = skinny_cu_lds(M, K, rows_max);
   const int np = skinny_cu_pieces(M, K);
-  if (M < 1 || M > 16 || np == 0 || lds > 160 * 1024 || rows_max * (K >> 1) >= (int64_t(1) << 31))
+  if (M < 1 || M > 16 || np == 0 || K % 128 != 0 || lds > 160 * 1024 ||
+      rows_max * (K >> 1) >= (int64_t(1) << 31))
     return hipErrorInvalidValue;
   if (lds < 81 * 1024) lds = 81 * 1024;           // one block per compute unit
   const dim3 grid((unsigned)nblk), block(1024);
 #define AWQ_SC(NP)                                                                                    \
   hipLaunchKernelGGL((k_gemm_skinny_cu<DT, YDT, HAS_R, NP, P>), grid, block, lds, st, x, (int)M, K, ldx, r, \
-                     qw, scales, zeros, N, y, ldy)
+                     qw, scales, zeros, N, y, ldy, glog)
   if (np == 1) AWQ_SC(1);
   else if (np == 2) AWQ_SC(2);
   else if (np == 4) AWQ_SC(4);
@@ -816,63 +827,69 @@ hipError_t skinny_cu_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t l
 
 template <int DT, int YDT, bool HAS_R, int P = kSkP>
 hipError_t skinny_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
-                           const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
-                           void* y, int64_t ldy, void* ws, hipStream_t st) {
-  const GemmWs w = gemm_ws(ws, M, N, K);
+                           const uint16_t* scales, const uint8_t* zeros, int64_t N, int glog,
+                           const float* r, void* y, int64_t ldy, void* ws, hipStream_t st) {
+  const GemmWs w = gemm_ws(ws, M, N, K, 1 << glog);
   hipLaunchKernelGGL((k_rows_f16<DT, HAS_R, true>), dim3((unsigned)M), dim3(256), 0, st, x, K, ldx,
                      r, w.xq, w.pm);
   hipLaunchKernelGGL((k_gemm_skinny<YDT, P>), dim3((unsigned)((N + 15) / 16)), dim3(64 * kSkW), 0, st,
-                     w.xq, (int)M, K, w.pm, qw, scales, zeros, N, y, ldy);
+                     w.xq, (int)M, K, w.pm, qw, scales, zeros, N, y, ldy, glog);
   return hipGetLastError();
 }
 
 template <int DT, int YDT>
 hipError_t w4a16_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
-                          const uint16_t* scales, const uint8_t* zeros, int64_t N, const float* r,
-                          void* y, int64_t ldy, void* ws, hipStream_t st) {
+                          const uint16_t* scales, const uint8_t* zeros, int64_t N, int glog,
+                          const float* r, void* y, int64_t ldy, void* ws, hipStream_t st) {
   if (M == 1 && awq::gemv1_supported(K, N))
-    return awq::launch_gemv1(x, DT, K, qw, scales, zeros, N, r, y, YDT, st);
+    return awq::launch_gemv1(x, DT, K, qw, scales, zeros, N, 1 << glog, r, y, YDT, st);
   if (const int nblk = skinny_cu_blocks(M, N, K)) {
     // deeper ring for long K slices (few rows per block)
     const int64_t rows = (N + nblk - 1) / nblk, tiles = (rows + 15) / 16;
-    const bool deep = (K / kGroup) * tiles >= 16 * 16;
-    if (r) return deep ? skinny_cu_dispatch<DT, YDT, true, 4>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, nblk, st)
-                       : skinny_cu_dispatch<DT, YDT, true, 2>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, nblk, st);
-    return deep ? skinny_cu_dispatch<DT, YDT, false, 4>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, nblk, st)
-                : skinny_cu_dispatch<DT, YDT, false, 2>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, nblk, st);
+    const bool deep = (K / 128) * tiles >= 16 * 16;
+    if (r) return deep ? skinny_cu_dispatch<DT, YDT, true, 4>(x, M, K, ldx, qw, scales, zeros, N, glog, r, y, ldy, nblk, st)
+                       : skinny_cu_dispatch<DT, YDT, true, 2>(x, M, K, ldx, qw, scales, zeros, N, glog, r, y, ldy, nblk, st);
+    return deep ? skinny_cu_dispatch<DT, YDT, false, 4>(x, M, K, ldx, qw, scales, zeros, N, glog, r, y, ldy, nblk, st)
+                : skinny_cu_dispatch<DT, YDT, false, 2>(x, M, K, ldx, qw, scales, zeros, N, glog, r, y, ldy, nblk, st);
   }
-  if (M <= kSkMaxM) {
-    if (r) return skinny_dispatch<DT, YDT, true>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, ws, st);
-    return skinny_dispatch<DT, YDT, false>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, ws, st);
+  if (M <= kSkMaxM && K % 128 == 0) {
+    if (r) return skinny_dispatch<DT, YDT, true>(x, M, K, ldx, qw, scales, zeros, N, glog, r, y, ldy, ws, st);
+    return skinny_dispatch<DT, YDT, false>(x, M, K, ldx, qw, scales, zeros, N, glog, r, y, ldy, ws, st);
   }
-  if (r) return gemm_dispatch<DT, YDT, true>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, ws, st);
-  return gemm_dispatch<DT, YDT, false>(x, M, K, ldx, qw, scales, zeros, N, r, y, ldy, ws, st);
+  if (r) return gemm_dispatch<DT, YDT, true>(x, M, K, ldx, qw, scales, zeros, N, glog, r, y, ldy, ws, st);
+  return gemm_dispatch<DT, YDT, false>(x, M, K, ldx, qw, scales, zeros, N, glog, r, y, ldy, ws, st);
 }
 
 }  // namespace awqk
 
 namespace awq {
 
-size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0 || (M == 1 && gemv1_supported(K, N)) || awqk::skinny_cu_blocks(M, N, K))
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int group) {
+  if (M <= 0 || N <= 0 || K <= 0 || group <= 0 || (M == 1 && gemv1_supported(K, N)) ||
+      awqk::skinny_cu_blocks(M, N, K))
     return 0;
-  return awqk::gemm_ws(nullptr, M, N, K).bytes;
+  return awqk::gemm_ws(nullptr, M, N, K, group).bytes;
 }
 
 hipError_t launch_w4a16(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx,
                         const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros,
-                        int64_t N, const float* inv_s, void* y, int ydt, int64_t ldy, void* ws,
-                        hipStream_t st) {
+                        int64_t N, int group, const float* inv_s, void* y, int ydt, int64_t ldy,
+                        void* ws, hipStream_t st) {
   using namespace awqk;
   const uint16_t* xp = (const uint16_t*)x;
+  const int glog = group == 64 ? 6 : group == 128 ? 7 : group == 256 ? 8 : -1;
+  if (glog < 0) return hipErrorInvalidValue;
+#define AWQ_WD(XT, YT) \
+  return w4a16_dispatch<XT, YT>(xp, M, K, ldx, qw, scales, zeros, N, glog, inv_s, y, ldy, ws, st)
   if (xdt == DT_F16) {
-    if (ydt == DT_F16) return w4a16_dispatch<DT_F16, DT_F16>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
-    if (ydt == DT_BF16) return w4a16_dispatch<DT_F16, DT_BF16>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
-    return w4a16_dispatch<DT_F16, DT_F32>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
+    if (ydt == DT_F16) AWQ_WD(DT_F16, DT_F16);
+    if (ydt == DT_BF16) AWQ_WD(DT_F16, DT_BF16);
+    AWQ_WD(DT_F16, DT_F32);
   }
-  if (ydt == DT_F16) return w4a16_dispatch<DT_BF16, DT_F16>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
-  if (ydt == DT_BF16) return w4a16_dispatch<DT_BF16, DT_BF16>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
-  return w4a16_dispatch<DT_BF16, DT_F32>(xp, M, K, ldx, qw, scales, zeros, N, inv_s, y, ldy, ws, st);
+  if (ydt == DT_F16) AWQ_WD(DT_BF16, DT_F16);
+  if (ydt == DT_BF16) AWQ_WD(DT_BF16, DT_BF16);
+  AWQ_WD(DT_BF16, DT_F32);
+#undef AWQ_WD
 }
 
 }  // namespace awq
