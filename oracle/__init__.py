@@ -33,5 +33,6 @@ from .awq import (  # noqa: F401
     search_losses, search_losses_operand_model, choose_candidate, search_scales,
     w4a16_matmul, w4a16_matmul_rows,
     round_bf16, round_storage, fold_scales,
+    salient_channels,
     symmetric_rtn,
 )

@@ -107,7 +107,8 @@ def code_max(bits: int = NBITS, symmetric: bool = False) -> int:
     return (1 << bits) if symmetric else (1 << bits) - 1
 
 
-def group_quant_params(wg: np.ndarray, bits: int = NBITS, symmetric: bool = False):
+def group_quant_params(wg: np.ndarray, bits: int = NBITS, symmetric: bool = False,
+                       exclude: np.ndarray | None = None):
     """Step and zero point of each group.  ``wg`` float32 [..., G, group].
 
     Asymmetric (the default; scale and zero point per group, "AWQ > Benefits
@@ -120,17 +121,20 @@ def group_quant_params(wg: np.ndarray, bits: int = NBITS, symmetric: bool = Fals
       d  = fp32( max|w'| / 2^(N-1) )                     exact: a power-of-two divisor
       z  = 2^(N-1)                                       codes stored shifted by z
     Both: step (fp16) = round-up(d), at least 2^-24; D = fp32(step).
+    ``exclude`` (bool, broadcast against wg): weights kept in 16-bit, left out
+    of the min / max (a group with none left has lo = hi = 0).
     Returns (D float32, step float16, z float32, d float32).
     """
     wg = np.asarray(wg, dtype=np.float32)
     assert np.all(np.isfinite(wg)), "non-finite weights are outside the method's domain"
     assert 2 <= bits <= (7 if symmetric else 8), "codes must fit one byte"
+    ex = np.zeros(wg.shape, dtype=bool) if exclude is None else np.broadcast_to(exclude, wg.shape)
     if symmetric:
-        amax = np.max(np.abs(wg), axis=-1)
+        amax = np.max(np.where(ex, np.float32(0), np.abs(wg)), axis=-1)
         d = amax / np.float32(1 << (bits - 1))
     else:
-        lo = np.minimum(wg.min(axis=-1), np.float32(0))
-        hi = np.maximum(wg.max(axis=-1), np.float32(0))
+        lo = np.minimum(np.where(ex, np.float32(np.inf), wg).min(axis=-1), np.float32(0))
+        hi = np.maximum(np.where(ex, np.float32(-np.inf), wg).max(axis=-1), np.float32(0))
         d = (hi - lo) / np.float32((1 << bits) - 1)
     step = fp16_round_up(np.maximum(d, np.float32(FP16_TINY)))
     assert np.all(np.isfinite(step)), "group range exceeds the float16 step range"
@@ -168,7 +172,7 @@ def unscale_activation(x: np.ndarray, s: np.ndarray) -> np.ndarray:
 
 
 def quantize_layer(W: np.ndarray, s: np.ndarray | None = None, group: int = GROUP,
-                   bits: int = NBITS, symmetric: bool = False):
+                   bits: int = NBITS, symmetric: bool = False, keep: np.ndarray | None = None):
     """Quantize W' = W * diag(s) ("AWQ Math", "The equivalent transform").
 
     W float32 [N, K] holding fp16/bf16 values; s float32 [K] or None (s = 1,
@@ -177,14 +181,17 @@ def quantize_layer(W: np.ndarray, s: np.ndarray | None = None, group: int = GROU
     ``symmetric`` select the grid (``group_quant_params``).  Returns dict with
     codes q uint8 [N, K], step float16 [N, G], D float32 [N, G], z uint8
     [N, G], d float32 [N, G] (pre-rounding step), wp float32 [N, K] (the
-    scaled weights).
+    scaled weights).  ``keep`` (bool [K], optional): input channels kept in
+    16-bit, left out of their groups' ranges (their codes are computed but
+    not used).
     """
     W = np.asarray(W, dtype=np.float32)
     N, K = W.shape
     assert K % group == 0, "K must be a multiple of the group size"
     wp = W if s is None else scale_columns(W, np.asarray(s, dtype=np.float32))
     wg = wp.reshape(N, K // group, group)
-    D, step, z, d = group_quant_params(wg, bits, symmetric)
+    ex = None if keep is None else np.asarray(keep, dtype=bool).reshape(1, K // group, group)
+    D, step, z, d = group_quant_params(wg, bits, symmetric, ex)
     q = quantize_codes(wg, D, z, code_max(bits, symmetric)).reshape(N, K)
     return {"q": q, "step": step, "D": D, "z": z.astype(np.uint8), "d": d, "wp": wp}
 
@@ -217,24 +224,29 @@ def unpack_codes(words: np.ndarray) -> np.ndarray:
 #     the calibration activations; a small grid of alpha; forward passes only.
 # --------------------------------------------------------------------------
 def _dequantized_weight(W: np.ndarray, s: np.ndarray, group: int = GROUP,
-                        bits: int = NBITS, symmetric: bool = False) -> np.ndarray:
-    """W_hat = Q(W diag(s)) diag(s)^-1 in float64."""
-    r = quantize_layer(W, s, group, bits, symmetric)
+                        bits: int = NBITS, symmetric: bool = False,
+                        keep: np.ndarray | None = None) -> np.ndarray:
+    """W_hat = Q(W diag(s)) diag(s)^-1 in float64; kept channels are W itself."""
+    r = quantize_layer(W, s, group, bits, symmetric, keep)
     N, K = W.shape
     G = K // group
     grid = dequantize(r["q"].reshape(N, G, group), r["D"], r["z"].astype(np.float32))
-    return unscale_activation(grid.reshape(N, K), np.asarray(s, dtype=np.float32))
+    Wh = unscale_activation(grid.reshape(N, K), np.asarray(s, dtype=np.float32))
+    if keep is not None:
+        Wh = np.where(np.asarray(keep, dtype=bool)[None, :], np.asarray(W, dtype=np.float64), Wh)
+    return Wh
 
 
 def search_losses(W: np.ndarray, X: np.ndarray, S: np.ndarray, group: int = GROUP,
-                  t_chunk: int = 4096, *, bits: int = NBITS, symmetric: bool = False) -> np.ndarray:
+                  t_chunk: int = 4096, *, bits: int = NBITS, symmetric: bool = False,
+                  keep: np.ndarray | None = None) -> np.ndarray:
     """L_i = (1 / (T N)) * sum_t sum_n ( sum_k (W - W_hat_i)[n, k] x_t[k] )^2.
 
     READING: the objective is the mean squared error (same argmin as the norm);
     the target is the unrounded W x; W_hat_i uses the stored fp16 step, so the
     loss scores exactly what is deployed.  W float32 [N, K], X float32 [T, K],
     S float32 [n_alpha, K]; ``bits`` / ``symmetric`` select the quantizer's
-    grid.  float64 throughout.
+    grid; ``keep`` marks channels kept in 16-bit (no error).  float64 throughout.
     """
     W = np.asarray(W, dtype=np.float32)
     X = np.asarray(X, dtype=np.float32)
@@ -243,7 +255,7 @@ def search_losses(W: np.ndarray, X: np.ndarray, S: np.ndarray, group: int = GROU
     out = np.empty(S.shape[0], dtype=np.float64)
     W64 = W.astype(np.float64)
     for i in range(S.shape[0]):
-        E = W64 - _dequantized_weight(W, S[i], group, bits, symmetric)
+        E = W64 - _dequantized_weight(W, S[i], group, bits, symmetric, keep)
         acc = 0.0
         for t0 in range(0, T, t_chunk):
             P = X[t0:t0 + t_chunk].astype(np.float64) @ E.T
@@ -271,7 +283,8 @@ def _round_rows_fp16(a32: np.ndarray):
 def search_losses_operand_model(W: np.ndarray, X: np.ndarray, S: np.ndarray,
                                 x_is_fp16: bool = True, group: int = GROUP,
                                 t_chunk: int = 4096, *, bits: int = NBITS,
-                                symmetric: bool = False) -> np.ndarray:
+                                symmetric: bool = False,
+                                keep: np.ndarray | None = None) -> np.ndarray:
     """The same losses as ``search_losses``, scored in the precision of a
     matrix-core evaluation, so that the chosen index -- an integer decided by
     floating point -- is taken in the precision that evaluation uses.
@@ -296,11 +309,13 @@ def search_losses_operand_model(W: np.ndarray, X: np.ndarray, S: np.ndarray,
     out = np.empty(S.shape[0], dtype=np.float64)
     for i in range(S.shape[0]):
         s = np.asarray(S[i], dtype=np.float32)
-        r = quantize_layer(W, s, group, bits, symmetric)
+        r = quantize_layer(W, s, group, bits, symmetric, keep)
         Dk = np.repeat(r["D"], group, axis=1)                       # float32 [N, K]
         zk = np.repeat(r["z"].astype(np.float32), group, axis=1)
         grid = Dk * (r["q"].astype(np.float32) - zk)                # exact in float32
         E32 = W - grid / s[None, :]                                 # float32 division, subtraction
+        if keep is not None:
+            E32 = np.where(np.asarray(keep, dtype=bool)[None, :], np.float32(0), E32)
         Eh, pe = _round_rows_fp16(E32)
         acc = 0.0
         for t0 in range(0, T, t_chunk):
@@ -324,7 +339,7 @@ def choose_candidate(losses: np.ndarray) -> int:
 
 def search_scales(W: np.ndarray, X: np.ndarray, m: np.ndarray, alphas: np.ndarray,
                   group: int = GROUP, operand_model: str | None = None, *,
-                  bits: int = NBITS, symmetric: bool = False):
+                  bits: int = NBITS, symmetric: bool = False, keep: np.ndarray | None = None):
     """Full search: candidate scales, losses, argmin.  Returns
     (best index, s* float32 [K], 1/s* float32 [K], losses float64 [n]).
     operand_model: None scores exactly (float64); "fp16" / "fp16-scaled-x"
@@ -332,10 +347,10 @@ def search_scales(W: np.ndarray, X: np.ndarray, m: np.ndarray, alphas: np.ndarra
     float16, or rounded to float16 per token)."""
     S = candidate_scales(m, alphas)
     if operand_model is None:
-        L = search_losses(W, X, S, group, bits=bits, symmetric=symmetric)
+        L = search_losses(W, X, S, group, bits=bits, symmetric=symmetric, keep=keep)
     else:
         L = search_losses_operand_model(W, X, S, operand_model == "fp16", group,
-                                        bits=bits, symmetric=symmetric)
+                                        bits=bits, symmetric=symmetric, keep=keep)
     i = choose_candidate(L)
     s = S[i]
     return i, s, (np.float32(1.0) / s).astype(np.float32), L
@@ -414,6 +429,28 @@ def fold_scales(v: np.ndarray, s: np.ndarray, axis: int = 1, dtype: str = "f16")
     s32 = np.asarray(s, dtype=np.float32)
     q = v32 / (s32[None, :] if axis == 1 else s32[:, None])   # IEEE binary32 division
     return round_storage(q, dtype)
+
+
+# --------------------------------------------------------------------------
+# O9  the mixed-precision baseline AWQ replaces
+#     "AWQ vs. GPTQ: Understanding Weight Quantization Principles", sections
+#     on the central insight (the salient weights are those of the channels
+#     with large activation magnitudes; protecting about 1 % of them greatly
+#     reduces the degradation) and on per-channel scaling (keeping them in a
+#     higher precision works but gives a mixed-precision model); "AWQ Math",
+#     "Weight-only quantization and where it breaks" (keep the important
+#     weights in FP16 and quantize the rest).
+#     READING: the n_keep channels with the largest mean |x_j|, ties to the
+#     lower index; they are left out of their groups' ranges and carry no
+#     error (``keep`` of quantize_layer and the search losses).
+# --------------------------------------------------------------------------
+def salient_channels(m: np.ndarray, n_keep: int) -> np.ndarray:
+    """bool [K]: True for the n_keep channels of largest m (stable order)."""
+    m = np.asarray(m, dtype=np.float32)
+    order = np.argsort(-m.astype(np.float64), kind="stable")
+    keep = np.zeros(m.shape[0], dtype=bool)
+    keep[order[:n_keep]] = True
+    return keep
 
 
 # --------------------------------------------------------------------------

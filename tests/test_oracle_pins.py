@@ -775,3 +775,84 @@ def test_search_loss_variants_against_loops(group, bits, symmetric):
         assert L8[0] < L[0]
     Lm = O.search_losses_operand_model(W, X, S, True, group, bits=bits, symmetric=symmetric)
     assert np.all(np.abs(Lm - L) <= 2e-3 * L)
+
+
+# ------------------------------------------------ mixed-precision baseline
+def test_salient_channels_rank_brute_force():
+    """The n most salient channels by mean |x| ("AWQ vs. GPTQ", the central
+    insight: saliency follows the activation magnitude), by an explicit rank
+    count: rank_j = #{i: m_i > m_j} + #{i < j: m_i = m_j}, kept when rank_j < n."""
+    g = _rng(120)
+    for K in (128, 515, 1024):
+        m = g.integers(0, 40, K).astype(np.float32) * np.float32(0.25)   # many ties
+        for n in (0, 1, max(1, K // 100), K // 3, K):
+            keep = O.salient_channels(m, n)
+            assert keep.sum() == n
+            for j in range(0, K, 7):
+                rank = sum(1 for i in range(K) if m[i] > m[j] or (m[i] == m[j] and i < j))
+                assert keep[j] == (rank < n)
+
+
+def test_keep_all_is_lossless_and_keep_none_is_plain():
+    g = _rng(121)
+    N, K, T = 3, 256, 7
+    W = _fp16_values(g.standard_normal((N, K)) * 0.02)
+    X = _fp16_values(g.standard_normal((T, K)))
+    S = O.candidate_scales(O.act_mean_abs(X), np.array([0.0, 0.5]))
+    assert np.all(O.search_losses(W, X, S, keep=np.ones(K, bool)) == 0.0)
+    assert np.array_equal(O.search_losses(W, X, S, keep=np.zeros(K, bool)), O.search_losses(W, X, S))
+    Lm = O.search_losses_operand_model(W, X, S, keep=np.ones(K, bool))
+    assert np.all(Lm == 0.0)
+
+
+def _loss_by_loops_keep(W, X, s, keep, group=128):
+    """Loop loss with kept channels exact and every group's range taken over
+    the weights left after removing the kept ones (explicit deletion)."""
+    N, K = W.shape
+    wp = O.scale_columns(W, s)
+    tot = 0.0
+    Wh = np.zeros((N, K))
+    for n in range(N):
+        for gi in range(K // group):
+            idx = np.arange(gi * group, (gi + 1) * group)
+            rest = idx[~keep[idx]]
+            sub = wp[n, rest][None, :] if rest.size else np.zeros((1, 1), np.float32)
+            D, _, z, _ = O.group_quant_params(sub)
+            q = O.quantize_codes(wp[n, idx][None, :], D, z)[0]
+            for t, k in enumerate(idx):
+                Wh[n, k] = float(W[n, k]) if keep[k] else float(D[0]) * (int(q[t]) - int(z[0])) / float(s[k])
+    for t in range(X.shape[0]):
+        for n in range(N):
+            y = math.fsum(float(W[n, k]) * float(X[t, k]) for k in range(K))
+            yq = math.fsum(Wh[n, k] * float(X[t, k]) for k in range(K))
+            tot += (y - yq) ** 2
+    return tot / (X.shape[0] * N)
+
+
+def test_keep_excludes_channels_from_the_range():
+    """Kept channels carry no error and do not set their groups' steps: with
+    the outlier channels kept, the steps shrink to the rest's range; the loss
+    matches explicit loops; and on a layer whose boosted channels are the
+    salient ones, keeping 1 % of the channels lowers the loss against plain
+    round-to-nearest ("AWQ vs. GPTQ", protecting about 1 % of the salient
+    weights reduces the degradation)."""
+    g = _rng(122)
+    N, K, T = 4, 512, 9
+    W = _fp16_values(g.standard_normal((N, K)) * 0.02)
+    boosted = np.array([5, 200, 301, 450, 470])
+    W[:, boosted] *= 25                          # outlier weights on the boosted channels
+    b = np.ones(K, np.float32)
+    b[boosted] = 30.0
+    X = _fp16_values(g.standard_normal((T, K)) * b)
+    m = O.act_mean_abs(X)
+    keep = O.salient_channels(m, len(boosted))
+    assert set(np.flatnonzero(keep)) == set(boosted.tolist())
+    r0 = O.quantize_layer(W, None)
+    rk = O.quantize_layer(W, None, keep=keep)
+    assert np.all(rk["D"] <= r0["D"]) and np.any(rk["D"] < r0["D"])
+    S = O.candidate_scales(m, np.array([0.0, 0.4]))
+    L = O.search_losses(W, X, S, keep=keep)
+    for i in range(2):
+        ref = _loss_by_loops_keep(W, X, S[i], keep)
+        assert abs(L[i] - ref) <= 1e-9 * ref
+    assert L[0] < O.search_losses(W, X, S[:1])[0]
