@@ -250,6 +250,14 @@ def main() -> int:
         variants.append({"group": g, "bits": bits, "grid": "symmetric" if sym else "asymmetric",
                          "loss_rtn": Lv[0], "loss_awq": Lv[iv], "alpha": float(alphas_h[iv]),
                          "rtn_over_awq": Lv[0] / Lv[iv]})
+    # the mixed-precision baseline AWQ replaces: the 1 % most salient channels
+    # (largest mean |x|) kept in 16-bit, the rest round-to-nearest
+    n_keep = KA // 100
+    kept = awq.awq_salient_channels(m, n_keep)
+    _, _, Lm, _ = awq.awq_search_scales(WA, XA, m, alphas[:1], ws=ws_search, kept=kept)
+    mixed = {"kept_channels": n_keep, "group": 128, "bits": 4, "loss": float(Lm.cpu()[0]),
+             "loss_rtn": loss_h[0], "loss_awq": loss_h[best_h],
+             "loss_over_awq": float(Lm.cpu()[0]) / loss_h[best_h]}
     stats_bytes = wa.T * KA * 2
     quant_bytes = NA * KA * 2 + bytes_a
     stages = {
@@ -297,6 +305,7 @@ def main() -> int:
                          "flop_per_launch": gemm_flop, "kernel": "k_gemm"},
         "stages": stages,
         "quantizer_variants": variants,
+        "mixed_precision_baseline": mixed,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(WA, qs[0], scs[0], zs[0], xa1)

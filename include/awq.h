@@ -23,6 +23,10 @@
  *   awq_quantize_codes the quantizer's variants (N bits, asymmetric or
  *                      symmetric grid), one unpacked code per byte; the search
  *                      scores the same variants
+ * and, for the mixed-precision baseline that AWQ replaces (the salient
+ * channels kept in 16-bit, the rest quantized), a channel selector whose mask
+ * the search accepts:
+ *   awq_salient_channels  the n channels with the largest mean |x_j|
  * Linears that read the same input (q, k and v; gate and up) are searched
  * together by passing their row-concatenated W to awq_search_scales: they then
  * share s, and one fold serves them all.
@@ -150,6 +154,10 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
  *   group_size  64, 128 or 256; K a multiple of it and of 128
  *   bits, symmetric  the grid, as for awq_quantize_codes (4 and 0: the grid
  *               of awq_quantize_pack)
+ *   kept        [K] uint8 or NULL, 16-byte aligned: channels with kept[k] != 0
+ *               stay in 16-bit (W_hat = W there) and are left out of their
+ *               groups' ranges; with alphas = {0} the loss is that of the
+ *               mixed-precision baseline (see awq_salient_channels)
  *   s_out       [K] float: s of the best candidate
  *   inv_s_out   [K] float: 1.0f / s (IEEE division); may be NULL
  *   loss_out    [n_alpha] double; may be NULL
@@ -173,9 +181,29 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
 awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
                              const void* x_calib, int64_t T, int64_t ldx,
                              const float* mean_abs, const double* alphas, int n_alpha,
-                             int group_size, int bits, int symmetric, float* s_out,
-                             float* inv_s_out, double* loss_out, int32_t* best_idx_out, void* ws,
-                             size_t ws_bytes, void* stream);
+                             int group_size, int bits, int symmetric, const uint8_t* kept,
+                             float* s_out, float* inv_s_out, double* loss_out,
+                             int32_t* best_idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The salient channels of the mixed-precision baseline that AWQ replaces.
+ * "AWQ vs. GPTQ: Understanding Weight Quantization Principles", sections on
+ * the central insight (a weight's importance follows the magnitude of the
+ * activations it meets; protecting about 1 % of the salient weights greatly
+ * reduces the degradation) and on per-channel scaling (keeping them in higher
+ * precision works but makes the layer mixed-precision); "AWQ Math", section
+ * "Weight-only quantization and where it breaks" (keep the important weights
+ * in FP16 and quantize the rest).
+ *   kept[j] = 1 if rank_j < n_keep else 0,
+ *   rank_j  = #{i : m_i > m_j} + #{i < j : m_i = m_j}   (ties: lower index first)
+ *
+ *   mean_abs  [K] float (output of awq_act_stats), finite
+ *   K         > 0;  n_keep  0..K
+ *   kept      [K] uint8, written
+ * O(K^2) comparisons; not part of the quantization path.
+ */
+awq_status awq_salient_channels(const float* mean_abs, int64_t K, int64_t n_keep, uint8_t* kept,
+                                void* stream);
 
 /*
  * Group-wise asymmetric 4-bit round-to-nearest of W' = W diag(s).

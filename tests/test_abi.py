@@ -28,8 +28,8 @@ def declared_functions():
 def test_header_declares_the_four_calls_and_helpers():
     names = declared_functions()
     for n in ("awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_w4a16_gemm",
-              "awq_fold_scales", "awq_quantize_codes", "awq_workspace_bytes", "awq_status_str",
-              "awq_abi_version"):
+              "awq_fold_scales", "awq_quantize_codes", "awq_salient_channels", "awq_workspace_bytes",
+              "awq_status_str", "awq_abi_version"):
         assert n in names
 
 
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.awq_abi_version() == 3
+    assert lib.awq_abi_version() == 4
     for code in range(8):
         assert lib.awq_status_str(code).decode()
     assert lib.awq_status_str(0).decode() == "ok"
@@ -88,11 +88,11 @@ def test_search_validation():
 
     def call(**kw):
         a = dict(w=A, dt=E.AWQ_F16, N=512, K=512, x=A2, T=64, ldx=512, m=A3, al=A3, na=20, g=128,
-                 bits=4, sym=0, s=A2, inv=NULL, loss=NULL, best=NULL, ws=A3, wsb=ws)
+                 bits=4, sym=0, kept=NULL, s=A2, inv=NULL, loss=NULL, best=NULL, ws=A3, wsb=ws)
         a.update(kw)
         return f(a["w"], a["dt"], a["N"], a["K"], a["x"], a["T"], a["ldx"], a["m"], a["al"], a["na"],
-                 a["g"], a["bits"], a["sym"], a["s"], a["inv"], a["loss"], a["best"], a["ws"], a["wsb"],
-                 NULL)
+                 a["g"], a["bits"], a["sym"], a["kept"], a["s"], a["inv"], a["loss"], a["best"], a["ws"],
+                 a["wsb"], NULL)
 
     assert call(w=NULL) == 1
     assert call(s=NULL) == 1
@@ -112,6 +112,7 @@ def test_search_validation():
     assert call(N=0) == 2
     assert call(ldx=256) == 2
     assert call(w=BAD) == 4
+    assert call(kept=ctypes.c_void_p(0x20008)) == 4   # the mask is read 8 channels at a time
     assert call(ws=NULL) == 6
     assert call(wsb=1024) == 6
 
@@ -154,6 +155,18 @@ def test_quantize_codes_validation():
     assert call(q=ctypes.c_void_p(0x20008)) == 4  # codes 16-byte aligned
     assert call(w=BAD) == 4
     assert call(s=BAD) == 4
+
+
+def test_salient_validation():
+    lib = _lib()
+    f = lib.awq_salient_channels
+    assert f(NULL, 512, 5, A2, NULL) == 1
+    assert f(A, 512, 5, NULL, NULL) == 1
+    assert f(A, 0, 0, A2, NULL) == 2
+    assert f(A, 512, -1, A2, NULL) == 2
+    assert f(A, 512, 513, A2, NULL) == 2
+    assert f(ctypes.c_void_p(0x10002), 512, 5, A2, NULL) == 4
+    assert f(A, 1 << 20, 5, A2, NULL) == 5
 
 
 def test_gemm_validation():

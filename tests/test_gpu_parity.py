@@ -223,34 +223,44 @@ def test_product_special_cases():
 SEARCH_MODEL_RTOL = 1e-5   # GPU loss vs the oracle scored in the same operand precision
 
 
-def _check_search(W, X, dtype, n_alpha=20, group=128, bits=4, sym=False):
+def _check_search(W, X, dtype, n_alpha=20, group=128, bits=4, sym=False, keep=None, alphas=None):
     """Statistic bit-exact; chosen index, s and 1/s bit-exact against the
     oracle scored in the matrix-core operand precision (the decision is taken
     in the same precision on both sides); every loss within SEARCH_MODEL_RTOL
     of that oracle and within the rigorous rounding bound of the exact fp64
-    losses.  group / bits / sym select the quantizer variant."""
-    alphas = WL.alpha_grid(n_alpha)
+    losses.  group / bits / sym select the quantizer variant; keep (bool [K])
+    the channels kept in 16-bit."""
+    alphas = WL.alpha_grid(n_alpha) if alphas is None else alphas
+    n_alpha = len(alphas)
     m = awq.awq_act_stats(gpu(X))
+    kept = None if keep is None else gpu(torch.from_numpy(keep.astype(np.uint8)))
     s, inv, L, best = awq.awq_search_scales(gpu(W), gpu(X), m, gpu(torch.from_numpy(alphas)), group,
-                                            bits=bits, symmetric=sym)
+                                            bits=bits, symmetric=sym, kept=kept)
     torch.cuda.synchronize()
     s, inv, L, best = s.cpu().numpy(), inv.cpu().numpy(), L.cpu().numpy(), int(best.cpu()[0])
     m_ref = O.act_mean_abs(f32(X))
     assert np.array_equal(m.cpu().numpy().view(np.uint32), m_ref.view(np.uint32))
     model = "fp16" if dtype == F16 else "fp16-scaled-x"
     i_mod, s_mod, inv_mod, L_mod = O.search_scales(f32(W), f32(X), m_ref, alphas, group,
-                                                   operand_model=model, bits=bits, symmetric=sym)
+                                                   operand_model=model, bits=bits, symmetric=sym,
+                                                   keep=keep)
     S = O.candidate_scales(m_ref, alphas)
-    L_ex = O.search_losses(f32(W), f32(X), S, group, bits=bits, symmetric=sym)
+    L_ex = O.search_losses(f32(W), f32(X), S, group, bits=bits, symmetric=sym, keep=keep)
     W64, X64 = f32(W).astype(np.float64), f32(X).astype(np.float64)
     N, K = W64.shape
     for i in range(n_alpha):
         assert abs(L[i] - L_mod[i]) <= SEARCH_MODEL_RTOL * L_mod[i], (i, L[i], L_mod[i])
-        r = O.quantize_layer(f32(W), S[i], group, bits, sym)
+        r = O.quantize_layer(f32(W), S[i], group, bits, sym, keep)
         grid = O.dequantize(r["q"].reshape(N, K // group, group), r["D"],
                             r["z"].astype(np.float32)).reshape(N, K)
-        b, _ = loss_error_bound(W64, X64, O.unscale_activation(grid, S[i]), FP16_U)
+        Wh = O.unscale_activation(grid, S[i])
+        if keep is not None:
+            Wh = np.where(keep[None, :], W64, Wh)
+        b, _ = loss_error_bound(W64, X64, Wh, FP16_U)
         assert abs(L[i] - L_ex[i]) <= b + 1e-6 * L_ex[i], (i, L[i], L_ex[i], b)
+    if n_alpha == 1:
+        assert best == 0
+        return L
     order = np.argsort(L_mod)
     gap = (L_mod[order[1]] - L_mod[order[0]]) / L_mod[order[0]]
     print(f"search N={N} K={K} g={group} bits={bits} sym={sym}: best {i_mod} "
@@ -261,6 +271,7 @@ def _check_search(W, X, dtype, n_alpha=20, group=128, bits=4, sym=False):
     assert best == i_mod
     assert np.array_equal(s.view(np.uint32), s_mod.view(np.uint32))
     assert np.array_equal(inv.view(np.uint32), inv_mod.view(np.uint32))
+    return L
 
 
 def test_search_single_linear_512():
@@ -545,3 +556,42 @@ def test_group_end_to_end(group):
         ref = O.w4a16_matmul(f32(xs[:M]), q.cpu().numpy(), sc.cpu().numpy(), z.cpu().numpy(),
                              inv.cpu().numpy(), group)
         assert rel_max_err(f32(y), ref) <= GEMM_TOL
+
+
+# ------------------------------------------------------------- mixed-precision baseline
+@pytest.mark.parametrize("K,n_keep,ties", [(4096, 41, False), (512, 5, True), (11008, 110, False),
+                                           (128, 0, False), (384, 384, True), (1000, 1, True)])
+def test_salient_channels_bit_exact(K, n_keep, ties):
+    """awq_salient_channels on the GPU's own statistic: the mask equals the
+    oracle's on the same (bit-exact) statistic, ties included (pairs of equal
+    columns)."""
+    x = _act(64, K, F16, seed=K + n_keep)
+    if ties:
+        x[:, 1::2] = x[:, 0::2]
+    m = awq.awq_act_stats(gpu(x))
+    kept = awq.awq_salient_channels(m, n_keep)
+    torch.cuda.synchronize()
+    ref = O.salient_channels(O.act_mean_abs(f32(x)), n_keep)
+    got = kept.cpu().numpy()
+    assert got.max(initial=0) <= 1 and np.array_equal(got.astype(bool), ref)
+
+
+@pytest.mark.parametrize("N,K,T,dtype,group", [(300, 1024, 200, F16, 128), (130, 768, 3000, BF16, 128),
+                                               (256, 1024, 300, F16, 64), (200, 512, 2500, F16, 256)])
+def test_search_with_kept_channels(N, K, T, dtype, group):
+    """The mixed-precision baseline: 1 % of the channels (the most salient)
+    kept in 16-bit, the rest round-to-nearest (alpha = 0), and the search with
+    those channels kept, against the oracle (direct and Gram forms of the
+    loss); keeping them lowers the plain loss on this outlier layer."""
+    W = WL.random_matrix((N, K), torch.float32, seed=N + K, scale=0.02)
+    W[:, ::97] *= 10.0                         # outlier weights on the boosted channels
+    W = W.to(dtype)
+    X = _act(T, K, dtype, seed=T + K)
+    n_keep = max(1, K // 100)
+    keep = O.salient_channels(O.act_mean_abs(f32(X)), n_keep)
+    kept_gpu = awq.awq_salient_channels(awq.awq_act_stats(gpu(X)), n_keep)
+    assert np.array_equal(kept_gpu.cpu().numpy().astype(bool), keep)
+    L_mixed = _check_search(W, X, dtype, group=group, keep=keep, alphas=np.array([0.0]))
+    L_rtn = _check_search(W, X, dtype, group=group, alphas=np.array([0.0]))
+    assert L_mixed[0] < L_rtn[0]
+    _check_search(W, X, dtype, group=group, keep=keep)

@@ -18,7 +18,8 @@ from ._abi import (AWQ_BF16, AWQ_F16, AWQ_F32, AWQ_GROUP, AWQ_OP_ACT_STATS, AWQ_
                    AWQ_OP_QUANTIZE, AWQ_OP_SEARCH, AwqError, lib)
 
 __all__ = ["awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_quantize_codes",
-           "awq_w4a16_gemm", "awq_fold_scales", "awq_workspace_bytes", "AwqError", "lib"]
+           "awq_w4a16_gemm", "awq_fold_scales", "awq_salient_channels", "awq_workspace_bytes",
+           "AwqError", "lib"]
 
 _DT = {torch.float16: AWQ_F16, torch.bfloat16: AWQ_BF16, torch.float32: AWQ_F32}
 
@@ -75,9 +76,10 @@ def awq_search_scales(w: torch.Tensor, x_calib: torch.Tensor, mean_abs: torch.Te
                       s_out: torch.Tensor | None = None, inv_s_out: torch.Tensor | None = None,
                       loss_out: torch.Tensor | None = None, best_idx_out: torch.Tensor | None = None,
                       ws: torch.Tensor | None = None, stream=None, *, bits: int = 4,
-                      symmetric: bool = False):
+                      symmetric: bool = False, kept: torch.Tensor | None = None):
     """Returns (s [K] f32, inv_s [K] f32, losses [n] f64, best index int32 [1]).
-    bits / symmetric select the quantizer's grid (4 / False: awq_quantize_pack's)."""
+    bits / symmetric select the quantizer's grid (4 / False: awq_quantize_pack's);
+    kept (uint8 [K]) marks channels kept in 16-bit (the mixed-precision baseline)."""
     for t, n in ((w, "w"), (x_calib, "x_calib"), (mean_abs, "mean_abs"), (alphas, "alphas")):
         _dev(t, n)
     if not w.is_contiguous() or w.dim() != 2:
@@ -97,8 +99,9 @@ def awq_search_scales(w: torch.Tensor, x_calib: torch.Tensor, mean_abs: torch.Te
     ws, wsb = _workspace(awq_workspace_bytes(AWQ_OP_SEARCH, 0, N, K, T, n_alpha), dev, ws)
     st = lib().awq_search_scales(_ptr(w), _DT.get(w.dtype, -1), N, K, _ptr(x_calib), T, ldx,
                                  _ptr(mean_abs), _ptr(alphas), n_alpha, group_size, bits,
-                                 int(bool(symmetric)), _ptr(s_out), _ptr(inv_s_out), _ptr(loss_out),
-                                 _ptr(best_idx_out), _ptr(ws), wsb, _stream(dev, stream))
+                                 int(bool(symmetric)), _ptr(kept), _ptr(s_out), _ptr(inv_s_out),
+                                 _ptr(loss_out), _ptr(best_idx_out), _ptr(ws), wsb,
+                                 _stream(dev, stream))
     _abi.check("awq_search_scales", st)
     return s_out, inv_s_out, loss_out, best_idx_out
 
@@ -143,6 +146,19 @@ def awq_quantize_codes(w: torch.Tensor, s: torch.Tensor | None = None, group_siz
                                   _stream(dev, stream))
     _abi.check("awq_quantize_codes", st)
     return codes, scales, zeros
+
+
+def awq_salient_channels(mean_abs: torch.Tensor, n_keep: int, kept: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """uint8 [K]: 1 for the n_keep channels of largest mean |x| (ties: lower index)."""
+    _dev(mean_abs, "mean_abs")
+    if mean_abs.dtype != torch.float32 or mean_abs.dim() != 1 or not mean_abs.is_contiguous():
+        raise ValueError("mean_abs must be a contiguous float32 vector")
+    K = mean_abs.numel()
+    kept = torch.empty(K, dtype=torch.uint8, device=mean_abs.device) if kept is None else kept
+    st = lib().awq_salient_channels(_ptr(mean_abs), K, n_keep, _ptr(kept), _stream(mean_abs.device, stream))
+    _abi.check("awq_salient_channels", st)
+    return kept
 
 
 def awq_w4a16_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,

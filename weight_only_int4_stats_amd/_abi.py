@@ -28,7 +28,8 @@ SIGNATURES = {
     "awq_workspace_bytes": (_sz, [_i, _i64, _i64, _i64, _i64, _i]),
     "awq_act_stats": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _sz, _p]),
     "awq_search_scales": (_i, [_p, _i, _i64, _i64, _p, _i64, _i64, _p, _p, _i, _i, _i, _i, _p, _p,
-                               _p, _p, _p, _sz, _p]),
+                               _p, _p, _p, _p, _sz, _p]),
+    "awq_salient_channels": (_i, [_p, _i64, _i64, _p, _p]),
     "awq_quantize_pack": (_i, [_p, _i, _i64, _i64, _p, _i, _p, _p, _p, _p, _p]),
     "awq_quantize_codes": (_i, [_p, _i, _i64, _i64, _p, _i, _i, _i, _p, _p, _p, _p]),
     "awq_w4a16_gemm": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _i64, _i, _p, _p, _i, _i64, _p,

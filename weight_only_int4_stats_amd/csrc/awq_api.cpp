@@ -23,7 +23,7 @@ bool grid_ok(int bits, int symmetric) {
 
 extern "C" {
 
-int awq_abi_version(void) { return 3; }
+int awq_abi_version(void) { return 4; }
 
 const char* awq_status_str(awq_status st) {
   switch (st) {
@@ -65,9 +65,9 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
 awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
                              const void* x_calib, int64_t T, int64_t ldx,
                              const float* mean_abs, const double* alphas, int n_alpha,
-                             int group_size, int bits, int symmetric, float* s_out,
-                             float* inv_s_out, double* loss_out, int32_t* best_idx_out, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             int group_size, int bits, int symmetric, const uint8_t* kept,
+                             float* s_out, float* inv_s_out, double* loss_out,
+                             int32_t* best_idx_out, void* ws, size_t ws_bytes, void* stream) {
   if (!w || !x_calib || !mean_abs || !alphas || !s_out) return AWQ_ERR_NULL;
   if (!is_act_dtype(dt)) return AWQ_ERR_DTYPE;
   if (!group_ok(group_size) || !grid_ok(bits, symmetric)) return AWQ_ERR_UNSUPPORTED;
@@ -76,7 +76,8 @@ awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
   if (N <= 0 || K <= 0 || T <= 0 || ldx < K || K % group_size != 0 || K % 128 != 0)
     return AWQ_ERR_SHAPE;
   if (K > AWQ_MAX_K || N > 0x7FFFFFFF || ldx > AWQ_MAX_LDX_SEARCH) return AWQ_ERR_UNSUPPORTED;
-  if (ldx % 8 != 0 || !aligned16(w) || !aligned16(x_calib) || !aligned16(mean_abs))
+  if (ldx % 8 != 0 || !aligned16(w) || !aligned16(x_calib) || !aligned16(mean_abs) ||
+      (kept && !aligned16(kept)))
     return AWQ_ERR_ALIGN;
   if (!ws || ws_bytes < awq::search_ws_bytes((int)dt, N, K, T, n_alpha) || !aligned256(ws))
     return AWQ_ERR_WORKSPACE;
@@ -85,8 +86,17 @@ awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
   qv.bits = bits;
   qv.sym = symmetric != 0;
   return from_hip(awq::launch_search(w, (int)dt, N, K, x_calib, T, ldx, mean_abs, alphas, n_alpha,
-                                     qv, s_out, inv_s_out, loss_out, best_idx_out, ws,
+                                     qv, kept, s_out, inv_s_out, loss_out, best_idx_out, ws,
                                      (hipStream_t)stream));
+}
+
+awq_status awq_salient_channels(const float* mean_abs, int64_t K, int64_t n_keep, uint8_t* kept,
+                                void* stream) {
+  if (K <= 0 || n_keep < 0 || n_keep > K) return AWQ_ERR_SHAPE;
+  if (!mean_abs || !kept) return AWQ_ERR_NULL;
+  if (K > AWQ_MAX_K) return AWQ_ERR_UNSUPPORTED;
+  if (((uintptr_t)mean_abs & 3u) != 0) return AWQ_ERR_ALIGN;
+  return from_hip(awq::launch_salient_channels(mean_abs, K, n_keep, kept, (hipStream_t)stream));
 }
 
 awq_status awq_quantize_pack(const void* w, awq_dtype dt, int64_t N, int64_t K, const float* s,

@@ -103,7 +103,8 @@ __device__ __forceinline__ GroupGrid group_grid(float mn, float mx, const QSpec 
   GroupGrid g;
   float lo = 0.0f;
   if constexpr (SYM) {
-    g.d = fmaxf(-mn, mx) / q.div;                     // max|w| / 2^(N-1): exact
+    // max|w| / 2^(N-1), exact; 0 when every weight of the group is left out
+    g.d = fmaxf(fmaxf(-mn, mx), 0.0f) / q.div;
   } else {
     lo = fminf(mn, 0.0f);
     const float hi = fmaxf(mx, 0.0f);

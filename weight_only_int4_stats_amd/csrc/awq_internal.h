@@ -33,8 +33,12 @@ hipError_t launch_quantize_codes(const void* w, int dt, int64_t N, int64_t K, co
 size_t search_ws_bytes(int dt, int64_t N, int64_t K, int64_t T, int n_alpha);
 hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void* x, int64_t T,
                          int64_t ldx, const float* mean_abs, const double* alphas, int n_alpha,
-                         QuantVariant qv, float* s_out, float* inv_s_out, double* loss_out,
-                         int32_t* best_out, void* ws, hipStream_t st);
+                         QuantVariant qv, const uint8_t* kept, float* s_out, float* inv_s_out,
+                         double* loss_out, int32_t* best_out, void* ws, hipStream_t st);
+
+// ---- mixed-precision baseline: the n most salient channels (k_salient.hip) ---
+hipError_t launch_salient_channels(const float* mean_abs, int64_t K, int64_t n_keep, uint8_t* kept,
+                                   hipStream_t st);
 
 // Gram form of the search loss (k_gram.hip): Xt [K][Tp] 16-bit, fp32 partial
 // tiles of G (gram_partial_floats), G [K][K] fp64, P [K][2 Kp] fp16 (Kp = K

@@ -52,11 +52,19 @@ __global__ void k_cand_scales(const float* __restrict__ m, const double* __restr
 // constants, any asymmetric one, any symmetric one.
 enum { kGridQ4 = 0, kGridAsym = 1, kGridSym = 2 };
 
-template <int DT, int GL, int GR>
+// KEPT: channels with kept[k] != 0 stay in 16-bit (the mixed-precision
+// baseline): they are left out of the group's min / max and have no error.
+template <int DT, int GL, int GR, bool KEPT>
 __device__ __forceinline__ void err_word(const uint16_t* __restrict__ wrow,
-                                         const float* __restrict__ s, int64_t k0, QSpec q,
+                                         const float* __restrict__ s,
+                                         const uint8_t* __restrict__ kept, int64_t k0, QSpec q,
                                          float e[8]) {
   const u32x4 raw = ldg128(wrow + k0);
+  uint2 kb = {0u, 0u};
+  if constexpr (KEPT) kb = *reinterpret_cast<const uint2*>(kept + k0);
+  auto is_kept = [&](int j) {
+    return KEPT && (((j < 4 ? kb.x : kb.y) >> (8 * (j & 3))) & 0xFFu) != 0u;
+  };
   const f32x4 s0 = *reinterpret_cast<const f32x4*>(s + k0);
   const f32x4 s1 = *reinterpret_cast<const f32x4*>(s + k0 + 4);
   float w[8], sv[8], wp[8];
@@ -69,11 +77,11 @@ __device__ __forceinline__ void err_word(const uint16_t* __restrict__ wrow,
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) wp[j] = w[j] * sv[j];
-  float mn = wp[0], mx = wp[0];
+  float mn = is_kept(0) ? INFINITY : wp[0], mx = is_kept(0) ? -INFINITY : wp[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) {
-    mn = fminf(mn, wp[j]);
-    mx = fmaxf(mx, wp[j]);
+    mn = fminf(mn, is_kept(j) ? INFINITY : wp[j]);
+    mx = fmaxf(mx, is_kept(j) ? -INFINITY : wp[j]);
   }
   seg_minmax<GL>(mn, mx);
   const GroupGrid g = group_grid<GR == kGridSym>(mn, mx, GR == kGridQ4 ? kQ4 : q);
@@ -81,16 +89,18 @@ __device__ __forceinline__ void err_word(const uint16_t* __restrict__ wrow,
   for (int j = 0; j < 8; ++j) {
     const float c = quant_code(wp[j], g);
     const float grid = g.D * (c - g.z);            // exact: fp16 step x small integer
-    e[j] = w[j] - grid / sv[j];
+    e[j] = is_kept(j) ? 0.0f : w[j] - grid / sv[j];
   }
 }
 
 constexpr int kErrKeep = 4;   // packed words per thread kept in registers (K <= 8192)
 
-// GL: threads per quantization group (group / 8); q: the grid, GR its kind.
-template <int DT, int GL, int GR>
+// GL: threads per quantization group (group / 8); q: the grid, GR its kind;
+// KEPT: a mask of channels kept in 16-bit.
+template <int DT, int GL, int GR, bool KEPT>
 __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W, int64_t N,
                                                  int64_t K, const float* __restrict__ s, QSpec q,
+                                                 const uint8_t* __restrict__ kept,
                                                  uint16_t* __restrict__ E, int* __restrict__ pexp) {
   const int64_t n = blockIdx.x;
   const uint16_t* wrow = W + n * K;
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
     for (int i = 0; i < kErrKeep; ++i) {
       const int64_t c = threadIdx.x + 256 * i;
       if (c < wpr) {
-        err_word<DT, GL, GR>(wrow, s, c * 8, q, e[i]);
+        err_word<DT, GL, GR, KEPT>(wrow, s, kept, c * 8, q, e[i]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) emax = fmaxf(emax, fabsf(e[i][j]));
       }
@@ -151,7 +161,7 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
     const int64_t c = c0 + threadIdx.x;
     float e[8];
     if (c < wpr) {
-      err_word<DT, GL, GR>(wrow, s, c * 8, q, e);
+      err_word<DT, GL, GR, KEPT>(wrow, s, kept, c * 8, q, e);
 #pragma unroll
       for (int j = 0; j < 8; ++j) emax = fmaxf(emax, fabsf(e[j]));
     }
@@ -162,7 +172,7 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
     const int64_t c = c0 + threadIdx.x;
     if (c < wpr) {
       float e[8];
-      err_word<DT, GL, GR>(wrow, s, c * 8, q, e);
+      err_word<DT, GL, GR, KEPT>(wrow, s, kept, c * 8, q, e);
       store(c, e, p);
     }
   }
@@ -426,8 +436,8 @@ size_t search_ws_bytes(int dt, int64_t N, int64_t K, int64_t T, int n_alpha) {
 
 hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void* x, int64_t T,
                          int64_t ldx, const float* mean_abs, const double* alphas, int n_alpha,
-                         QuantVariant qv, float* s_out, float* inv_s_out, double* loss_out,
-                         int32_t* best_out, void* ws, hipStream_t st) {
+                         QuantVariant qv, const uint8_t* kept, float* s_out, float* inv_s_out,
+                         double* loss_out, int32_t* best_out, void* ws, hipStream_t st) {
   using namespace awqk;
   const SearchWs sw = carve(ws, dt, N, K, T, n_alpha);
   const int64_t nS = (int64_t)n_alpha * K;
@@ -440,11 +450,13 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
     uint16_t* E = sw.E + (int64_t)c * N * K;
     int* pe = sw.pexp + (int64_t)c * N;
     const uint16_t* W = (const uint16_t*)w;
-#define AWQ_EG2(GL, GR)                                                                             \
+#define AWQ_EG3(GL, GR, KP)                                                                         \
   if (dt == DT_F16)                                                                                 \
-    hipLaunchKernelGGL((k_err_gen<DT_F16, GL, GR>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, q, E, pe); \
+    hipLaunchKernelGGL((k_err_gen<DT_F16, GL, GR, KP>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, q, kept, E, pe); \
   else                                                                                              \
-    hipLaunchKernelGGL((k_err_gen<DT_BF16, GL, GR>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, q, E, pe)
+    hipLaunchKernelGGL((k_err_gen<DT_BF16, GL, GR, KP>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, q, kept, E, pe)
+#define AWQ_EG2(GL, GR) \
+  if (kept) { AWQ_EG3(GL, GR, true); } else { AWQ_EG3(GL, GR, false); }
 #define AWQ_EG(GL)                                                                                  \
   if (q.sym) { AWQ_EG2(GL, kGridSym); }                                                             \
   else if (qv.bits == 4) { AWQ_EG2(GL, kGridQ4); }                                                  \
@@ -452,6 +464,7 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
     if (qv.group == 64) { AWQ_EG(8); }
     else if (qv.group == 256) { AWQ_EG(32); }
     else { AWQ_EG(16); }
+#undef AWQ_EG3
 #undef AWQ_EG2
 #undef AWQ_EG
   };
