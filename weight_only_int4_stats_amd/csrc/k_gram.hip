@@ -274,14 +274,31 @@ __global__ __launch_bounds__(256) void k_gram_loss(const uint16_t* __restrict__ 
   contract_tile<false>(cs, lds0, lds1, lds2, lds3, acc);
 
   // epilogue: lane value v of block (mb, nb): channel k = k0 + wn 128 + nb 32 + lane % 32,
-  // row n = n0 + wm 128 + mb 32 + 8 (v / 4) + 4 (lane / 32) + v % 4
+  // row n = n0 + wm 128 + mb 32 + 8 (v / 4) + 4 (lane / 32) + v % 4.  Per row block mb
+  // the lane's 64 error values are loaded together (64 loads in flight, one
+  // memory latency per row block; rows and channels past the end read 0), then
+  // multiplied in double.
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
+  const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(E + n0 * K), (short)0, (int)(rn * K * 2), kBufferWord3);
   double tot = 0.0;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
+    uint32_t eh[4][16];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int64_t k = k0 + wn * 128 + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int nl = wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const bool ok = k < K && nl < rn;
+        eh[nb][v] = __builtin_amdgcn_raw_buffer_load_b16(
+            ers, ok ? (uint32_t)(((int64_t)nl * K + k) * 2) : kBufferOob, 0, 0);
+      }
+    }
     int pn[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -291,16 +308,12 @@ __global__ __launch_bounds__(256) void k_gram_loss(const uint16_t* __restrict__ 
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int64_t k = k0 + wn * 128 + nb * 32 + (lane & 31);
-      if (k >= K) continue;
-      const int s = sk[k];
+      const int s = sk[k < K ? k : K - 1];
       double part = 0.0;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t n = n0 + wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (n < N) {
-          const double e = (double)f16_to_f32(E[n * K + k]);
-          part += ldexp(e * (double)acc[mb][nb][v], -2 * pn[v]);
-        }
+        const double e = (double)f16_to_f32(eh[nb][v]);     // 0 past the ends
+        part += ldexp(e * (double)acc[mb][nb][v], -2 * pn[v]);
       }
       tot += ldexp(part, s + 1);   // the diagonal blocks were halved
     }
