@@ -235,10 +235,9 @@ __global__ __launch_bounds__(256) void k_gram_loss(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ P,
                                                    const int* __restrict__ sk,
                                                    double* __restrict__ partial, int nc) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[kCStage];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[kCStage];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[kCStage];
-  __shared__ __attribute__((aligned(16))) uint8_t lds3[kCStage];
+  // one array for the four stages, so that the epilogue can use 66.5 KB of it at once
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kCStage];
+  __shared__ __attribute__((aligned(16))) int sks[kCT];
   __shared__ double wsum[kCWaves];
 
   const int64_t gx = (K + kCT - 1) / kCT, gy = (N + kCT - 1) / kCT;
@@ -271,52 +270,69 @@ __global__ __launch_bounds__(256) void k_gram_loss(const uint16_t* __restrict__ 
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-  contract_tile<false>(cs, lds0, lds1, lds2, lds3, acc);
+  contract_tile<false>(cs, lds, lds + kCStage, lds + 2 * kCStage, lds + 3 * kCStage, acc);
 
-  // epilogue: lane value v of block (mb, nb): channel k = k0 + wn 128 + nb 32 + lane % 32,
-  // row n = n0 + wm 128 + mb 32 + 8 (v / 4) + 4 (lane / 32) + v % 4.  Per row block mb
-  // the lane's 64 error values are loaded together (64 loads in flight, one
-  // memory latency per row block; rows and channels past the end read 0), then
-  // multiplied in double.
+  // Epilogue: the tile's sum of E'_nk C_nk 2^(s_k + 1 - 2 p_n) in double (the + 1
+  // undoes the halved diagonal blocks).  Lane value v of accumulator block
+  // (mb, nb) is tile row wm 128 + mb 32 + 8 (v / 4) + 4 (lane / 32) + v % 4,
+  // column wn 128 + nb 32 + lane % 32.  Pass mb writes the 64 tile rows
+  // mb 32 + 0..31 and 128 + mb 32 + 0..31 to LDS as fp32 rows of kEpiLd floats;
+  // thread t then takes pass row t % 64 and the 64 columns 64 (t / 64) + 0..63,
+  // its error values read 16 bytes at a time (past the ends: 0).
+  constexpr int kEpiLd = 260;    // a 16-lane read pass (16 rows) covers all 64 banks
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
+  float* ct = reinterpret_cast<float*>(lds);
+  for (int t = tid; t < kCT; t += 256) sks[t] = k0 + t < K ? sk[k0 + t] : 0;
+  const uint64_t ea = (uint64_t)(uintptr_t)(E + n0 * K);
+  const uint32_t ea_lo = __builtin_amdgcn_readfirstlane((uint32_t)ea);
+  const uint32_t ea_hi = __builtin_amdgcn_readfirstlane((uint32_t)(ea >> 32));
   const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(E + n0 * K), (short)0, (int)(rn * K * 2), kBufferWord3);
+      (void*)(((uint64_t)ea_hi << 32) | ea_lo), (short)0,
+      __builtin_amdgcn_readfirstlane((int)(rn * K * 2)), kBufferWord3);
+  const int q = tid & 63, cg = tid >> 6;
   double tot = 0.0;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    uint32_t eh[4][16];
+    __syncthreads();             // every wave done with the stages / the previous pass
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int64_t k = k0 + wn * 128 + nb * 32 + (lane & 31);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int nl = wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const bool ok = k < K && nl < rn;
-        eh[nb][v] = __builtin_amdgcn_raw_buffer_load_b16(
-            ers, ok ? (uint32_t)(((int64_t)nl * K + k) * 2) : kBufferOob, 0, 0);
-      }
-    }
-    int pn[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t n = n0 + wm * 128 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      pn[v] = pexp[n < N ? n : N - 1];
-    }
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int64_t k = k0 + wn * 128 + nb * 32 + (lane & 31);
-      const int s = sk[k < K ? k : K - 1];
-      double part = 0.0;
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const double e = (double)f16_to_f32(eh[nb][v]);     // 0 past the ends
-        part += ldexp(e * (double)acc[mb][nb][v], -2 * pn[v]);
+        const int r = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        ct[r * kEpiLd + wn * 128 + nb * 32 + (lane & 31)] = acc[mb][nb][v];
       }
-      tot += ldexp(part, s + 1);   // the diagonal blocks were halved
+    __syncthreads();
+    const int nl = (q >> 5) * 128 + mb * 32 + (q & 31);   // tile row of pass row q
+    const int64_t n = n0 + nl;
+    const int pn = pexp[n < N ? n : N - 1];
+    u32x4 e8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = cg * 64 + 8 * j;
+      const bool ok = nl < rn && k0 + c < K;               // K is a multiple of 8
+      e8[j] = __builtin_amdgcn_raw_buffer_load_b128(
+          ers, ok ? (uint32_t)(((int64_t)nl * K + k0 + c) * 2) : kBufferOob, 0, 0);
     }
+    double part = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = cg * 64 + 8 * j;
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(ct + q * kEpiLd + c);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(ct + q * kEpiLd + c + 4);
+      const i32x4 s0 = *reinterpret_cast<const i32x4*>(sks + c);
+      const i32x4 s1 = *reinterpret_cast<const i32x4*>(sks + c + 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float cv = i < 4 ? c0[i] : c1[i - 4];
+        const int sc = i < 4 ? s0[i] : s1[i - 4];
+        const double e = (double)f16_to_f32((e8[j][i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        part += ldexp(e * (double)cv, sc);
+      }
+    }
+    tot += ldexp(part, 1 - 2 * pn);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
