@@ -132,3 +132,77 @@ def test_full_prefill_gemm_sampled_channels():
     err = rel_max_err(f32(y)[:, rows], ref, torch.bfloat16)
     print(f"prefill: rel max err {err:.3e} on {len(rows)} channels x 2048 tokens")
     assert err <= GEMM_TOL
+
+
+@pytest.mark.parametrize("group", [64, 256])
+def test_full_groups_quantize_and_decode(up7b, group):
+    """The full 7B layer quantized with groups of 64 and 256 (bit-exact codes,
+    steps, zero points), then batch-1 and batch-8 products on sampled
+    channels, in the launch configuration of the benchmark."""
+    w, W, X, m_ref = up7b
+    s_ref = O.candidate_scales(m_ref, np.array([6 / 19]))[0]
+    q, sc, z = awq.awq_quantize_pack(gpu(W), gpu(torch.from_numpy(s_ref)), group)
+    torch.cuda.synchronize()
+    r = O.quantize_layer(f32(W), s_ref, group)
+    words = O.pack_codes(r["q"])
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), r["step"].view(np.uint16))
+    assert np.array_equal(z.cpu().numpy(), r["z"])
+    assert np.array_equal(q.cpu().numpy(), words)
+    inv = (np.float32(1) / s_ref).astype(np.float32)
+    rows = _sample_rows(w.N, 53, 3)
+    for M in (1, 8):
+        x = WL.decode_input(w, M)
+        y = awq.awq_w4a16_gemm(gpu(x), q, sc, z, gpu(torch.from_numpy(inv)), group_size=group)
+        torch.cuda.synchronize()
+        ref = O.w4a16_matmul_rows(f32(x), words, r["step"], r["z"], rows, inv, group)
+        err = rel_max_err(f32(y)[:, rows], ref, torch.float16)
+        print(f"group {group} decode M={M}: rel max err {err:.3e}")
+        assert err <= GEMM_TOL
+
+
+@pytest.mark.parametrize("group", [64, 256])
+def test_full_prefill_gemm_groups(group):
+    """M = 2048 bf16 prefill through the 8192 -> 28672 layer with groups of 64
+    and 256, sampled channels."""
+    w = WL.workload(4, "up")
+    g = np.random.Generator(np.random.PCG64(4343 + group))
+    N, K = w.N, w.K
+    words = g.integers(-2 ** 31, 2 ** 31, (N, K // 8), dtype=np.int64).astype(np.int32)
+    step = g.uniform(5e-4, 5e-3, (N, K // group)).astype(np.float16)
+    z = g.integers(0, 16, (N, K // group)).astype(np.uint8)
+    x = WL.prefill_input(w, 2048)
+    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                           gpu(torch.from_numpy(z)), group_size=group)
+    torch.cuda.synchronize()
+    rows = _sample_rows(N, 211, 5)
+    ref = O.w4a16_matmul_rows(f32(x), words, step, z, rows, None, group)
+    err = rel_max_err(f32(y)[:, rows], ref, torch.bfloat16)
+    print(f"group {group} prefill: rel max err {err:.3e} on {len(rows)} channels")
+    assert err <= GEMM_TOL
+
+
+@pytest.mark.parametrize("group,bits,sym,keep", [(64, 4, False, False), (128, 3, True, False),
+                                                 (128, 4, False, True)])
+def test_full_search_variants_row_slice(up7b, group, bits, sym, keep):
+    """Quantizer variants and the mixed-precision baseline at the full token
+    count (65536) on a 64-row slice, against the oracle scored in the
+    operand precision."""
+    w, W, X, m_ref = up7b
+    alphas = WL.alpha_grid(20)[::4].copy()
+    m = gpu(torch.from_numpy(m_ref))
+    kept = O.salient_channels(m_ref, w.K // 100) if keep else None
+    s, inv, L, best = awq.awq_search_scales(
+        gpu(W[:64].contiguous()), gpu(X), m, gpu(torch.from_numpy(alphas)), group, bits=bits,
+        symmetric=sym, kept=None if kept is None else gpu(torch.from_numpy(kept.astype(np.uint8))))
+    torch.cuda.synchronize()
+    i_mod, s_mod, _, L_mod = O.search_scales(f32(W[:64]), f32(X), m_ref, alphas, group,
+                                             operand_model="fp16", bits=bits, symmetric=sym,
+                                             keep=kept)
+    L = L.cpu().numpy()
+    print(f"variant g={group} bits={bits} sym={sym} keep={keep}: "
+          f"max rel loss diff {np.max(np.abs(L - L_mod) / L_mod):.2e}")
+    assert np.all(np.abs(L - L_mod) <= 1e-5 * L_mod)
+    order = np.argsort(L_mod)
+    if (L_mod[order[1]] - L_mod[order[0]]) / L_mod[order[0]] > 2e-5:
+        assert int(best.cpu()[0]) == i_mod
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), s_mod.view(np.uint32))
