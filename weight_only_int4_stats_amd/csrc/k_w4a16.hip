@@ -525,16 +525,16 @@ hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
 // ---------------------------------------------------------------------------
 // Skinny product, one block of 16 waves per compute unit (2 <= M <= 16, the
 // M x K activations in LDS).  The block converts x * r to fp16 once, with an
-// exact power of two per (token, group) from the group's largest |x r| (so
-// every group sits in fp16's normal range) and the eight elements of every
-// packed word in the unpack order.  Block b owns output rows
+// exact power of two per (token, 128-channel unit) from the unit's largest
+// |x r| (so every unit sits in fp16's normal range) and the eight elements of
+// every packed word in the unpack order.  Block b owns output rows
 // [b N / B, (b + 1) N / B), cut into 16-row tiles; with t tiles each tile's
-// groups are split into S = 16 / t slices and wave w takes the items
-// (tile, slice) w, w + 16, ...  Per group a lane loads one 128-bit chunk of
-// its row plus the step and zero point, reads the matching activations from
-// LDS, runs the group's four MFMAs into a fresh 16 x 16 tile and adds it with
-// the group's activation scale 2^-p.  Slices of a tile are added in LDS in a
-// fixed order.
+// units are split into S = 16 / t slices and wave w takes the items
+// (tile, slice) w, w + 16, ...  Per unit a lane loads one 128-bit chunk of
+// its row plus the step and zero point of the chunk's weight group, reads the
+// matching activations from LDS, runs the unit's four MFMAs into a fresh
+// 16 x 16 tile and adds it with the unit's activation scale 2^-p.  Slices of
+// a tile are added in LDS in a fixed order.
 // ---------------------------------------------------------------------------
 constexpr int kScWaves = 16;
 constexpr size_t kScRedBytes = (size_t)kScWaves * 256 * 4;      // per-item 16 x 16 partial tiles
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_cu(
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- stage fp16(x r 2^p) in unpack order (0,4,2,6,1,5,3,7) with p per
-  // (token, group): the group's 16 pieces sit in 16 consecutive lanes
+  // (token, 128-channel unit): the unit's 16 pieces sit in 16 consecutive lanes
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const uint32_t j = (uint32_t)i;
