@@ -595,3 +595,21 @@ def test_search_with_kept_channels(N, K, T, dtype, group):
     L_rtn = _check_search(W, X, dtype, group=group, alphas=np.array([0.0]))
     assert L_mixed[0] < L_rtn[0]
     _check_search(W, X, dtype, group=group, keep=keep)
+
+
+@pytest.mark.parametrize("ydt", [F16, BF16, torch.float32])
+def test_gemm_strided_output_ragged_tail(ydt):
+    """Tiled GEMM into a strided output (row pitch 1024, N = 1001): the
+    16-byte stores of whole row pieces, the element stores of the last
+    partial piece, and the padding left untouched."""
+    M, N, K = 70, 1001, 1024
+    words, step, z = _random_packed_g(N, K, 991, 128)
+    x = _act(M, K, F16, 17)
+    big = torch.full((M, 1024), 7.0, dtype=ydt, device="cuda")
+    y = big[:, :N]
+    awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                       gpu(torch.from_numpy(z)), y=y)
+    torch.cuda.synchronize()
+    ref = O.w4a16_matmul(f32(x), words, step, z)
+    assert rel_max_err(f32(y.cpu()), ref, ydt) <= GEMM_TOL
+    assert torch.all(big[:, N:] == 7.0).item()

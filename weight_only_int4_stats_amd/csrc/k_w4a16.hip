@@ -165,7 +165,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
                                              const uint32_t* __restrict__ qw,
                                              const uint32_t* __restrict__ ctab,
                                              const int* __restrict__ en, int64_t N,
-                                             void* __restrict__ y, int64_t ldy, int glog) {
+                                             void* __restrict__ y, int64_t ldy, int glog, int vec_ok) {
   // three LDS arrays, the loop unrolled by three: each stage is a known array
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kStage];
@@ -331,19 +331,84 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
     if (s + 2 < S) stage(s + 2, lds2, lds0, lds1);
   }
 
-  // 16x16 accumulator layout: column = lane % 16, row = 4 (lane / 16) + v
+  // 16x16 accumulator layout: column = lane % 16, row = 4 (lane / 16) + v.
+  // Each wave stages its 128 x 64 outputs through a private LDS area, 32 rows
+  // at a time, and stores whole 128-byte (fp32: 256-byte) row pieces with
+  // 16-byte stores; the row pitch is padded so that the writes of the four
+  // lane groups (rows 4 apart) and the 16-lane read passes hit distinct banks.
+  // Unaligned outputs, and columns of a ragged last tile, are stored one by one.
+  constexpr int kEs = YDT == DT_F32 ? 4 : 2;              // output bytes
+  constexpr int kRowB = 64 * kEs;                         // bytes of a 64-column row piece
+  constexpr int kLd = kRowB + (YDT == DT_F32 ? 16 : 16);  // padded LDS pitch
+  constexpr int kLpr = kRowB / 16;                        // lanes per row (8 or 16)
+  constexpr int kRpi = 64 / kLpr;                         // rows per read pass (8 or 4)
+  static_assert(4 * 32 * kLd <= kStage, "four waves' staging in one stage array");
+  int en_l[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t n = n0 + wn * 64 + nb * 16 + (lane & 15);
-    if (n >= N) continue;
-    const int e = en[n];
+    en_l[nb] = n < N ? en[n] : 0;
+  }
+  if (!vec_ok) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int nb = 0; nb < 4; ++nb) {
+      const int64_t n = n0 + wn * 64 + nb * 16 + (lane & 15);
+      if (n >= N) continue;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t m = m0 + wm * 128 + mb * 16 + 4 * (lane >> 4) + v;
+          if (m < M) store_y<YDT>(y, m * ldy + n, ldexpf(acc[mb][nb][v], -(pm[m] + en_l[nb])));
+        }
+    }
+    return;
+  }
+  __syncthreads();                                        // every wave done with the stages
+  uint8_t* stg = (wv < 4 ? lds0 : lds1) + (wv & 3) * 32 * kLd;
+#pragma unroll
+  for (int hp = 0; hp < 4; ++hp) {                        // rows wm 128 + hp 32 + 0..31
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mb = 2 * hp + h;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
+        const int r = h * 16 + 4 * (lane >> 4) + v;       // staging row
         const int64_t m = m0 + wm * 128 + mb * 16 + 4 * (lane >> 4) + v;
-        if (m < M) store_y<YDT>(y, m * ldy + n, ldexpf(acc[mb][nb][v], -(pm[m] + e)));
+        const int pmm = m < M ? pm[m] : 0;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const float o = ldexpf(acc[mb][nb][v], -(pmm + en_l[nb]));
+          uint8_t* dst = stg + r * kLd + (nb * 16 + (lane & 15)) * kEs;
+          if constexpr (YDT == DT_F32) *reinterpret_cast<float*>(dst) = o;
+          else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)from_f32<YDT>(o);
+        }
       }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0): the wave's writes landed
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 32 / kRpi; ++i) {
+      const int r = i * kRpi + lane / kLpr;
+      const int cb = (lane % kLpr) * 16;                  // byte offset in the row piece
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stg + r * kLd + cb);
+      const int64_t m = m0 + wm * 128 + hp * 32 + r;
+      const int64_t n = n0 + wn * 64 + cb / kEs;
+      if (m < M) {
+        uint8_t* out = reinterpret_cast<uint8_t*>(y) + (m * ldy + n) * kEs;
+        if (n + 16 / kEs <= N) {
+          *reinterpret_cast<u32x4*>(out) = val;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16 / kEs; ++j)
+            if (n + j < N) {
+              if constexpr (YDT == DT_F32) reinterpret_cast<uint32_t*>(out)[j] = val[j];
+              else reinterpret_cast<uint16_t*>(out)[j] = (uint16_t)(val[j >> 1] >> (16 * (j & 1)));
+            }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -517,8 +582,11 @@ hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
                      r, w.xq, w.pm);
   hipLaunchKernelGGL(k_gemm_consts, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st, scales, zeros, N,
                      K >> glog, w.en, w.ctab);
+  // 16-byte output stores need a 16-byte aligned y and row pitch
+  const int es = YDT == DT_F32 ? 4 : 2;
+  const int vec_ok = ((uintptr_t)y % 16 == 0) && ((ldy * es) % 16 == 0);
   hipLaunchKernelGGL((k_gemm<YDT>), dim3((unsigned)gemm_blocks(M, N)), dim3(512), 0, st, w.xq, M, K, w.pm,
-                     qw, w.ctab, w.en, N, y, ldy, glog);
+                     qw, w.ctab, w.en, N, y, ldy, glog, vec_ok);
   return hipGetLastError();
 }
 
