@@ -613,3 +613,17 @@ def test_gemm_strided_output_ragged_tail(ydt):
     ref = O.w4a16_matmul(f32(x), words, step, z)
     assert rel_max_err(f32(y.cpu()), ref, ydt) <= GEMM_TOL
     assert torch.all(big[:, N:] == 7.0).item()
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (1, 3), (2, 5), (17, 2), (40, 65)])
+def test_product_single_group_64(M, N):
+    """K = 64 with groups of 64: one group per row; the tiled GEMM then runs a
+    single 64-channel stage, and tiny N leaves most of a tile empty."""
+    K, group = 64, 64
+    words, step, z = _random_packed_g(N, K, 500 + M * 10 + N, group)
+    x = _act(M, K, F16, 9 + M)
+    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                           gpu(torch.from_numpy(z)), out_dtype=torch.float32, group_size=group)
+    torch.cuda.synchronize()
+    ref = O.w4a16_matmul(f32(x), words, step, z, None, group)
+    assert rel_max_err(f32(y), ref) <= GEMM_TOL
