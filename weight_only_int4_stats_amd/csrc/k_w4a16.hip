@@ -664,7 +664,9 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_cu(
     const uint32_t k8 = K8 <= 1024u ? k80 : k80 + 1024u * (j / (uint32_t)M);
     if (live) {
       sx[i] = ldg128(x + (int64_t)m * ldx + (int64_t)k8 * 8);
-      if constexpr (HAS_R) {
+      // with K / 8 <= 1024 every piece of the thread has the same k8, so 1/s is
+      // read once (piece 0) and reused
+      if (HAS_R && (K8 > 1024u || i == 0)) {
         sr0[i] = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8);
         sr1[i] = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8 + 4);
       }
@@ -731,8 +733,9 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_cu(
     if constexpr (HAS_R) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        v[q] *= live ? sr0[i][q] : 0.0f;
-        v[4 + q] *= live ? sr1[i][q] : 0.0f;
+        const int ir = K8 <= 1024u ? 0 : i;
+        v[q] *= live ? sr0[ir][q] : 0.0f;
+        v[4 + q] *= live ? sr1[ir][q] : 0.0f;
       }
     }
     float amax = 0.0f;
