@@ -4,10 +4,10 @@
 // activation magnitude over a calibration set).
 //
 // The column sums are exact.  Each |x| is taken in fixed point with LSB 2^-24
-// (floor(|x| * 2^24), exact for every fp16 value), accumulated per thread in
-// double (exact while the sum stays below 2^53 LSBs), combined across the
-// block in double (still exact), and added across blocks with 64-bit integer
-// atomics (exact and order-free).  The finalisation divides once in double
+// (floor(|x| * 2^24), exact for every fp16 value), built from the 16-bit
+// pattern with integer operations (the significand shifted by the exponent),
+// accumulated per thread and across the block in 64-bit integers, and added
+// across blocks with 64-bit integer atomics (exact and order-free).  The finalisation divides once in double
 // and rounds once to float, so the result does not depend on the grid.
 //
 // Layout: X is [T][ldx] row-major.  A thread owns 8 consecutive columns (one
@@ -27,16 +27,29 @@ __global__ void k_fill_u64(unsigned long long* p, int64_t n) {
   if (i < n) p[i] = 0ull;
 }
 
+// floor(|x| 2^24) of one 16-bit value, as an integer.  fp16: a subnormal is
+// m 2^-24 -> m; a normal (1024 + m) 2^(e - 25) -> (1024 + m) 2^(e - 1).  bf16:
+// (128 + m) 2^(e - 134) -> (128 + m) 2^(e - 110), shifted right (the floor)
+// below 2^24 and 0 for subnormals.  Shifts are capped at 40: values that large
+// already break the statistic's range (sum below 2^29).
 template <int DT>
-__device__ __forceinline__ void accum_word(uint32_t w, double& a, double& b) {
-  float lo = fabsf(lo_f32<DT>(w)) * 16777216.0f;   // exact scaling by 2^24
-  float hi = fabsf(hi_f32<DT>(w)) * 16777216.0f;
-  if constexpr (DT == DT_BF16) {                   // bf16 can hold bits below 2^-24
-    lo = floorf(lo);
-    hi = floorf(hi);
+__device__ __forceinline__ uint64_t fixed24(uint32_t h) {
+  if constexpr (DT == DT_F16) {
+    const uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+    return e ? (uint64_t)(1024u | m) << (e - 1) : (uint64_t)m;
+  } else {
+    const int e = (int)((h >> 7) & 0xFFu);
+    const uint32_t m = (h & 0x7Fu) | 0x80u;
+    const int sh = e - 110;
+    if (e == 0 || sh <= -8) return 0;
+    return sh >= 0 ? (uint64_t)m << (sh < 40 ? sh : 40) : (uint64_t)(m >> -sh);
   }
-  a += (double)lo;
-  b += (double)hi;
+}
+
+template <int DT>
+__device__ __forceinline__ void accum_word(uint32_t w, uint64_t& a, uint64_t& b) {
+  a += fixed24<DT>(w & 0xFFFFu);
+  b += fixed24<DT>(w >> 16);
 }
 
 template <int DT>
@@ -49,9 +62,9 @@ __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __r
   const int64_t col = (int64_t)blockIdx.x * kStatsCols + lane * 8;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r1 = min(T, r0 + rows_per_block);
-  double s[8];
+  uint64_t s[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) s[j] = 0.0;
+  for (int j = 0; j < 8; ++j) s[j] = 0;
 
   if (col < K) {
     const uint16_t* base = x + col;
@@ -78,15 +91,15 @@ __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __r
     }
   }
 
-  __shared__ double red[4][8][64];
+  __shared__ uint64_t red[4][8][64];
 #pragma unroll
   for (int j = 0; j < 8; ++j) red[wv][j][lane] = s[j];
   __syncthreads();
   if (wv == 0 && col < K) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const double t = red[0][j][lane] + red[1][j][lane] + red[2][j][lane] + red[3][j][lane];
-      if (t != 0.0) atomicAdd(&acc[col + j], (unsigned long long)t);
+      const uint64_t t = red[0][j][lane] + red[1][j][lane] + red[2][j][lane] + red[3][j][lane];
+      if (t != 0) atomicAdd(&acc[col + j], (unsigned long long)t);
     }
   }
 }
