@@ -55,12 +55,20 @@ __device__ __forceinline__ void accum_word(uint32_t w, uint64_t& a, uint64_t& b)
 template <int DT>
 __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __restrict__ x,
                                                              int64_t T, int64_t K, int64_t ldx,
-                                                             int64_t rows_per_block,
+                                                             int64_t rows_per_block, int64_t slabs,
+                                                             int64_t chunks,
                                                              unsigned long long* __restrict__ acc) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int64_t col = (int64_t)blockIdx.x * kStatsCols + lane * 8;
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+  // Block i runs on L2 slice i mod 8; slice x takes chunks x, x + 8, ... with
+  // all column slabs of a chunk back to back, so each slice reads whole rows.
+  const int64_t bi = blockIdx.x;
+  const int64_t xs = bi % 8, slot = bi / 8;
+  const int64_t slab = slot % slabs;
+  const int64_t chunk = (slot / slabs) * 8 + xs;
+  if (chunk >= chunks) return;
+  const int64_t col = slab * kStatsCols + lane * 8;
+  const int64_t r0 = chunk * rows_per_block;
   const int64_t r1 = min(T, r0 + rows_per_block);
   uint64_t s[8];
 #pragma unroll
@@ -135,13 +143,14 @@ hipError_t launch_act_stats(const void* x, int dt, int64_t T, int64_t K, int64_t
   int64_t rpb = (T + chunks - 1) / chunks;
   rpb = (rpb + quantum - 1) / quantum * quantum;
   chunks = (T + rpb - 1) / rpb;
-  dim3 grid((unsigned)slabs, (unsigned)chunks);
+  // chunks rounded up to a multiple of 8 slices; blocks past the last chunk exit
+  const dim3 grid((unsigned)(slabs * ((chunks + 7) / 8) * 8));
   if (dt == DT_F16)
     hipLaunchKernelGGL(k_act_accum<DT_F16>, grid, dim3(kStatsThreads), 0, st,
-                       (const uint16_t*)x, T, K, ldx, rpb, acc);
+                       (const uint16_t*)x, T, K, ldx, rpb, slabs, chunks, acc);
   else
     hipLaunchKernelGGL(k_act_accum<DT_BF16>, grid, dim3(kStatsThreads), 0, st,
-                       (const uint16_t*)x, T, K, ldx, rpb, acc);
+                       (const uint16_t*)x, T, K, ldx, rpb, slabs, chunks, acc);
   hipLaunchKernelGGL(k_act_finalize, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, acc, K,
                      T, mean_abs);
   return hipGetLastError();
