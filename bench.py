@@ -189,9 +189,13 @@ def main() -> int:
     torch.cuda.synchronize()
 
     names = ["act_stats", "search", "quantize", "gemv_m1", "gemv_m8", "gemm_prefill"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
 
-    def step():
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+
+    ev = new_events()
+
+    def step(ev):
         ev[0].record(stream)
         awq.awq_act_stats(XA, m, ws=ws_stats)
         ev[1].record(stream)
@@ -208,17 +212,21 @@ def main() -> int:
         ev[6].record(stream)
 
     for _ in range(args.warmup):
-        step()
+        step(ev)
     torch.cuda.synchronize()
+    # the K steps are enqueued back to back (the host runs ahead of the GPU, so
+    # the events time GPU work, not the host's enqueue latency) and bracketed
+    # by one synchronization on each side
+    evs = [new_events() for _ in range(args.steps)]
     per = {n: 0.0 for n in names}
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-        torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            per[n] += ev[i].elapsed_time(ev[i + 1])
-    wall = time.perf_counter() - t0
+    for k in range(args.steps):
+        step(evs[k])
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for e in evs:
+        for i, n in enumerate(names):
+            per[n] += e[i].elapsed_time(e[i + 1])
     K_ = args.steps
     avg = {n: per[n] / K_ for n in names}            # ms per step per phase
     ms_step = wall * 1000.0 / K_
