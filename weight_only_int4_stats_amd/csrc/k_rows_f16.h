@@ -20,11 +20,9 @@ constexpr int kRowsKeep = 8;   // 8-element chunks per thread kept in registers 
 // PERMUTE each 8-element chunk is stored as (k0,k4,k2,k6,k1,k5,k3,k7), the
 // order in which the packed-nibble unpack yields weight pairs.
 template <int DT, bool HAS_R, bool PERMUTE>
-__global__ __launch_bounds__(256) void k_rows_f16(const uint16_t* __restrict__ src, int64_t K,
-                                                  int64_t ld, const float* __restrict__ r,
-                                                  uint16_t* __restrict__ dst,
-                                                  int* __restrict__ pexp) {
-  const int64_t row = blockIdx.x;
+__device__ __forceinline__ void rows_f16_block(int64_t row, const uint16_t* __restrict__ src, int64_t K,
+                                               int64_t ld, const float* __restrict__ r,
+                                               uint16_t* __restrict__ dst, int* __restrict__ pexp) {
   const uint16_t* s = src + row * ld;
   const int64_t nch = K >> 3;
   auto load8 = [&](int64_t c, float v[8]) {
@@ -105,4 +103,12 @@ __global__ __launch_bounds__(256) void k_rows_f16(const uint16_t* __restrict__ s
     store8(c, v, p);
   }
 }
+template <int DT, bool HAS_R, bool PERMUTE>
+__global__ __launch_bounds__(256) void k_rows_f16(const uint16_t* __restrict__ src, int64_t K,
+                                                  int64_t ld, const float* __restrict__ r,
+                                                  uint16_t* __restrict__ dst,
+                                                  int* __restrict__ pexp) {
+  rows_f16_block<DT, HAS_R, PERMUTE>(blockIdx.x, src, K, ld, r, dst, pexp);
+}
+
 }  // namespace awqk

@@ -15,7 +15,7 @@
 // * k_gemm (M > 16): fp16 matrix-core GEMM on 256x256 output tiles.  A
 //   pre-pass rounds each activation row x * r, scaled by an exact power of
 //   two, to fp16 (exact for bf16 input without 1/s) in the order the nibble
-//   unpack produces; a second pre-pass picks a power of two per weight row so
+//   unpack produces; the same launch picks a power of two per weight row so
 //   that step * 15 stays inside fp16.  Each lane dequantizes its packed word
 //   to step * (q - z) rounded once to fp16 and feeds v_mfma_f32_16x16x32_f16;
 //   the epilogue undoes both powers of two exactly.
@@ -40,10 +40,10 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
 // fp16; then, for every group g, the fp16 constants of the packed-fma
 // dequantization, group-major so a block's columns are contiguous:
 //   ctab[g][n] = (fp16(D' 2^24) | fp16(D' 2^20) << 16, fp16(-D' z) twice).
-__global__ __launch_bounds__(256) void k_gemm_consts(const uint16_t* __restrict__ scales,
-                                                     const uint8_t* __restrict__ zeros, int64_t N,
-                                                     int64_t G, int* __restrict__ en,
-                                                     uint32_t* __restrict__ ctab) {
+__device__ __forceinline__ void gemm_consts_block(int64_t bid, const uint16_t* __restrict__ scales,
+                                                  const uint8_t* __restrict__ zeros, int64_t N,
+                                                  int64_t G, int* __restrict__ en,
+                                                  uint32_t* __restrict__ ctab) {
   // A block takes 64 rows; 64 groups at a time are staged in LDS (reads along
   // the groups, all issued together).  Thread r < 64 takes row r's maximum
   // from LDS; the constants are written with the rows fastest, so that every
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void k_gemm_consts(const uint16_t* __restrict_
   __shared__ uint8_t zero_s[64][65];
   __shared__ int e_s[64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  const int64_t n0 = bid * 64;
   const int rows = (int)(N - n0 < 64 ? N - n0 : 64);
   auto stage = [&](int64_t g0, int gc) {
 #pragma unroll
@@ -145,6 +145,19 @@ __device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 c24, f16x2 c
 // ordered for the chip's eight L2 slices: block i runs on slice i mod 8, and
 // slice x takes the x-th eighth of the tiles in a grouped order (4 m-tiles,
 // m fastest, then n), so its ~32 concurrent blocks cover about 4 x 8 tiles.
+// The GEMM's two pre-passes in one launch (they are independent): blocks
+// 0 .. M - 1 convert activation rows, the rest build the constants.
+template <int DT, bool HAS_R>
+__global__ __launch_bounds__(256) void k_gemm_prep(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                   int64_t ldx, const float* __restrict__ r,
+                                                   uint16_t* __restrict__ xq, int* __restrict__ pm,
+                                                   const uint16_t* __restrict__ scales,
+                                                   const uint8_t* __restrict__ zeros, int64_t N, int64_t G,
+                                                   int* __restrict__ en, uint32_t* __restrict__ ctab) {
+  if ((int64_t)blockIdx.x < M) rows_f16_block<DT, HAS_R, true>(blockIdx.x, x, K, ldx, r, xq, pm);
+  else gemm_consts_block((int64_t)blockIdx.x - M, scales, zeros, N, G, en, ctab);
+}
+
 constexpr int kMT = 256;                // tile rows (m)
 constexpr int kNT = 256;                // tile columns (n)
 constexpr int kBK = 64;                 // k per stage
@@ -578,10 +591,8 @@ hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
                          const uint16_t* scales, const uint8_t* zeros, int64_t N, int glog,
                          const float* r, void* y, int64_t ldy, void* ws, hipStream_t st) {
   const GemmWs w = gemm_ws(ws, M, N, K, 1 << glog);
-  hipLaunchKernelGGL((k_rows_f16<DT, HAS_R, true>), dim3((unsigned)M), dim3(256), 0, st, x, K, ldx,
-                     r, w.xq, w.pm);
-  hipLaunchKernelGGL(k_gemm_consts, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st, scales, zeros, N,
-                     K >> glog, w.en, w.ctab);
+  hipLaunchKernelGGL((k_gemm_prep<DT, HAS_R>), dim3((unsigned)(M + (N + 63) / 64)), dim3(256), 0, st, x, M, K,
+                     ldx, r, w.xq, w.pm, scales, zeros, N, K >> glog, w.en, w.ctab);
   // 16-byte output stores need a 16-byte aligned y and row pitch
   const int es = YDT == DT_F32 ? 4 : 2;
   const int vec_ok = ((uintptr_t)y % 16 == 0) && ((ldy * es) % 16 == 0);
