@@ -290,7 +290,9 @@ def search_losses_operand_model(W: np.ndarray, X: np.ndarray, S: np.ndarray,
     floating point -- is taken in the precision that evaluation uses.
 
     READING (the pages fix no precision for the search): the error of each
-    weight is formed in float32 as E = W - fp32(fp32(D (q - z)) / s); each row
+    weight is formed in float32 as E = W - fp32(fp32(D (q - z)) * r) with
+    r = fp32(1 / s), the product with diag(s)^-1 as "AWQ Math" writes it
+    ("The equivalent transform") and as the fused product applies it; each row
     of E is scaled by an exact power of two 2^p (row max below 2^14) and
     rounded to float16; calibration tokens that are not float16 already
     (bfloat16 input) get the same treatment per token; the products and sums
@@ -313,7 +315,8 @@ def search_losses_operand_model(W: np.ndarray, X: np.ndarray, S: np.ndarray,
         Dk = np.repeat(r["D"], group, axis=1)                       # float32 [N, K]
         zk = np.repeat(r["z"].astype(np.float32), group, axis=1)
         grid = Dk * (r["q"].astype(np.float32) - zk)                # exact in float32
-        E32 = W - grid / s[None, :]                                 # float32 division, subtraction
+        r = (np.float32(1) / s).astype(np.float32)                  # fp32(1 / s), IEEE division
+        E32 = W - grid * r[None, :]                                 # float32 product, subtraction
         if keep is not None:
             E32 = np.where(np.asarray(keep, dtype=bool)[None, :], np.float32(0), E32)
         Eh, pe = _round_rows_fp16(E32)

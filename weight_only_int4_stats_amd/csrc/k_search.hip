@@ -9,8 +9,9 @@
 // the matrix cores.  Three steps per candidate:
 //   1. k_err_gen    one block per row: the row's groups are quantized exactly
 //                   as awq_quantize_pack (the 4-bit asymmetric grid) or
-//                   awq_quantize_codes (any grid) do, E = W - D (q - z) / s
-//                   in float;
+//                   awq_quantize_codes (any grid) do, E = W - D (q - z) r in
+//                   float with r = fp32(1 / s) (diag(s)^-1, computed once per
+//                   candidate and channel);
 //                   the row's max|E| fixes p (so the row fits fp16's normal
 //                   range), then E * 2^p is written as fp16 into the
 //                   workspace, with p per row (the errors stay in registers
@@ -36,13 +37,15 @@ namespace awqk {
 // candidate scales: S[i][j] = float(pow(max(double(m_j), 2^-14), alpha_i))
 // ---------------------------------------------------------------------------
 __global__ void k_cand_scales(const float* __restrict__ m, const double* __restrict__ alphas,
-                              int n_alpha, int64_t K, float* __restrict__ S) {
+                              int n_alpha, int64_t K, float* __restrict__ S, float* __restrict__ IS) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)n_alpha * K) return;
   const int64_t i = idx / K;
   const int64_t j = idx - i * K;
   const double b = fmax((double)m[j], 0x1p-14);
-  S[idx] = (float)pow(b, alphas[i]);
+  const float sv = (float)pow(b, alphas[i]);
+  S[idx] = sv;
+  IS[idx] = 1.0f / sv;                           // IEEE division, once per candidate and channel
 }
 
 // ---------------------------------------------------------------------------
@@ -56,7 +59,7 @@ enum { kGridQ4 = 0, kGridAsym = 1, kGridSym = 2 };
 // baseline): they are left out of the group's min / max and have no error.
 template <int DT, int GL, int GR, bool KEPT>
 __device__ __forceinline__ void err_word(const uint16_t* __restrict__ wrow,
-                                         const float* __restrict__ s,
+                                         const float* __restrict__ s, const float* __restrict__ is,
                                          const uint8_t* __restrict__ kept, int64_t k0, QSpec q,
                                          float e[8]) {
   const u32x4 raw = ldg128(wrow + k0);
@@ -67,13 +70,17 @@ __device__ __forceinline__ void err_word(const uint16_t* __restrict__ wrow,
   };
   const f32x4 s0 = *reinterpret_cast<const f32x4*>(s + k0);
   const f32x4 s1 = *reinterpret_cast<const f32x4*>(s + k0 + 4);
-  float w[8], sv[8], wp[8];
+  const f32x4 r0 = *reinterpret_cast<const f32x4*>(is + k0);
+  const f32x4 r1 = *reinterpret_cast<const f32x4*>(is + k0 + 4);
+  float w[8], sv[8], rv[8], wp[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     w[2 * j] = lo_f32<DT>(raw[j]);
     w[2 * j + 1] = hi_f32<DT>(raw[j]);
     sv[j] = s0[j];
     sv[4 + j] = s1[j];
+    rv[j] = r0[j];
+    rv[4 + j] = r1[j];
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) wp[j] = w[j] * sv[j];
@@ -89,7 +96,7 @@ __device__ __forceinline__ void err_word(const uint16_t* __restrict__ wrow,
   for (int j = 0; j < 8; ++j) {
     const float c = quant_code(wp[j], g);
     const float grid = g.D * (c - g.z);            // exact: fp16 step x small integer
-    e[j] = is_kept(j) ? 0.0f : w[j] - grid / sv[j];
+    e[j] = is_kept(j) ? 0.0f : w[j] - grid * rv[j];  // times fp32(1 / s): diag(s)^-1
   }
 }
 
@@ -99,7 +106,8 @@ constexpr int kErrKeep = 4;   // packed words per thread kept in registers (K <=
 // KEPT: a mask of channels kept in 16-bit.
 template <int DT, int GL, int GR, bool KEPT>
 __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W, int64_t N,
-                                                 int64_t K, const float* __restrict__ s, QSpec q,
+                                                 int64_t K, const float* __restrict__ s,
+                                                 const float* __restrict__ is, QSpec q,
                                                  const uint8_t* __restrict__ kept,
                                                  uint16_t* __restrict__ E, int* __restrict__ pexp) {
   const int64_t n = blockIdx.x;
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
     for (int i = 0; i < kErrKeep; ++i) {
       const int64_t c = threadIdx.x + 256 * i;
       if (c < wpr) {
-        err_word<DT, GL, GR, KEPT>(wrow, s, kept, c * 8, q, e[i]);
+        err_word<DT, GL, GR, KEPT>(wrow, s, is, kept, c * 8, q, e[i]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) emax = fmaxf(emax, fabsf(e[i][j]));
       }
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
     const int64_t c = c0 + threadIdx.x;
     float e[8];
     if (c < wpr) {
-      err_word<DT, GL, GR, KEPT>(wrow, s, kept, c * 8, q, e);
+      err_word<DT, GL, GR, KEPT>(wrow, s, is, kept, c * 8, q, e);
 #pragma unroll
       for (int j = 0; j < 8; ++j) emax = fmaxf(emax, fabsf(e[j]));
     }
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
     const int64_t c = c0 + threadIdx.x;
     if (c < wpr) {
       float e[8];
-      err_word<DT, GL, GR, KEPT>(wrow, s, kept, c * 8, q, e);
+      err_word<DT, GL, GR, KEPT>(wrow, s, is, kept, c * 8, q, e);
       store(c, e, p);
     }
   }
@@ -377,6 +385,7 @@ bool search_uses_gram(int64_t N, int64_t K, int64_t T, int n_alpha) {
 
 struct SearchWs {
   float* S;
+  float* IS;        // fp32(1 / S)
   int* pexp;
   uint16_t* E;
   double* partial;
@@ -405,6 +414,7 @@ SearchWs carve(void* ws, int dt, int64_t N, int64_t K, int64_t T, int n_alpha) {
   w.gram = search_uses_gram(N, K, T, n_alpha);
   w.nc = w.gram ? (n_alpha < kGramBatch ? n_alpha : kGramBatch) : 1;
   w.S = (float*)take((size_t)n_alpha * K * 4);
+  w.IS = (float*)take((size_t)n_alpha * K * 4);
   w.pexp = (int*)take((size_t)w.nc * N * 4);
   w.E = (uint16_t*)take((size_t)w.nc * N * K * 2);
   w.losses = (double*)take((size_t)n_alpha * 8);
@@ -442,19 +452,21 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
   const SearchWs sw = carve(ws, dt, N, K, T, n_alpha);
   const int64_t nS = (int64_t)n_alpha * K;
   hipLaunchKernelGGL(k_cand_scales, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, mean_abs,
-                     alphas, n_alpha, K, sw.S);
+                     alphas, n_alpha, K, sw.S, sw.IS);
   const double tn = (double)T * (double)N;
   // error rows of candidate i into slot c of the workspace
   const QSpec q = qspec(qv.bits, qv.sym);
-  auto err_gen = [&](const float* s_i, int c) {
+  auto err_gen = [&](int cand, int c) {
+    const float* s_i = sw.S + (int64_t)cand * K;
+    const float* is_i = sw.IS + (int64_t)cand * K;
     uint16_t* E = sw.E + (int64_t)c * N * K;
     int* pe = sw.pexp + (int64_t)c * N;
     const uint16_t* W = (const uint16_t*)w;
 #define AWQ_EG3(GL, GR, KP)                                                                         \
   if (dt == DT_F16)                                                                                 \
-    hipLaunchKernelGGL((k_err_gen<DT_F16, GL, GR, KP>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, q, kept, E, pe); \
+    hipLaunchKernelGGL((k_err_gen<DT_F16, GL, GR, KP>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, is_i, q, kept, E, pe); \
   else                                                                                              \
-    hipLaunchKernelGGL((k_err_gen<DT_BF16, GL, GR, KP>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, q, kept, E, pe)
+    hipLaunchKernelGGL((k_err_gen<DT_BF16, GL, GR, KP>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, is_i, q, kept, E, pe)
 #define AWQ_EG2(GL, GR) \
   if (kept) { AWQ_EG3(GL, GR, true); } else { AWQ_EG3(GL, GR, false); }
 #define AWQ_EG(GL)                                                                                  \
@@ -475,7 +487,7 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
     const int64_t nt = gram_loss_tiles(N, K);
     for (int i0 = 0; i0 < n_alpha; i0 += sw.nc) {
       const int nc = n_alpha - i0 < sw.nc ? n_alpha - i0 : sw.nc;
-      for (int c = 0; c < nc; ++c) err_gen(sw.S + (int64_t)(i0 + c) * K, c);
+      for (int c = 0; c < nc; ++c) err_gen(i0 + c, c);
       const hipError_t el = launch_gram_loss(sw.E, N, K, sw.pexp, sw.P, sw.sk, sw.partial, nc, st);
       if (el != hipSuccess) return el;
       for (int c = 0; c < nc; ++c)
@@ -496,7 +508,7 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
     const int64_t gx = (N + kCT - 1) / kCT;
     const int64_t gy = (T + kCT - 1) / kCT;
     for (int i = 0; i < n_alpha; ++i) {
-      err_gen(sw.S + (int64_t)i * K, 0);
+      err_gen(i, 0);
       hipLaunchKernelGGL(k_err_contract, dim3((unsigned)contract_blocks(T, N)), dim3(256), 0, st, Xop, T,
                          ldop, px, sw.E, N, K, sw.pexp, sw.partial);
       hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial, gx * gy, tn,
