@@ -20,7 +20,7 @@ namespace awqk {
 
 constexpr int kStatsThreads = 256;
 constexpr int kStatsCols = 512;      // columns per block (64 lanes x 8)
-constexpr int kStatsUnroll = 8;      // rows per wave per loop trip (loads in flight)
+constexpr int kStatsUnroll = 16;     // rows per wave per loop trip (loads in flight)
 
 __global__ void k_fill_u64(unsigned long long* p, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
