@@ -11,6 +11,8 @@
  *   awq_act_stats      per-input-channel mean |x_j| over calibration tokens
  *   awq_search_scales  s_j = (mean|x_j|)^alpha, alpha chosen on a grid by the
  *                      layer-output MSE of Q(W diag(s)) diag(s)^-1 x
+ *                      (awq_search_scales_ex: the same under the quantizer's
+ *                      variants and with channels kept in 16-bit)
  *   awq_quantize_pack  group-wise asymmetric 4-bit round-to-nearest of
  *                      W diag(s): codes packed 8 per int32, one fp16 step and
  *                      one uint8 zero point per group (of 64, 128 or 256)
@@ -138,9 +140,9 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
  * required": s_j = (s_X,j)^alpha with s_X,j = mean |x_j|, alpha on a small grid
  * in [0, 1], and the alpha that minimises the mean squared error between the
  * layer output W x and Q(W diag(s)) diag(s)^-1 x over the calibration tokens
- * wins.  Q is the quantizer of awq_quantize_pack (fp16 step as stored) or,
- * for other bit widths and the symmetric grid, of awq_quantize_codes; with
- * alpha = 0 (s = 1) the loss is that of plain round-to-nearest.
+ * wins.  Q is the quantizer of awq_quantize_pack (4-bit asymmetric grid, fp16
+ * step as stored); with alpha = 0 (s = 1) the loss is that of plain
+ * round-to-nearest.
  *
  *   candidate i: s_ij = float( pow( max(double(mean_abs[j]), 2^-14), alphas[i] ) )
  *   loss_i      = (1 / (T N)) sum_t sum_n ( ((W - W_hat_i) x_t)_n )^2
@@ -152,16 +154,11 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
  *   alphas      [n_alpha] double, device memory
  *   n_alpha     1..AWQ_MAX_ALPHA
  *   group_size  64, 128 or 256; K a multiple of it and of 128
- *   bits, symmetric  the grid, as for awq_quantize_codes (4 and 0: the grid
- *               of awq_quantize_pack)
- *   kept        [K] uint8 or NULL, 16-byte aligned: channels with kept[k] != 0
- *               stay in 16-bit (W_hat = W there) and are left out of their
- *               groups' ranges; with alphas = {0} the loss is that of the
- *               mixed-precision baseline (see awq_salient_channels)
  *   s_out       [K] float: s of the best candidate
  *   inv_s_out   [K] float: 1.0f / s (IEEE division); may be NULL
  *   loss_out    [n_alpha] double; may be NULL
  *   best_idx_out  int32; may be NULL; -1 if every loss is NaN
+ *   ws          >= awq_workspace_bytes(AWQ_OP_SEARCH, 0, N, K, T, n_alpha)
  * The error products run on fp16/bf16 matrix cores with fp32 accumulation;
  * the per-row error is scaled by an exact power of two before rounding to
  * fp16 so that it stays in the normal range.  Two equivalent forms of the
@@ -173,17 +170,41 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
  * parts (22 significant bits); with G symmetric, a candidate contracts only
  * over the 256 x 256 blocks of G on and below the diagonal (off-diagonal
  * blocks counted twice), 2 N 256^2 g (g + 1) operations for g = ceil(K / 256),
- * about 2 N K^2.  The Gram form is taken when K <= 16384 and its total is
- * under half of the direct one's.
+ * about 2 N K^2.  The Gram form is taken when K <= 16384, Tp < 2^23 (its
+ * token rows are addressed with 32-bit offsets) and its total is under half
+ * of the direct one's.
  * Linears that read the same input may be searched together by passing their
  * row-concatenated W.
  */
 awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
                              const void* x_calib, int64_t T, int64_t ldx,
                              const float* mean_abs, const double* alphas, int n_alpha,
-                             int group_size, int bits, int symmetric, const uint8_t* kept,
-                             float* s_out, float* inv_s_out, double* loss_out,
+                             int group_size, float* s_out, float* inv_s_out, double* loss_out,
                              int32_t* best_idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The scale search of awq_search_scales under the quantizer's variants and
+ * with channels kept out of the quantization.  "AWQ Math", sections
+ * "Weight-only quantization and where it breaks" (N-bit weights; the
+ * symmetric step max|w| / 2^(N-1)) and "Shapes, granularity, and complexity"
+ * (groups with their own step and zero point); for kept channels, "AWQ vs.
+ * GPTQ: Understanding Weight Quantization Principles" (the salient weights
+ * kept in higher precision).  Same arguments and workspace as
+ * awq_search_scales, plus:
+ *   bits, symmetric  the grid, as for awq_quantize_codes (4 and 0: the grid
+ *               of awq_quantize_pack, which awq_search_scales scores)
+ *   kept        [K] uint8 or NULL, 16-byte aligned: channels with kept[k] != 0
+ *               stay in 16-bit (W_hat = W there) and are left out of their
+ *               groups' ranges; with alphas = {0} the loss is that of the
+ *               mixed-precision baseline (see awq_salient_channels)
+ * bits = 4, symmetric = 0, kept = NULL is exactly awq_search_scales.
+ */
+awq_status awq_search_scales_ex(const void* w, awq_dtype dt, int64_t N, int64_t K,
+                                const void* x_calib, int64_t T, int64_t ldx,
+                                const float* mean_abs, const double* alphas, int n_alpha,
+                                int group_size, int bits, int symmetric, const uint8_t* kept,
+                                float* s_out, float* inv_s_out, double* loss_out,
+                                int32_t* best_idx_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The salient channels of the mixed-precision baseline that AWQ replaces.

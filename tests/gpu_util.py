@@ -54,3 +54,21 @@ def loss_error_bound(W, X, Wq_over_s, u_op):
     P = E @ X.T
     T, N = X.shape[0], W.shape[0]
     return float(np.sum(2 * np.abs(P) * B + B * B)) / (T * N), float(np.sum(P * P)) / (T * N)
+
+
+def loss_rounding_sigma(E, G, T, N):
+    """Standard deviation of the change in one search loss caused by rounding
+    each error value E[n, k] once to fp16, under the probabilistic model of
+    rounding errors (Higham and Mary, "A new approach to probabilistic
+    rounding error analysis", SIAM J. Sci. Comput. 2019): the rounding errors
+    eta[n, k] are independent, zero-mean and |eta| <= 2^-11 |E| (half an fp16
+    ulp; each row is first scaled by an exact power of two that keeps it in
+    the normal range, so a subnormal error is at most 2^-38 of the row's
+    largest value).  To first order
+        L(E + eta) - L(E) = (2 / (T N)) sum_nk eta_nk c_nk,   c = E (X^T X),
+    so Var <= (2 / (T N))^2 sum_nk Var(eta_nk) c_nk^2 with Var(eta) <= bound^2 / 3.
+    E is [N, K] float64 (the exact W - W_hat), G = X^T X [K, K] float64."""
+    c = E @ G
+    rowmax = np.max(np.abs(E), axis=1, keepdims=True)
+    var = (2.0 ** -11 * np.abs(E)) ** 2 / 3.0 + (rowmax * 2.0 ** -38) ** 2
+    return 2.0 * float(np.sqrt(np.sum(var * c * c))) / (float(T) * float(N))

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_four_calls_and_helpers():
     names = declared_functions()
-    for n in ("awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_w4a16_gemm",
+    for n in ("awq_act_stats", "awq_search_scales", "awq_search_scales_ex", "awq_quantize_pack", "awq_w4a16_gemm",
               "awq_fold_scales", "awq_quantize_codes", "awq_salient_channels", "awq_workspace_bytes",
               "awq_status_str", "awq_abi_version"):
         assert n in names
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.awq_abi_version() == 4
+    assert lib.awq_abi_version() == 5
     for code in range(8):
         assert lib.awq_status_str(code).decode()
     assert lib.awq_status_str(0).decode() == "ok"
@@ -83,7 +83,7 @@ def test_act_stats_validation():
 
 def test_search_validation():
     lib = _lib()
-    f = lib.awq_search_scales
+    f = lib.awq_search_scales_ex
     ws = 1 << 40
 
     def call(**kw):
@@ -115,6 +115,102 @@ def test_search_validation():
     assert call(kept=ctypes.c_void_p(0x20008)) == 4   # the mask is read 8 channels at a time
     assert call(ws=NULL) == 6
     assert call(wsb=1024) == 6
+
+
+def test_plain_search_validation():
+    """awq_search_scales (the 4-bit asymmetric grid, no mask) validates the
+    same way as the variant entry point."""
+    lib = _lib()
+    f = lib.awq_search_scales
+
+    def call(**kw):
+        a = dict(w=A, dt=E.AWQ_F16, N=512, K=512, x=A2, T=64, ldx=512, m=A3, al=A3, na=20, g=128,
+                 s=A2, inv=NULL, loss=NULL, best=NULL, ws=A3, wsb=1 << 40)
+        a.update(kw)
+        return f(a["w"], a["dt"], a["N"], a["K"], a["x"], a["T"], a["ldx"], a["m"], a["al"], a["na"],
+                 a["g"], a["s"], a["inv"], a["loss"], a["best"], a["ws"], a["wsb"], NULL)
+
+    assert call(x=NULL) == 1
+    assert call(dt=E.AWQ_F32) == 3
+    assert call(K=500, ldx=504) == 2
+    assert call(g=96) == 5
+    assert call(na=65) == 5
+    assert call(x=BAD) == 4
+    assert call(wsb=1024) == 6
+
+
+def _prototypes():
+    """name -> (return type, [parameter types]) of every function in awq.h,
+    whitespace normalised, parameter names dropped."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for ret, name, params in re.findall(r"([A-Za-z_][\w\s\*]*?)\s*\b(awq_[a-z0-9_]+)\s*\(([^;{]*?)\)\s*;",
+                                        text):
+        types = []
+        for prm in params.split(","):
+            prm = " ".join(prm.split())
+            if prm in ("", "void"):
+                continue
+            m = re.match(r"(.*?)([A-Za-z_]\w*)$", prm)
+            types.append(m.group(1).replace(" *", "*").strip())
+        out[name] = (" ".join(ret.split()).replace(" *", "*"), types)
+    return out
+
+
+# The boundary contract: the four calls and two helpers, their argument types
+# in order.  A stream is a hipStream_t, which this header (free of HIP
+# headers) passes as void*: the same pointer in the calling convention.
+CONTRACT = {
+    "awq_act_stats": ("awq_status", ["const void*", "awq_dtype", "int64_t", "int64_t", "int64_t",
+                                     "float*", "void*", "size_t", "void*"]),
+    "awq_search_scales": ("awq_status", ["const void*", "awq_dtype", "int64_t", "int64_t",
+                                         "const void*", "int64_t", "int64_t", "const float*",
+                                         "const double*", "int", "int", "float*", "float*",
+                                         "double*", "int32_t*", "void*", "size_t", "void*"]),
+    "awq_quantize_pack": ("awq_status", ["const void*", "awq_dtype", "int64_t", "int64_t",
+                                         "const float*", "int", "int32_t*", "uint16_t*", "uint8_t*",
+                                         "float*", "void*"]),
+    "awq_w4a16_gemm": ("awq_status", ["const void*", "awq_dtype", "int64_t", "int64_t", "int64_t",
+                                      "const int32_t*", "const uint16_t*", "const uint8_t*",
+                                      "int64_t", "int", "const float*", "void*", "awq_dtype",
+                                      "int64_t", "void*", "size_t", "void*"]),
+    "awq_workspace_bytes": ("size_t", ["awq_op", "int64_t", "int64_t", "int64_t", "int64_t", "int"]),
+    "awq_status_str": ("const char*", ["awq_status"]),
+}
+
+
+def test_header_prototypes_match_the_contract():
+    protos = _prototypes()
+    for name, want in CONTRACT.items():
+        assert protos.get(name) == want, (name, protos.get(name), want)
+
+
+def test_binding_argument_counts_match_the_header():
+    for name, (_, types) in _prototypes().items():
+        assert len(abi.SIGNATURES[name][1]) == len(types), name
+
+
+def _direct_search_ws(N, K, T, n_alpha):
+    """Bytes of the direct-form search workspace for bf16 tokens (the larger
+    layout): candidate scales and reciprocals, row exponents, one error row
+    set, losses, tile partials, the tokens rounded to fp16 and their
+    exponents, each piece rounded up to 256 bytes."""
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    tiles = -(-N // 256) * -(-T // 256)
+    return (2 * up(n_alpha * K * 4) + up(N * 4) + up(N * K * 2) + up(n_alpha * 8) + up(tiles * 8) +
+            up(T * K * 2) + up(T * 4))
+
+
+def test_gram_form_token_limit():
+    """Past 2^23 padded tokens the Gram form's 32-bit row offsets would wrap:
+    the search then takes the direct form, whose workspace the library
+    reports; just below the limit it still takes the Gram form."""
+    lib = _lib()
+    N, K = 256, 256
+    for T in ((1 << 23), (1 << 23) + 1000):
+        assert lib.awq_workspace_bytes(abi.AWQ_OP_SEARCH, 0, N, K, T, 20) == _direct_search_ws(N, K, T, 20)
+    T = (1 << 23) - 256
+    assert lib.awq_workspace_bytes(abi.AWQ_OP_SEARCH, 0, N, K, T, 20) != _direct_search_ws(N, K, T, 20)
 
 
 def test_quantize_validation():

@@ -6,16 +6,23 @@ N=28672, bf16, M=2048).
 The statistic, codes, steps and zero points are compared in full.  Products
 are compared on sampled output channels (output channels are independent, so
 a sample is an exact check of those channels).  The search is checked on a
-row slice against the oracle at the full token count, and at full size
-through properties that hold at any size.
+row slice against the oracle at the full token count, and on the whole layer
+against exact losses the oracle wrote to tests/golden/.
 """
+import hashlib
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import workloads as WL
-from tests.gpu_util import GEMM_TOL, f32, gpu, rel_max_err
+from tests.gpu_util import GEMM_TOL, f32, gpu, loss_rounding_sigma, rel_max_err
+from tests.search_check import check_search_outputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "llama7b_up_search_losses.json")
 
 pytestmark = pytest.mark.gpu
 
@@ -75,28 +82,34 @@ def test_full_quantize_pack_and_decode(up7b):
         assert err <= GEMM_TOL
 
 
-def test_full_search_row_slice_and_properties(up7b):
-    """Row slice of the layer with all 65536 tokens against the oracle
-    (operand-precision scoring); the full layer on the GPU: the choice is the
-    minimal loss, no worse than plain round-to-nearest, its s is the oracle's
-    candidate for that index, and two runs are bit-identical."""
+def test_full_search_row_slice(up7b):
+    """Row slice of the layer (64 rows) with all 65536 tokens: every loss
+    against the exact fp64 loss, the index against its argmin, s and 1/s
+    bit-exact (tests/search_check.py)."""
     w, W, X, m_ref = up7b
     alphas = WL.alpha_grid(20)
-    al = gpu(torch.from_numpy(alphas))
-    m = gpu(torch.from_numpy(m_ref))
-    Wg, Xg = gpu(W), gpu(X)
-    # slice: 64 rows, every token
-    s, inv, L, best = awq.awq_search_scales(Wg[:64].contiguous(), Xg, m, al)
+    s, inv, L, best = awq.awq_search_scales(gpu(W[:64].contiguous()), gpu(X), gpu(torch.from_numpy(m_ref)),
+                                            gpu(torch.from_numpy(alphas)))
     torch.cuda.synchronize()
-    i_mod, s_mod, _, L_mod = O.search_scales(f32(W[:64]), f32(X), m_ref, alphas,
-                                             operand_model="fp16")
-    L = L.cpu().numpy()
-    assert np.all(np.abs(L - L_mod) <= 1e-5 * L_mod)
-    order = np.argsort(L_mod)
-    if (L_mod[order[1]] - L_mod[order[0]]) / L_mod[order[0]] > 2e-5:
-        assert int(best.cpu()[0]) == i_mod
-        assert np.array_equal(s.cpu().numpy().view(np.uint32), s_mod.view(np.uint32))
-    # full layer
+    check_search_outputs(L.cpu().numpy(), int(best.cpu()[0]), s.cpu().numpy(), inv.cpu().numpy(),
+                         f32(W[:64]), f32(X), m_ref, alphas, True, label="64-row slice")
+
+
+def test_full_search_against_exact_losses(up7b):
+    """The whole layer (Gram form of the loss, as the benchmark runs it)
+    against the exact fp64 losses of the definition that the CPU oracle wrote
+    to tests/golden/llama7b_up_search_losses.json: every loss within the
+    tolerance of tests/search_check.py, the index equal to their argmin, s and
+    1/s bit-exact; two runs bit-identical."""
+    w, W, X, m_ref = up7b
+    gold = json.load(open(GOLDEN))
+    alphas = WL.alpha_grid(20)
+    assert (gold["N"], gold["K"], gold["T"]) == (w.N, w.K, w.T)
+    assert np.array_equal(np.array(gold["alphas"]), alphas)
+    assert gold["mean_abs_sha"] == hashlib.sha256(m_ref.tobytes()).hexdigest()
+    L_ex = np.array(gold["losses"])
+    al, m = gpu(torch.from_numpy(alphas)), gpu(torch.from_numpy(m_ref))
+    Wg, Xg = gpu(W), gpu(X)
     outs = []
     for _ in range(2):
         s, inv, L, best = awq.awq_search_scales(Wg, Xg, m, al)
@@ -105,12 +118,27 @@ def test_full_search_row_slice_and_properties(up7b):
     (s, inv, L, b), (s2, inv2, L2, b2) = outs
     assert b == b2 and torch.equal(s, s2) and torch.equal(L, L2) and torch.equal(inv, inv2)
     L = L.numpy()
-    assert L[b] == np.min(L) and np.all(L[:b] > L[b]) and L[b] <= L[0]
-    S_ref = O.candidate_scales(m_ref, alphas)
-    assert np.array_equal(s.numpy().view(np.uint32), S_ref[b].view(np.uint32))
+    # tolerance: 8 sigma of the fp16 rounding of the error values (computed
+    # here on the full layer, in float32: an estimate of a spread) plus 1e-5
+    Wf, Xf = f32(W), f32(X)
+    G = (Xf.T @ Xf).astype(np.float32)
+    S = O.candidate_scales(m_ref, alphas)
+    tol = np.empty(20)
+    for i in range(20):
+        r = O.quantize_layer(Wf, S[i])
+        grid = O.dequantize(r["q"].reshape(w.N, w.K // 128, 128), r["D"], r["z"].astype(np.float32))
+        E = (Wf.astype(np.float64) - O.unscale_activation(grid.reshape(w.N, w.K), S[i])).astype(np.float32)
+        tol[i] = 8.0 * loss_rounding_sigma(E, G, w.T, w.N) + 1e-5 * L_ex[i]
+    dev = np.abs(L - L_ex)
+    print(f"full search: GPU argmin {b}, exact argmin {gold['argmin']} (gap "
+          f"{gold['relative_gap_best_to_runner_up']:.2e}); max |L - L_exact| / L_exact "
+          f"{np.max(dev / L_ex):.2e}, tolerance up to {np.max(tol / L_ex):.2e}")
+    assert np.all(dev <= tol)
+    assert gold["relative_gap_best_to_runner_up"] > 2 * np.max(tol / L_ex)
+    assert b == gold["argmin"]
+    assert np.array_equal(s.numpy().view(np.uint32), S[b].view(np.uint32))
     assert np.array_equal(inv.numpy().view(np.uint32),
-                          (np.float32(1) / S_ref[b]).astype(np.float32).view(np.uint32))
-    print(f"full search: alpha index {b}, loss {L[b]:.4e} vs round-to-nearest {L[0]:.4e}")
+                          (np.float32(1) / S[b]).astype(np.float32).view(np.uint32))
 
 
 def test_full_prefill_gemm_sampled_channels():
@@ -185,24 +213,81 @@ def test_full_prefill_gemm_groups(group):
                                                  (128, 4, False, True)])
 def test_full_search_variants_row_slice(up7b, group, bits, sym, keep):
     """Quantizer variants and the mixed-precision baseline at the full token
-    count (65536) on a 64-row slice, against the oracle scored in the
-    operand precision."""
+    count (65536) on a 64-row slice, against the exact losses (every fourth
+    candidate exponent)."""
     w, W, X, m_ref = up7b
     alphas = WL.alpha_grid(20)[::4].copy()
-    m = gpu(torch.from_numpy(m_ref))
     kept = O.salient_channels(m_ref, w.K // 100) if keep else None
     s, inv, L, best = awq.awq_search_scales(
-        gpu(W[:64].contiguous()), gpu(X), m, gpu(torch.from_numpy(alphas)), group, bits=bits,
-        symmetric=sym, kept=None if kept is None else gpu(torch.from_numpy(kept.astype(np.uint8))))
+        gpu(W[:64].contiguous()), gpu(X), gpu(torch.from_numpy(m_ref)), gpu(torch.from_numpy(alphas)),
+        group, bits=bits, symmetric=sym,
+        kept=None if kept is None else gpu(torch.from_numpy(kept.astype(np.uint8))))
     torch.cuda.synchronize()
-    i_mod, s_mod, _, L_mod = O.search_scales(f32(W[:64]), f32(X), m_ref, alphas, group,
-                                             operand_model="fp16", bits=bits, symmetric=sym,
-                                             keep=kept)
-    L = L.cpu().numpy()
-    print(f"variant g={group} bits={bits} sym={sym} keep={keep}: "
-          f"max rel loss diff {np.max(np.abs(L - L_mod) / L_mod):.2e}")
-    assert np.all(np.abs(L - L_mod) <= 1e-5 * L_mod)
-    order = np.argsort(L_mod)
-    if (L_mod[order[1]] - L_mod[order[0]]) / L_mod[order[0]] > 2e-5:
-        assert int(best.cpu()[0]) == i_mod
-        assert np.array_equal(s.cpu().numpy().view(np.uint32), s_mod.view(np.uint32))
+    check_search_outputs(L.cpu().numpy(), int(best.cpu()[0]), s.cpu().numpy(), inv.cpu().numpy(),
+                         f32(W[:64]), f32(X), m_ref, alphas, True, group, bits, sym, kept,
+                         label=f"variant g={group} bits={bits} sym={sym} keep={keep}")
+
+
+@pytest.mark.parametrize("linear,ydt", [("down", torch.float32), ("down", torch.bfloat16),
+                                        ("up", torch.float32)])
+def test_full_prefill_gemm_down_and_f32(linear, ydt):
+    """M = 2048 bf16 prefill through the Llama-70B MLP down-projection
+    (K = 28672 -> N = 8192: 224 groups per row, 448 stages per tile) and the
+    up-projection with float32 output; float32 output is the parity measure,
+    bf16 output adds its own rounding (half an ulp, not counted)."""
+    w = WL.workload(4, linear)
+    g = np.random.Generator(np.random.PCG64(4545 + w.K))
+    N, K = w.N, w.K
+    words = g.integers(-2 ** 31, 2 ** 31, (N, K // 8), dtype=np.int64).astype(np.int32)
+    step = g.uniform(5e-4, 5e-3, (N, K // 128)).astype(np.float16)
+    z = g.integers(0, 16, (N, K // 128)).astype(np.uint8)
+    inv = (1.0 / np.exp(g.uniform(-1, 1, K))).astype(np.float32)
+    x = WL.prefill_input(w, 2048)
+    y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                           gpu(torch.from_numpy(z)), gpu(torch.from_numpy(inv)), out_dtype=ydt)
+    torch.cuda.synchronize()
+    rows = _sample_rows(N, 131, 7)
+    ref = O.w4a16_matmul_rows(f32(x), words, step, z, rows, inv)
+    err = rel_max_err(f32(y)[:, rows], ref, ydt)
+    print(f"prefill {linear} {K}->{N} -> {ydt}: rel max err {err:.3e} on {len(rows)} channels")
+    assert err <= GEMM_TOL
+
+
+def test_full_decoder_layer_7b():
+    """A whole Llama-7B-shaped decoder layer (q, k, v, o 4096 x 4096; gate, up
+    4096 -> 11008; down 11008 -> 4096; fp16; 64 calibration tokens per input):
+    statistics, search, quantize + pack per linear on the GPU, then the decode
+    products at M = 1, 8 and 32 with 1/s.  The statistic, s (the oracle's
+    candidate for the chosen index, which has the smallest loss), the packed
+    codes, steps and zero points are compared in full; the products on
+    sampled output channels."""
+    al = WL.alpha_grid(20)
+    for lin in ("q", "k", "v", "o", "gate", "up", "down"):
+        w = WL.workload(3, lin)
+        W, X = WL.weight(w), WL.calibration(w)
+        m = awq.awq_act_stats(gpu(X))
+        s, inv, L, best = awq.awq_search_scales(gpu(W), gpu(X), m, gpu(torch.from_numpy(al)))
+        q, sc, z = awq.awq_quantize_pack(gpu(W), s)
+        torch.cuda.synchronize()
+        m_ref = O.act_mean_abs(f32(X))
+        assert np.array_equal(m.cpu().numpy().view(np.uint32), m_ref.view(np.uint32)), lin
+        b, Lh = int(best.cpu()[0]), L.cpu().numpy()
+        assert Lh[b] == np.min(Lh) and np.all(Lh[:b] > Lh[b]), lin
+        s_np = O.candidate_scales(m_ref, al)[b]
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), s_np.view(np.uint32)), lin
+        r = O.quantize_layer(f32(W), s_np)
+        words = O.pack_codes(r["q"])
+        assert np.array_equal(q.cpu().numpy(), words), lin
+        assert np.array_equal(sc.cpu().numpy().view(np.uint16), r["step"].view(np.uint16)), lin
+        assert np.array_equal(z.cpu().numpy(), r["z"]), lin
+        inv_np = (np.float32(1) / s_np).astype(np.float32)
+        assert np.array_equal(inv.cpu().numpy().view(np.uint32), inv_np.view(np.uint32)), lin
+        rows = _sample_rows(w.N, 41, 11)
+        for M in (1, 8, 32):
+            x = WL.decode_input(w, M)
+            y = awq.awq_w4a16_gemm(gpu(x), q, sc, z, inv)
+            torch.cuda.synchronize()
+            ref = O.w4a16_matmul_rows(f32(x), words, r["step"], r["z"], rows, inv_np)
+            err = rel_max_err(f32(y)[:, rows], ref, torch.float16)
+            print(f"7B layer {lin} {w.K}->{w.N} M={M}: alpha index {b}, rel max err {err:.3e}")
+            assert err <= GEMM_TOL, (lin, M)

@@ -369,6 +369,56 @@ def _loss_by_loops(W, X, s):
     return tot / (X.shape[0] * N)
 
 
+def _fp32_correctly_rounded(v):
+    """The float32 nearest to the Decimal v > 0 (ties: even), and the distance
+    from v to the nearest float32 rounding boundary relative to v."""
+    import decimal
+    c = np.float32(float(v))
+    cands = {c, np.nextafter(c, np.float32(np.inf)), np.nextafter(c, np.float32(0))}
+    # neighbours of every candidate, so that the bracketing pair is present
+    cands |= {np.nextafter(x, np.float32(np.inf)) for x in list(cands)}
+    cands |= {np.nextafter(x, np.float32(0)) for x in list(cands)}
+    ordered = sorted(cands, key=lambda x: (abs(decimal.Decimal(float(x)) - v), int(np.array(x).view(np.uint32)) & 1))
+    best = ordered[0]
+    lo = max((x for x in cands if decimal.Decimal(float(x)) <= v), key=lambda x: float(x))
+    hi = min((x for x in cands if decimal.Decimal(float(x)) >= v), key=lambda x: float(x))
+    mid = (decimal.Decimal(float(lo)) + decimal.Decimal(float(hi))) / 2
+    margin = abs(v - mid) / v if lo != hi else decimal.Decimal(1)
+    return best, margin
+
+
+def test_candidate_scales_against_decimal_powers():
+    """s = fp32(max(m, 2^-14)^alpha) at every alpha = i / 19 (the grid of the
+    workloads) against m^alpha = exp(alpha ln m) evaluated in 50-digit decimal
+    arithmetic, independent of the float64 pow the oracle uses: bit-exact
+    after correct rounding to float32, except where the exact power lies
+    within 2^-40 (relative) of a float32 rounding boundary, where a correctly
+    rounded float64 result may legitimately fall on either side."""
+    import decimal
+    ctx = decimal.Context(prec=50)
+    g = _rng(161)
+    m = np.concatenate([np.abs(g.standard_normal(40)) * 3, np.exp(g.uniform(-12, 4, 40)),
+                        [0.0, 1e-9, 2.0 ** -14, 1.0, 2.0, 0.5, 20.0]]).astype(np.float32)
+    alphas = np.arange(20, dtype=np.float64) / np.float64(19)
+    S = O.candidate_scales(m, alphas)
+    checked = skipped = 0
+    for j, mj in enumerate(m):
+        base = decimal.Decimal(float(max(np.float64(mj), 2.0 ** -14)))
+        ln = base.ln(ctx)
+        for i, a in enumerate(alphas):
+            v = (decimal.Decimal(float(a)) * ln).exp(ctx)          # alpha exactly as stored in float64
+            want, margin = _fp32_correctly_rounded(v)
+            if margin < decimal.Decimal(2) ** -40:
+                skipped += 1
+                continue
+            assert S[i, j] == want, (j, i, float(mj), float(a), S[i, j], want)
+            checked += 1
+    assert checked >= 0.99 * len(m) * len(alphas) and skipped <= 2
+    # a float32 pow, or a product in place of the power, fails this pin
+    bad = np.power(np.maximum(m, np.float32(2.0 ** -14))[None, :], alphas.astype(np.float32)[:, None])
+    assert not np.array_equal(bad.astype(np.float32), S)
+
+
 def test_search_loss_against_loops_and_gram_form():
     g = _rng(17)
     N, K, T = 3, 256, 6

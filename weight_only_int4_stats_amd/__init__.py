@@ -17,7 +17,7 @@ from . import _abi
 from ._abi import (AWQ_BF16, AWQ_F16, AWQ_F32, AWQ_GROUP, AWQ_OP_ACT_STATS, AWQ_OP_GEMM,  # noqa: F401
                    AWQ_OP_QUANTIZE, AWQ_OP_SEARCH, AwqError, lib)
 
-__all__ = ["awq_act_stats", "awq_search_scales", "awq_quantize_pack", "awq_quantize_codes",
+__all__ = ["awq_act_stats", "awq_search_scales", "awq_search_scales_ex", "awq_quantize_pack", "awq_quantize_codes",
            "awq_w4a16_gemm", "awq_fold_scales", "awq_salient_channels", "awq_workspace_bytes",
            "AwqError", "lib"]
 
@@ -78,8 +78,29 @@ def awq_search_scales(w: torch.Tensor, x_calib: torch.Tensor, mean_abs: torch.Te
                       ws: torch.Tensor | None = None, stream=None, *, bits: int = 4,
                       symmetric: bool = False, kept: torch.Tensor | None = None):
     """Returns (s [K] f32, inv_s [K] f32, losses [n] f64, best index int32 [1]).
-    bits / symmetric select the quantizer's grid (4 / False: awq_quantize_pack's);
-    kept (uint8 [K]) marks channels kept in 16-bit (the mixed-precision baseline)."""
+    With the defaults this calls awq_search_scales (the 4-bit asymmetric grid);
+    bits / symmetric (another grid) or kept (uint8 [K]: channels kept in
+    16-bit, the mixed-precision baseline) call awq_search_scales_ex."""
+    ex = bits != 4 or bool(symmetric) or kept is not None
+    return _search(w, x_calib, mean_abs, alphas, group_size, s_out, inv_s_out, loss_out,
+                   best_idx_out, ws, stream, (bits, symmetric, kept) if ex else None)
+
+
+def awq_search_scales_ex(w: torch.Tensor, x_calib: torch.Tensor, mean_abs: torch.Tensor,
+                         alphas: torch.Tensor, group_size: int = AWQ_GROUP, bits: int = 4,
+                         symmetric: bool = False, kept: torch.Tensor | None = None,
+                         s_out: torch.Tensor | None = None, inv_s_out: torch.Tensor | None = None,
+                         loss_out: torch.Tensor | None = None,
+                         best_idx_out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                         stream=None):
+    """awq_search_scales_ex: the search under the grid (bits, symmetric) with
+    the channels marked in kept (uint8 [K] or None) left in 16-bit."""
+    return _search(w, x_calib, mean_abs, alphas, group_size, s_out, inv_s_out, loss_out,
+                   best_idx_out, ws, stream, (bits, symmetric, kept))
+
+
+def _search(w, x_calib, mean_abs, alphas, group_size, s_out, inv_s_out, loss_out, best_idx_out,
+            ws, stream, variant):
     for t, n in ((w, "w"), (x_calib, "x_calib"), (mean_abs, "mean_abs"), (alphas, "alphas")):
         _dev(t, n)
     if not w.is_contiguous() or w.dim() != 2:
@@ -97,12 +118,17 @@ def awq_search_scales(w: torch.Tensor, x_calib: torch.Tensor, mean_abs: torch.Te
     loss_out = torch.empty(n_alpha, dtype=torch.float64, device=dev) if loss_out is None else loss_out
     best_idx_out = torch.empty(1, dtype=torch.int32, device=dev) if best_idx_out is None else best_idx_out
     ws, wsb = _workspace(awq_workspace_bytes(AWQ_OP_SEARCH, 0, N, K, T, n_alpha), dev, ws)
-    st = lib().awq_search_scales(_ptr(w), _DT.get(w.dtype, -1), N, K, _ptr(x_calib), T, ldx,
-                                 _ptr(mean_abs), _ptr(alphas), n_alpha, group_size, bits,
-                                 int(bool(symmetric)), _ptr(kept), _ptr(s_out), _ptr(inv_s_out),
-                                 _ptr(loss_out), _ptr(best_idx_out), _ptr(ws), wsb,
-                                 _stream(dev, stream))
-    _abi.check("awq_search_scales", st)
+    head = (_ptr(w), _DT.get(w.dtype, -1), N, K, _ptr(x_calib), T, ldx, _ptr(mean_abs),
+            _ptr(alphas), n_alpha, group_size)
+    tail = (_ptr(s_out), _ptr(inv_s_out), _ptr(loss_out), _ptr(best_idx_out), _ptr(ws), wsb,
+            _stream(dev, stream))
+    if variant is None:
+        st = lib().awq_search_scales(*head, *tail)
+        _abi.check("awq_search_scales", st)
+    else:
+        bits, symmetric, kept = variant
+        st = lib().awq_search_scales_ex(*head, bits, int(bool(symmetric)), _ptr(kept), *tail)
+        _abi.check("awq_search_scales_ex", st)
     return s_out, inv_s_out, loss_out, best_idx_out
 
 

@@ -23,7 +23,7 @@ bool grid_ok(int bits, int symmetric) {
 
 extern "C" {
 
-int awq_abi_version(void) { return 4; }
+int awq_abi_version(void) { return 5; }
 
 const char* awq_status_str(awq_status st) {
   switch (st) {
@@ -62,12 +62,12 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
   return from_hip(awq::launch_act_stats(x, (int)xdt, T, K, ldx, mean_abs, ws, (hipStream_t)stream));
 }
 
-awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
-                             const void* x_calib, int64_t T, int64_t ldx,
-                             const float* mean_abs, const double* alphas, int n_alpha,
-                             int group_size, int bits, int symmetric, const uint8_t* kept,
-                             float* s_out, float* inv_s_out, double* loss_out,
-                             int32_t* best_idx_out, void* ws, size_t ws_bytes, void* stream) {
+awq_status awq_search_scales_ex(const void* w, awq_dtype dt, int64_t N, int64_t K,
+                                const void* x_calib, int64_t T, int64_t ldx,
+                                const float* mean_abs, const double* alphas, int n_alpha,
+                                int group_size, int bits, int symmetric, const uint8_t* kept,
+                                float* s_out, float* inv_s_out, double* loss_out,
+                                int32_t* best_idx_out, void* ws, size_t ws_bytes, void* stream) {
   if (!w || !x_calib || !mean_abs || !alphas || !s_out) return AWQ_ERR_NULL;
   if (!is_act_dtype(dt)) return AWQ_ERR_DTYPE;
   if (!group_ok(group_size) || !grid_ok(bits, symmetric)) return AWQ_ERR_UNSUPPORTED;
@@ -88,6 +88,16 @@ awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
   return from_hip(awq::launch_search(w, (int)dt, N, K, x_calib, T, ldx, mean_abs, alphas, n_alpha,
                                      qv, kept, s_out, inv_s_out, loss_out, best_idx_out, ws,
                                      (hipStream_t)stream));
+}
+
+awq_status awq_search_scales(const void* w, awq_dtype dt, int64_t N, int64_t K,
+                             const void* x_calib, int64_t T, int64_t ldx,
+                             const float* mean_abs, const double* alphas, int n_alpha,
+                             int group_size, float* s_out, float* inv_s_out, double* loss_out,
+                             int32_t* best_idx_out, void* ws, size_t ws_bytes, void* stream) {
+  return awq_search_scales_ex(w, dt, N, K, x_calib, T, ldx, mean_abs, alphas, n_alpha, group_size,
+                              4, 0, nullptr, s_out, inv_s_out, loss_out, best_idx_out, ws, ws_bytes,
+                              stream);
 }
 
 awq_status awq_salient_channels(const float* mean_abs, int64_t K, int64_t n_keep, uint8_t* kept,

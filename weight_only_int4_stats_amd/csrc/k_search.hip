@@ -373,8 +373,11 @@ constexpr int kGramBatch = 4;
 // carried as two fp16 parts, over the blocks on and below the diagonal only)
 // replaces the T-long contraction when it costs well under half as many
 // matrix-core operations and G (K^2 doubles) is small.
+// The Gram build addresses 256 token rows of the transposed tokens with
+// 32-bit buffer offsets, so Tp stays below 2^23; longer calibration sets take
+// the direct form.
 bool search_uses_gram(int64_t N, int64_t K, int64_t T, int n_alpha) {
-  if (K > 16384) return false;
+  if (K > 16384 || gram_tokens_padded(T) >= (int64_t(1) << 23)) return false;
   const double Tp = (double)gram_tokens_padded(T);
   const double g = (double)((K + awqk::kCT - 1) / awqk::kCT);
   const double direct = (double)n_alpha * 2.0 * (double)T * (double)N * (double)K;

@@ -165,3 +165,62 @@ def random_matrix(shape, dtype: torch.dtype, seed: int, scale: float = 1.0) -> t
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([9999, seed])))
     a = g.standard_normal(shape, dtype=np.float32) * np.float32(scale)
     return _cast(a, dtype)
+
+
+# --------------------------------------------------------------------------
+# Device-side generators for the 80-layer 70B-shaped stack (about 140 GB of
+# fp16 weights, too large to draw on the host).  torch's device generator
+# (Philox) seeded from the same (config, role, layer, linear) key; the outlier
+# channels and boosts still come from channel_boosts.
+# --------------------------------------------------------------------------
+def _device_gen(device, cfg: int, role: int, layer: int = 0, linear: int = 0) -> torch.Generator:
+    seed = int(np.random.SeedSequence([cfg, role, layer, linear]).generate_state(1, np.uint64)[0] >> 1)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def device_weight(w: Workload, device, out: torch.Tensor | None = None) -> torch.Tensor:
+    """W [N, K] in the workload's dtype, drawn on the device (into ``out`` if
+    given) in pieces of at most 256 MB of float32."""
+    g = _device_gen(device, w.cfg, ROLE_W, w.layer, LINEAR_IDS[w.linear])
+    if out is None:
+        out = torch.empty((w.N, w.K), dtype=w.dtype, device=device)
+    rows = max(1, (1 << 26) // w.K)
+    for r0 in range(0, w.N, rows):
+        r1 = min(w.N, r0 + rows)
+        piece = torch.empty((r1 - r0, w.K), dtype=torch.float32, device=device)
+        piece.normal_(0.0, w.sigma_w, generator=g)
+        out[r0:r1].copy_(piece)
+    return out
+
+
+def device_activations(w: Workload, rows: int, device, role: int = ROLE_XCAL) -> torch.Tensor:
+    """X [rows, K] with the workload's outlier channels, drawn on the device."""
+    _, b = channel_boosts(w)
+    group = {"q": 0, "k": 0, "v": 0, "o": 3, "gate": 4, "up": 4, "down": 6, "single": 0}[w.linear]
+    g = _device_gen(device, w.cfg, role, w.layer, 16 * group)
+    bd = torch.from_numpy(b).to(device)
+    out = torch.empty((rows, w.K), dtype=w.dtype, device=device)
+    chunk = max(1, (1 << 26) // w.K)
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        z = torch.empty((r1 - r0, w.K), dtype=torch.float32, device=device)
+        z.normal_(0.0, 1.0, generator=g)
+        out[r0:r1].copy_(z * bd[None, :])
+    return out
+
+
+def device_packed(N: int, K: int, device, seed: int, group: int = 128,
+                  step_range=(5e-4, 5e-3)) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Seeded random packed codes (any 32-bit word), fp16 steps and uint8 zero
+    points in the layout of the quantizer's output, drawn on the device: the
+    decode products do the same work on any values, so layers whose values do
+    not matter for a measurement carry these."""
+    g = _device_gen(device, 90, seed)
+    q = torch.randint(-2 ** 31, 2 ** 31, (N, K // 8), dtype=torch.int64, device=device,
+                      generator=g).to(torch.int32)
+    sc = torch.empty((N, K // group), dtype=torch.float32, device=device)
+    sc.uniform_(step_range[0], step_range[1], generator=g)
+    z = torch.randint(0, 16, (N, K // group), dtype=torch.uint8, device=device, generator=g)
+    return q, sc.to(torch.float16), z
