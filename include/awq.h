@@ -310,6 +310,32 @@ awq_status awq_w4a16_gemm(const void* x, awq_dtype xdt, int64_t M, int64_t K, in
                           int64_t ldy, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The fused W4A16 product of awq_w4a16_gemm for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results and kernels as
+ * awq_w4a16_gemm, without the workspace: the product's scratch (for M > 16 the
+ * activations converted to fp16 and the dequantization constants, at most
+ * awq_workspace_bytes(AWQ_OP_GEMM, M, N, K, 0, 0) bytes) lives in one
+ * library-held device array of AWQ_NOALLOC_SCRATCH_BYTES per GPU, reserved
+ * when the library's code is loaded on that GPU and held until the process
+ * ends.  Its address is looked up on the first call on each device.  Nothing
+ * is allocated per call.
+ *   Sizes whose scratch exceeds AWQ_NOALLOC_SCRATCH_BYTES -> AWQ_ERR_UNSUPPORTED
+ *   (the prefill shape 2048 x 28672 -> 8192 with groups of 128 fits; with
+ *   groups of 64 it does not).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or host threads, without ordering) race and give
+ * undefined results.  The kernels write every scratch byte they read within
+ * the same call, so nothing has to start at zero.
+ */
+#define AWQ_NOALLOC_SCRATCH_BYTES (128u << 20)
+awq_status awq_w4a16_gemm_noalloc(const void* x, awq_dtype xdt, int64_t M, int64_t K, int64_t ldx,
+                                  const int32_t* qweight, const uint16_t* scales,
+                                  const uint8_t* zeros, int64_t N, int group_size,
+                                  const float* inv_s, void* y, awq_dtype ydt, int64_t ldy,
+                                  void* stream);
+
+/*
  * Folds the activation scaling into the operation that produces x, so that
  * the product runs with inv_s == NULL.  "AWQ Math", section "The equivalent
  * transform: scale up W, scale down x": the division of x_j by s_j can be

@@ -309,3 +309,27 @@ def test_fold_validation():
     assert f(ctypes.c_void_p((1 << 20) + 2), E.AWQ_F32, 4, 8, 8, S, 1, NULL) == 4
     assert f(NULL, E.AWQ_F16, 0, 8, 8, NULL, 1, NULL) == 0   # empty: no-op
 
+
+
+def test_gemm_noalloc_validation():
+    """awq_w4a16_gemm_noalloc rejects bad arguments on the host, and sizes
+    whose scratch exceeds the library's array, before any launch."""
+    lib = _lib()
+    f = lib.awq_w4a16_gemm_noalloc
+
+    def call(**kw):
+        a = dict(x=A, xdt=E.AWQ_F16, M=1, K=4096, ldx=4096, q=A2, sc=A3, z=A3, N=11008, g=128,
+                 r=NULL, y=A2, ydt=E.AWQ_F16, ldy=11008)
+        a.update(kw)
+        return f(a["x"], a["xdt"], a["M"], a["K"], a["ldx"], a["q"], a["sc"], a["z"], a["N"], a["g"],
+                 a["r"], a["y"], a["ydt"], a["ldy"], NULL)
+
+    assert call(M=0, x=NULL) == 0
+    assert call(x=NULL) == 1
+    assert call(xdt=E.AWQ_F32) == 3
+    assert call(K=4000, ldx=4000) == 2
+    assert call(g=32) == 5
+    assert call(x=BAD) == 4
+    # 2048 tokens, 28672 -> 8192, groups of 64: about 147 MB of scratch
+    assert call(M=2048, K=28672, ldx=28672, N=8192, ldy=8192, g=64, xdt=E.AWQ_BF16) == 5
+    assert abi.AWQ_NOALLOC_SCRATCH_BYTES == 128 << 20

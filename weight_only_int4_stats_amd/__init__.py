@@ -18,7 +18,7 @@ from ._abi import (AWQ_BF16, AWQ_F16, AWQ_F32, AWQ_GROUP, AWQ_OP_ACT_STATS, AWQ_
                    AWQ_OP_QUANTIZE, AWQ_OP_SEARCH, AwqError, lib)
 
 __all__ = ["awq_act_stats", "awq_search_scales", "awq_search_scales_ex", "awq_quantize_pack", "awq_quantize_codes",
-           "awq_w4a16_gemm", "awq_fold_scales", "awq_salient_channels", "awq_workspace_bytes",
+           "awq_w4a16_gemm", "awq_w4a16_gemm_noalloc", "awq_fold_scales", "awq_salient_channels", "awq_workspace_bytes",
            "AwqError", "lib"]
 
 _DT = {torch.float16: AWQ_F16, torch.bfloat16: AWQ_BF16, torch.float32: AWQ_F32}
@@ -207,6 +207,29 @@ def awq_w4a16_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
                               _ptr(zeros), N, group_size, _ptr(inv_s), _ptr(y), _DT.get(y.dtype, -1),
                               ldy, _ptr(ws), wsb, _stream(dev, stream))
     _abi.check("awq_w4a16_gemm", st)
+    return y
+
+
+def awq_w4a16_gemm_noalloc(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor,
+                           zeros: torch.Tensor, inv_s: torch.Tensor | None = None,
+                           y: torch.Tensor | None = None, out_dtype: torch.dtype | None = None,
+                           group_size: int = AWQ_GROUP, stream=None):
+    """awq_w4a16_gemm without a workspace: the library's own per-GPU scratch
+    array serves the product (calls that overlap on one GPU race).  Pass y to
+    call it without any allocation."""
+    _dev(x, "x")
+    _dev(qweight, "qweight")
+    M, K, ldx = _rows(x, "x")
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K:
+        raise ValueError("qweight must be [N, K/8]")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype or x.dtype, device=x.device)
+    ldy = y.stride(0) if y.dim() == 2 else N
+    st = lib().awq_w4a16_gemm_noalloc(_ptr(x), _DT.get(x.dtype, -1), M, K, ldx, _ptr(qweight),
+                                      _ptr(scales), _ptr(zeros), N, group_size, _ptr(inv_s), _ptr(y),
+                                      _DT.get(y.dtype, -1), ldy, _stream(x.device, stream))
+    _abi.check("awq_w4a16_gemm_noalloc", st)
     return y
 
 

@@ -19,6 +19,7 @@ AWQ_F16, AWQ_BF16, AWQ_F32 = 0, 1, 2
 AWQ_OP_ACT_STATS, AWQ_OP_SEARCH, AWQ_OP_QUANTIZE, AWQ_OP_GEMM = 0, 1, 2, 3
 AWQ_GROUP = 128
 AWQ_MAX_ALPHA = 64
+AWQ_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 # exported symbol -> (restype, argtypes)
 _i64, _p, _i, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -37,6 +38,8 @@ SIGNATURES = {
     "awq_w4a16_gemm": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _i64, _i, _p, _p, _i, _i64, _p,
                             _sz, _p]),
     "awq_fold_scales": (_i, [_p, _i, _i64, _i64, _i64, _p, _i, _p]),
+    "awq_w4a16_gemm_noalloc": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _i64, _i, _p, _p, _i, _i64,
+                                    _p]),
 }
 
 _lib = None
