@@ -597,3 +597,41 @@ def test_product_single_group_64(M, N):
     torch.cuda.synchronize()
     ref = O.w4a16_matmul(f32(x), words, step, z, None, group)
     assert rel_max_err(f32(y), ref) <= GEMM_TOL
+
+
+@pytest.mark.parametrize("M,N,K,dtype,ydt,with_r,group", [
+    (17, 4096, 4096, F16, F16, True, 128),        # 4 K slices meet in the last-arriving block
+    (24, 11008, 4096, BF16, torch.float32, True, 128),   # 172 row blocks
+    (32, 4096, 11008, F16, torch.float32, True, 128),    # 86 units: uneven slices
+    (48, 1000, 2560, BF16, BF16, False, 64),       # ragged last row block, groups of 64
+    (64, 777, 8192, F16, torch.float32, True, 256),     # four token groups, groups of 256
+    (33, 64, 128, F16, torch.float32, False, 128),  # one unit, one row block
+    (40, 3000, 28672, BF16, F16, True, 128),       # long K: 224 units over the slices
+])
+def test_small_batch_product_parity(M, N, K, dtype, ydt, with_r, group):
+    """17 <= M <= 64: the memory-bound small-batch product (split over K, the
+    partial sums added by the last block of each row block)."""
+    words, step, z = _random_packed_g(N, K, M * 31 + N + K + group, group)
+    x = _act(M, K, dtype, M + N)
+    r = None
+    if with_r:
+        g = np.random.Generator(np.random.PCG64(K + M))
+        r = (np.float32(1) / np.exp(g.uniform(-1.5, 1.5, K)).astype(np.float32)).astype(np.float32)
+    ldy = N + 40
+    big = torch.full((M, ldy), 9.0, dtype=ydt, device="cuda")
+    awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                       gpu(torch.from_numpy(z)), None if r is None else gpu(torch.from_numpy(r)),
+                       y=big[:, :N], group_size=group)
+    torch.cuda.synchronize()
+    ref = O.w4a16_matmul(f32(x), words, step, z, r, group)
+    err = rel_max_err(f32(big[:, :N].cpu()), ref, ydt)
+    print(f"small batch M={M} N={N} K={K} g={group}: rel max err {err:.3e}")
+    assert err <= GEMM_TOL
+    assert torch.all(big[:, N:] == 9.0).item()
+    # bit-identical on a second call (fixed order of the slice sums)
+    again = torch.empty((M, N), dtype=ydt, device="cuda")
+    awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                       gpu(torch.from_numpy(z)), None if r is None else gpu(torch.from_numpy(r)),
+                       y=again, group_size=group)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.uint8), big[:, :N].contiguous().view(torch.uint8))

@@ -70,6 +70,13 @@ hipError_t launch_w4a16(const void* x, int xdt, int64_t M, int64_t K, int64_t ld
                         int64_t N, int group, const float* inv_s, void* y, int ydt, int64_t ldy,
                         void* ws, hipStream_t st);
 
+// 2 <= M <= 64 (k_mid.hip): the memory-bound small-batch product
+bool mid_supported(int64_t M, int64_t N, int64_t K);
+size_t mid_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_mid(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
+                      const uint16_t* scales, const uint8_t* zeros, int64_t N, int group,
+                      const float* inv_s, void* y, int ydt, int64_t ldy, void* ws, hipStream_t st);
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Compute units of the current device (cached per device).

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(1024) void k_gemv1_cu(
       float val[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        if (j0 + d >= nj) break;                     // wave-uniform: padding slot
+        if (j0 + d < nj) {                           // wave-uniform: padding slot
         float acc = 0.0f;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -348,6 +348,7 @@ __global__ __launch_bounds__(1024) void k_gemv1_cu(
           acc = __builtin_fmaf(f16_to_f32(sb[d][c]) * xc[c][2], P, acc);
         }
         val[d] = acc;
+        }
       }
       float v;
       if constexpr (D >= 3) {
@@ -368,7 +369,6 @@ __global__ __launch_bounds__(1024) void k_gemv1_cu(
       }
       j0 += D;
       if (j0 >= nj) break;                           // wave-uniform
-#pragma unroll
       for (int d = 0; d < D; ++d) load_row(d, j0 + d);
     }
   }
@@ -449,14 +449,20 @@ hipError_t gemv1_dispatch(const uint16_t* x, int64_t K, const uint32_t* qw, cons
   const int path = gemv1_path(K, N);
   const int64_t need = ((K >> 3) + 3) / 4 * 4;     // staged 8-element pieces, whole quads
   if (path == 2) {
+    // rows in flight per wave: one for K <= 4096 (the staging loads then wait
+    // behind less weight traffic), two up to 16384, four beyond (a long
+    // staging phase, with few rows per wave to cover it)
     const int nblk = awq::device_cus();
     const int64_t nks = ((K >> 5) + 127) / 128;
     const int64_t threads = nks * (16 / nks) * 64;
-    if (need <= threads)
-      return gemv1_cu_launch<DT, YDT, HAS_R, 1, 1, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nblk, 16, st);
+    if (need <= threads) {
+      if (K <= 4096)
+        return gemv1_cu_launch<DT, YDT, HAS_R, 1, 1, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nblk, 16, st);
+      return gemv1_cu_launch<DT, YDT, HAS_R, 1, 2, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nblk, 16, st);
+    }
     if (need <= 2 * threads)
-      return gemv1_cu_launch<DT, YDT, HAS_R, 2, 1, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nblk, 16, st);
-    return gemv1_cu_launch<DT, YDT, HAS_R, 4, 1, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nblk, 16, st);
+      return gemv1_cu_launch<DT, YDT, HAS_R, 2, 2, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nblk, 16, st);
+    return gemv1_cu_launch<DT, YDT, HAS_R, 4, 4, 2>(x, K, qw, scales, zeros, N, gsh, r, y, nblk, 16, st);
   }
   if (path == 0) return hipErrorInvalidValue;
   const int64_t CH = K >> 5;

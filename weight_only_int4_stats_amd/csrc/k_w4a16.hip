@@ -925,6 +925,8 @@ hipError_t w4a16_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
                           const float* r, void* y, int64_t ldy, void* ws, hipStream_t st) {
   if (M == 1 && awq::gemv1_supported(K, N))
     return awq::launch_gemv1(x, DT, K, qw, scales, zeros, N, 1 << glog, r, y, YDT, st);
+  if (awq::mid_supported(M, N, K))
+    return awq::launch_mid(x, DT, M, K, ldx, qw, scales, zeros, N, 1 << glog, r, y, YDT, ldy, ws, st);
   if (const int nblk = skinny_cu_blocks(M, N, K)) {
     // deeper ring for long K slices (few rows per block)
     const int64_t rows = (N + nblk - 1) / nblk, tiles = (rows + 15) / 16;
@@ -947,9 +949,9 @@ hipError_t w4a16_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
 namespace awq {
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int group) {
-  if (M <= 0 || N <= 0 || K <= 0 || group <= 0 || (M == 1 && gemv1_supported(K, N)) ||
-      awqk::skinny_cu_blocks(M, N, K))
-    return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || group <= 0 || (M == 1 && gemv1_supported(K, N))) return 0;
+  if (mid_supported(M, N, K)) return mid_ws_bytes(M, N, K);
+  if (awqk::skinny_cu_blocks(M, N, K)) return 0;
   return awqk::gemm_ws(nullptr, M, N, K, group).bytes;
 }
 
