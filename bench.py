@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (used under a profiler)")
+    ap.add_argument("--sections", default="c1,c3,c4,c5",
+                    help="workloads besides the 7B up-projection (always run): any of c1,c3,c4,c5")
     ap.add_argument("--no-c5", action="store_true", help="leave out the 80-layer stack")
     ap.add_argument("--c5-quantize-all", action="store_true",
                     help="quantize every layer of the 80-layer stack by the full path (minutes)")
@@ -176,6 +178,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     awq.lib()
+    sections = {x.strip() for x in args.sections.split(",") if x.strip()}
+    if args.no_c5:
+        sections.discard("c5")
     alphas = torch.from_numpy(WL.alpha_grid(20)).to(dev)
 
     def ws_for(op, M=0, N=0, K=0, T=0, na=0):
@@ -222,7 +227,7 @@ def main() -> int:
 
     # ---------------- c4: Llama-70B MLP prefill (bf16), up and down
     c4 = {}
-    for lin in ("up", "down"):
+    for lin in (("up", "down") if "c4" in sections else ()):
         wb = WL.workload(4, lin)
         print(f"setup: {wb.name}, M={wb.Ms[0]}", file=sys.stderr, flush=True)
         WB = WL.weight(wb).to(dev)
@@ -261,7 +266,7 @@ def main() -> int:
     # ---------------- c3: Llama-7B decoder layer, 8 resident copies
     print("setup: llama7b decoder layer (7 linears)", file=sys.stderr, flush=True)
     c3 = {}
-    for lin in ("q", "k", "v", "o", "gate", "up", "down"):
+    for lin in (("q", "k", "v", "o", "gate", "up", "down") if "c3" in sections else ()):
         w3 = WL.workload(3, lin)
         qd = quantize(WL.weight(w3).to(dev), WL.calibration(w3).to(dev))
         copies = [(qd["q"], qd["sc"], qd["z"])]
@@ -276,7 +281,7 @@ def main() -> int:
 
     # ---------------- c5: 80-layer Llama-70B-shaped stack
     c5 = None
-    if not args.no_c5:
+    if "c5" in sections:
         c5 = setup_c5(torch, WL, awq, dev, alphas, ws_for, args.c5_quantize_all)
 
     # ---------------- decode graphs
@@ -320,8 +325,10 @@ def main() -> int:
         capture("c5_decode_inv_s", lambda: decode_c5(False))
     torch.cuda.synchronize()
 
-    phases = ["act_stats", "search", "quantize", "gemv_m1", "gemv_m8", "gemm_prefill_up",
-              "gemm_prefill_down", "c1_pipeline"]
+    phases = ["act_stats", "search", "quantize", "gemv_m1", "gemv_m8"]
+    phases += [f"gemm_prefill_{lin}" for lin in c4]
+    if "c1" in sections:
+        phases.append("c1_pipeline")
     phases += [f"c3_{lin}_m{M}" for lin in c3 for M in C3_MS]
     if c5 is not None:
         phases += ["c5_decode_folded", "c5_decode_inv_s"]
@@ -345,12 +352,13 @@ def main() -> int:
         mark()
         graphs["gemv_m8"].replay()
         mark()
-        for lin in ("up", "down"):
+        for lin in c4:
             d = c4[lin]
             awq.awq_w4a16_gemm(d["x"], d["q"], d["sc"], d["z"], d["inv"], y=d["y"], ws=d["ws"])
             mark()
-        c1_pass()
-        mark()
+        if "c1" in sections:
+            c1_pass()
+            mark()
         for lin in c3:
             for M in C3_MS:
                 graphs[f"c3_{lin}_m{M}"].replay()
@@ -407,7 +415,7 @@ def main() -> int:
     stats_bytes = wa.T * KA * 2
     quant_bytes = NA * KA * 2 + bytes_a
     gemm = {}
-    for lin in ("up", "down"):
+    for lin in c4:
         d = c4[lin]
         flop = 2.0 * d["M"] * d["N"] * d["K"]
         ms = avg[f"gemm_prefill_{lin}"]
@@ -427,16 +435,19 @@ def main() -> int:
         "quantize": {"ms": avg["quantize"], "GB/s": quant_bytes / (avg["quantize"] * 1e-3) / 1e9},
         "gemv_m1": {"us_per_launch": gemv1_us, "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS},
         "gemv_m8": {"us_per_launch": gemv8_us, "GB/s": gemv8_gbs, "frac_hbm": gemv8_gbs / HBM_PEAK_GBS},
-        "gemm_prefill": gemm["up"],
-        "gemm_prefill_down": gemm["down"],
-        "c1_single_linear": {"us_pipeline": avg["c1_pipeline"] * 1000.0,
-                             "what": "statistics + 20-candidate search + quantize + pack + batch-1 "
-                                     "product of the 512 x 512 linear (cache-resident: a latency)"},
     }
+    if c4:
+        stages["gemm_prefill"] = gemm["up"]
+        stages["gemm_prefill_down"] = gemm["down"]
+    if "c1" in sections:
+        stages["c1_single_linear"] = {"us_pipeline": avg["c1_pipeline"] * 1000.0,
+                                      "what": "statistics + 20-candidate search + quantize + pack + "
+                                              "batch-1 product of the 512 x 512 linear "
+                                              "(cache-resident: a latency)"}
     # ---------------- c3 figures
     c3_out = {"per_linear": {}, "per_layer": {}}
     layer_bytes = sum(packed_bytes(c3[lin]["N"], c3[lin]["K"]) for lin in c3)
-    for M in C3_MS:
+    for M in (C3_MS if c3 else ()):
         tot_us = 0.0
         for lin in c3:
             us = avg[f"c3_{lin}_m{M}"] * 1000.0 / (C3_COPIES * C3_PASS)
@@ -447,7 +458,8 @@ def main() -> int:
         c3_out["per_layer"][f"M={M}"] = {"us": tot_us, "GB/s": layer_bytes / (tot_us * 1e-6) / 1e9,
                                          "frac_hbm": layer_bytes / (tot_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
     c3_out["bytes_per_layer"] = layer_bytes
-    stages["c3_decoder_layer"] = c3_out
+    if c3:
+        stages["c3_decoder_layer"] = c3_out
     # ---------------- c5 figures
     if c5 is not None:
         out5 = {"bytes": c5["bytes"], "launches": c5["launches"], "quantize": c5["quantize"]}
@@ -478,7 +490,7 @@ def main() -> int:
     mixed = {"kept_channels": n_keep, "group": 128, "bits": 4, "loss": float(Lm.cpu()[0]),
              "loss_rtn": loss_h[0], "loss_awq": loss_h[best_h],
              "loss_over_awq": float(Lm.cpu()[0]) / loss_h[best_h]}
-    up = gemm["up"]
+    up = gemm.get("up")
     out = {
         "metric": METRIC,
         "value": gemv_gbs,
@@ -507,14 +519,15 @@ def main() -> int:
                      "frac": gemv_gbs / HBM_PEAK_GBS, "traffic": measured_traffic("k_gemv1_cu"),
                      "kernel": "k_gemv1_cu (batch 1, one block per compute unit)",
                      "bytes_per_launch": bytes_a},
-        "prefill_gemm": {"bound": "mfma", "achieved": up["TFLOP/s"], "peak": FP16_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": up["frac_fp16_mfma"],
-                         "flop_per_launch": 2.0 * 2048 * 28672 * 8192, "kernel": "k_gemm"},
+        "prefill_gemm": None if up is None else {
+            "bound": "mfma", "achieved": up["TFLOP/s"], "peak": FP16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": up["frac_fp16_mfma"],
+            "flop_per_launch": 2.0 * 2048 * 28672 * 8192, "kernel": "k_gemm"},
         "stages": stages,
         "quantizer_variants": variants,
         "mixed_precision_baseline": mixed,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and c4:
         c2 = {"W": WA, "X": XA, "N": NA, "K": KA, "T": wa.T, "s": s, "inv": inv, "q": qs[0],
               "sc": scs[0], "z": zs[0], "x1": xa1}
         out["cpu_baseline"] = cpu_baseline(c2, c4)
