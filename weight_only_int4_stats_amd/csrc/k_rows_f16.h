@@ -18,8 +18,10 @@ constexpr int kRowsKeep = 8;   // 8-element chunks per thread kept in registers 
 // Activation rows -> fp16: y_row = fp16(x_row * r * 2^p_row), p_row from the
 // row's max so the row sits in fp16's normal range.  One block per row.  With
 // PERMUTE each 8-element chunk is stored as (k0,k4,k2,k6,k1,k5,k3,k7), the
-// order in which the packed-nibble unpack yields weight pairs.
-template <int DT, bool HAS_R, bool PERMUTE>
+// order in which the packed-nibble unpack yields weight pairs.  A row of up to
+// 256 KEEP chunks stays in registers between its max and its conversion (read
+// once); a longer one is read twice.
+template <int DT, bool HAS_R, bool PERMUTE, int KEEP = kRowsKeep>
 __device__ __forceinline__ void rows_f16_block(int64_t row, const uint16_t* __restrict__ src, int64_t K,
                                                int64_t ld, const float* __restrict__ r,
                                                uint16_t* __restrict__ dst, int* __restrict__ pexp) {
@@ -70,11 +72,11 @@ __device__ __forceinline__ void rows_f16_block(int64_t row, const uint16_t* __re
     return p;
   };
   float amax = 0.0f;
-  if (nch <= 256 * kRowsKeep) {
+  if (nch <= 256 * KEEP) {
     // the row stays in registers between the max and the conversion
-    float v[kRowsKeep][8];
+    float v[KEEP][8];
 #pragma unroll
-    for (int i = 0; i < kRowsKeep; ++i) {
+    for (int i = 0; i < KEEP; ++i) {
       const int64_t c = threadIdx.x + 256 * i;
       if (c < nch) {
         load8(c, v[i]);
@@ -84,7 +86,7 @@ __device__ __forceinline__ void rows_f16_block(int64_t row, const uint16_t* __re
     }
     const int p = row_exp(amax);
 #pragma unroll
-    for (int i = 0; i < kRowsKeep; ++i) {
+    for (int i = 0; i < KEEP; ++i) {
       const int64_t c = threadIdx.x + 256 * i;
       if (c < nch) store8(c, v[i], p);
     }

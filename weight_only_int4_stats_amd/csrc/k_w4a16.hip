@@ -147,14 +147,15 @@ __device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 c24, f16x2 c
 // m fastest, then n), so its ~32 concurrent blocks cover about 4 x 8 tiles.
 // The GEMM's two pre-passes in one launch (they are independent): blocks
 // 0 .. M - 1 convert activation rows, the rest build the constants.
-template <int DT, bool HAS_R>
+// KEEP: activation chunks per thread held in registers (16: rows up to 32768).
+template <int DT, bool HAS_R, int KEEP>
 __global__ __launch_bounds__(256) void k_gemm_prep(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                    int64_t ldx, const float* __restrict__ r,
                                                    uint16_t* __restrict__ xq, int* __restrict__ pm,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros, int64_t N, int64_t G,
                                                    int* __restrict__ en, uint32_t* __restrict__ ctab) {
-  if ((int64_t)blockIdx.x < M) rows_f16_block<DT, HAS_R, true>(blockIdx.x, x, K, ldx, r, xq, pm);
+  if ((int64_t)blockIdx.x < M) rows_f16_block<DT, HAS_R, true, KEEP>(blockIdx.x, x, K, ldx, r, xq, pm);
   else gemm_consts_block((int64_t)blockIdx.x - M, scales, zeros, N, G, en, ctab);
 }
 
@@ -591,8 +592,13 @@ hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
                          const uint16_t* scales, const uint8_t* zeros, int64_t N, int glog,
                          const float* r, void* y, int64_t ldy, void* ws, hipStream_t st) {
   const GemmWs w = gemm_ws(ws, M, N, K, 1 << glog);
-  hipLaunchKernelGGL((k_gemm_prep<DT, HAS_R>), dim3((unsigned)(M + (N + 63) / 64)), dim3(256), 0, st, x, M, K,
-                     ldx, r, w.xq, w.pm, scales, zeros, N, K >> glog, w.en, w.ctab);
+  const dim3 pgrid((unsigned)(M + (N + 63) / 64));
+  if (K > 256 * 8 * kRowsKeep)
+    hipLaunchKernelGGL((k_gemm_prep<DT, HAS_R, 2 * kRowsKeep>), pgrid, dim3(256), 0, st, x, M, K, ldx, r,
+                       w.xq, w.pm, scales, zeros, N, K >> glog, w.en, w.ctab);
+  else
+    hipLaunchKernelGGL((k_gemm_prep<DT, HAS_R, kRowsKeep>), pgrid, dim3(256), 0, st, x, M, K, ldx, r,
+                       w.xq, w.pm, scales, zeros, N, K >> glog, w.en, w.ctab);
   // 16-byte output stores need a 16-byte aligned y and row pitch
   const int es = YDT == DT_F32 ? 4 : 2;
   const int vec_ok = ((uintptr_t)y % 16 == 0) && ((ldy * es) % 16 == 0);
