@@ -428,6 +428,10 @@ constexpr int64_t kCuMaxK = 32768;        // per-CU kernel: 4 staged pieces per 
 constexpr int kCuMinRowsPerCu = 24;       // below this the row-block kernel is faster
 
 // Which batch-1 kernel serves (K, N): 2 = per-CU, 1 = row-block, 0 = neither.
+// The row-block kernel stages the whole activation (and 1/s: 6 bytes per
+// channel) in every block; once its blocks' staging reads exceed twice the
+// packed weights (few rows per block and a long K, as 4096 x 11008), the
+// per-CU kernel, which stages once per compute unit, is faster.
 inline int gemv1_path(int64_t K, int64_t N) {
   const int64_t cus = awq::device_cus();
   const int64_t nblk = N < cus ? N : cus;
@@ -436,7 +440,12 @@ inline int gemv1_path(int64_t K, int64_t N) {
   const int64_t nks = (CH + 127) / 128;
   const bool cu_ok = K <= kCuMaxK && CH * 80 + nks * rows_max * 4 <= 160 * 1024 &&
                      rows_max * (K >> 1) < (int64_t(1) << 31);
-  if (cu_ok && (N >= kCuMinRowsPerCu * cus || K > kRowsMaxK)) return 2;
+  const int64_t rks = (CH + 63) / 64;                            // row-block kernel's K slices
+  int64_t rnrg = rks >= 8 ? 1 : 8 / rks;
+  if (rks * rnrg > 16) rnrg = 16 / rks;
+  const int64_t rblocks = (N + 4 * rnrg - 1) / (4 * rnrg);
+  const bool rows_staging_heavy = rblocks * K * 6 > 2 * (N * K / 2);
+  if (cu_ok && (N >= kCuMinRowsPerCu * cus || K > kRowsMaxK || rows_staging_heavy)) return 2;
   if (K <= kRowsMaxK) return 1;
   return cu_ok ? 2 : 0;
 }
