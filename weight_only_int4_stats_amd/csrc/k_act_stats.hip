@@ -4,17 +4,26 @@
 // activation magnitude over a calibration set).
 //
 // The column sums are exact.  Each |x| is taken in fixed point with LSB 2^-24
-// (floor(|x| * 2^24), exact for every fp16 value), built from the 16-bit
-// pattern with integer operations (the significand shifted by the exponent),
-// accumulated per thread and across the block in 64-bit integers, and added
-// across blocks with 64-bit integer atomics (exact and order-free).  The finalisation divides once in double
-// and rounds once to float, so the result does not depend on the grid.
+// (floor(|x| * 2^24), exact for every fp16 value) and summed per thread:
+//   fp16: built from the 16-bit pattern with integer operations (the
+//         significand shifted by the exponent), summed in 64-bit integers;
+//   bf16: |x| converted to double, times 2^24, floored, summed in double --
+//         every term and partial sum is an integer below 2^53 under the
+//         precondition (column sums below 2^29), so the double sum is exact and
+//         equal to the integer one; bf16's shift-heavy integer path was the
+//         slower one (79 against 35 us on 2048 x 28672).
+// Across the block the sums are 64-bit integers, and across blocks they are
+// added with 64-bit integer atomics (exact and order-free).  The finalisation
+// divides once in double and rounds once to float, so the result does not
+// depend on the grid.
 //
 // Layout: X is [T][ldx] row-major.  A thread owns 8 consecutive columns (one
 // 128-bit load per row); a wave covers 512 columns of a row, the four waves of
 // a block take interleaved rows of the block's row range.
 #include "awq_device.h"
 #include "awq_internal.h"
+
+#include <type_traits>
 
 namespace awqk {
 
@@ -46,10 +55,19 @@ __device__ __forceinline__ uint64_t fixed24(uint32_t h) {
   }
 }
 
+// The per-thread accumulator: 64-bit integers for fp16, double for bf16.
 template <int DT>
-__device__ __forceinline__ void accum_word(uint32_t w, uint64_t& a, uint64_t& b) {
-  a += fixed24<DT>(w & 0xFFFFu);
-  b += fixed24<DT>(w >> 16);
+using Acc24 = typename std::conditional<DT == DT_F16, uint64_t, double>::type;
+
+template <int DT>
+__device__ __forceinline__ void accum_word(uint32_t w, Acc24<DT>& a, Acc24<DT>& b) {
+  if constexpr (DT == DT_F16) {
+    a += fixed24<DT>(w & 0xFFFFu);
+    b += fixed24<DT>(w >> 16);
+  } else {
+    a += floor((double)fabsf(bf16_to_f32(w & 0xFFFFu)) * 16777216.0);   // exact: power-of-two scale
+    b += floor((double)fabsf(bf16_to_f32(w >> 16)) * 16777216.0);
+  }
 }
 
 template <int DT>
@@ -70,7 +88,7 @@ __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __r
   const int64_t col = slab * kStatsCols + lane * 8;
   const int64_t r0 = chunk * rows_per_block;
   const int64_t r1 = min(T, r0 + rows_per_block);
-  uint64_t s[8];
+  Acc24<DT> s[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) s[j] = 0;
 
@@ -101,7 +119,7 @@ __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __r
 
   __shared__ uint64_t red[4][8][64];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) red[wv][j][lane] = s[j];
+  for (int j = 0; j < 8; ++j) red[wv][j][lane] = (uint64_t)s[j];   // an integer below 2^53
   __syncthreads();
   if (wv == 0 && col < K) {
 #pragma unroll
@@ -133,8 +151,10 @@ hipError_t launch_act_stats(const void* x, int dt, int64_t T, int64_t K, int64_t
   unsigned long long* acc = reinterpret_cast<unsigned long long*>(ws);
   hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, acc, K);
   const int64_t slabs = (K + kStatsCols - 1) / kStatsCols;
-  // about 4096 blocks, each row range a multiple of 4 rows x unroll
-  int64_t chunks = (4096 + slabs - 1) / slabs;
+  // about 1024 blocks (four per compute unit), each row range a multiple of
+  // 4 rows x unroll: longer row ranges mean fewer 64-bit atomics per column
+  // (4096 blocks measured 125 against 108 us on 65536 x 4096)
+  int64_t chunks = (1024 + slabs - 1) / slabs;
   const int64_t quantum = 4 * kStatsUnroll;
   const int64_t max_chunks = (T + quantum - 1) / quantum;
   if (chunks > max_chunks) chunks = max_chunks;
