@@ -141,6 +141,8 @@ def _sampled_product(M, N, K, dtype, ydt, with_r, seed):
 
 @pytest.mark.parametrize("M,N,K,dtype,ydt,with_r", [
     (2, 28672, 8192, BF16, BF16, True),        # per-CU skinny, 7 row tiles per block
+    (3, 100000, 1024, F16, F16, True),         # 25 row tiles per block: waves run two items
+    (8, 10240, 8192, F16, F16, True),          # 8 staged pieces per thread (K = 8192)
     (12, 5000, 2048, BF16, torch.float32, True),  # 3 token phases per thread
     (16, 3000, 4096, F16, F16, False),         # 16 tokens, activations fill LDS
     (5, 11008, 4096, F16, F16, True),
@@ -185,9 +187,12 @@ def test_product_special_cases():
     """q == z gives 0; a one-hot x picks the dequantized column.  The GEMV
     accumulates exact int4 x activation products, so the one-hot column is
     exact there and q == z leaves only the rounding of the zero-point sum.  The
-    matrix-core path forms each operand as one fused step * q - fp16(step * z),
-    so q == z leaves the rounding of fp16(step * z) (at most 2^-11 of it) and,
-    with power-of-two steps (step * z exact in fp16), everything is exact."""
+    matrix-core paths for 17 or more tokens form each operand as one fused
+    step * q - fp16(step * z), so q == z leaves the rounding of fp16(step * z)
+    (at most 2^-11 of it) and, with power-of-two steps (step * z exact in
+    fp16), everything is exact.  The 2..16-token product multiplies the codes
+    themselves and applies step and zero point in fp32, so its one-hot
+    columns are exact with any step."""
     N, K = 200, 1024
     words, step, z = _random_packed(N, K, 5)
     qz = np.repeat(z, 128, axis=1)
@@ -211,7 +216,10 @@ def test_product_special_cases():
     assert float(y1.abs().max()) <= bound
     pow2 = np.ldexp(np.float16(1), np.random.Generator(np.random.PCG64(8)).integers(
         -12, -5, step.shape)).astype(np.float16)
-    for M, k, st in ((1, 0, step), (1, 777, step), (33, 130, pow2), (17, 1023, pow2)):
+    # 2..16 tokens: the zero point enters the accumulator as -z sum X and the step
+    # multiplies in fp32, so a one-hot token is exact with any step
+    for M, k, st in ((1, 0, step), (1, 777, step), (33, 130, pow2), (17, 1023, pow2),
+                     (8, 5, step), (4, 1000, step), (16, 129, step)):
         x = torch.zeros((M, K), dtype=F16)
         x[:, k] = 1.0
         y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(st)),

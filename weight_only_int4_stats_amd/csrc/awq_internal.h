@@ -77,6 +77,15 @@ hipError_t launch_mid(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx,
                       const uint16_t* scales, const uint8_t* zeros, int64_t N, int group,
                       const float* inv_s, void* y, int ydt, int64_t ldy, void* ws, hipStream_t st);
 
+// 2 <= M <= 16 (k_skinny.hip): one block per compute unit with the
+// activations, steps and zero points staged in LDS; blocks (0: shape not
+// covered) and launch.  No workspace.
+int skinny_st_blocks(int64_t M, int64_t N, int64_t K, int group);
+hipError_t launch_skinny_st(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx,
+                            const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros,
+                            int64_t N, int group, const float* inv_s, void* y, int ydt, int64_t ldy,
+                            hipStream_t st);
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Compute units of the current device (cached per device).

@@ -1,0 +1,433 @@
+// W4A16 product for 2..16 tokens ("AWQ > Benefits and Practical
+// Considerations": unpack the 4-bit integers, apply the group's step and zero
+// point and the optional per-channel inverse scale, fused with the multiply).
+// At decode batch sizes the product is bound by the packed weight stream
+// ("AWQ Math", "Weight-only quantization and where it breaks"), so this kernel
+// keeps every compute unit's weight loads in flight and spends few vector
+// instructions per packed word:
+//
+//  * One block of 16 waves per compute unit; block b owns the weight rows
+//    [b N / B, (b + 1) N / B) in 16-row tiles.  With t tiles each tile's
+//    128-channel units are split into S = 16 / t slices; wave w takes the
+//    items (tile, slice) w, w + 16, ... and keeps up to kStQ units of its
+//    packed words in flight.
+//  * v_mfma_f32_16x16x32_f16 with the tokens as A (16 rows; rows past M
+//    repeat token M - 1 and their outputs are dropped) and 16 weight rows as
+//    B.  A result lane holds the outputs of the weight row whose packed words
+//    it loaded, so the group's step multiplies the product once, in fp32.
+//  * The codes reach the matrix cores as fp16 subnormals: word & 0x000F000F is
+//    q 2^-24 for nibbles 0 and 4, word & 0x00F000F0 is q 2^-20 for nibbles 1
+//    and 5, and the same masks on word >> 8 give nibbles 2, 6 and 3, 7 (one
+//    shift and four ANDs per word; the matrix cores keep fp16 subnormal
+//    inputs).  The activations staged for odd nibbles are divided by 16, so
+//    every product is X q 2^-24.
+//  * The zero point enters as each unit's starting accumulator,
+//    -z 2^-24 sum_k X_k, from per-(token, unit) sums staged with the
+//    activations, and the step is staged as D 2^24:
+//    y = sum_units (D 2^24) 2^-p (sum_k X_k q_k 2^-24 - z 2^-24 sum_k X_k).
+//  * The block stages once, in LDS: X = fp16(x r 2^p) with one power of two per
+//    (token, 128-channel unit) (max |X| in [2^13, 2^14)), in the order the
+//    unpack yields (k0,k4,k2,k6,k1,k5,k3,k7 per word); the sums and 2^-p; and
+//    the block's steps and zero points as fp32 pairs.  K <= 8192, so that every thread stages pieces
+//    of one 8-channel column and holds one 1/s vector.
+#include "awq_device.h"
+#include "awq_internal.h"
+#include "k_rows_f16.h"
+
+namespace awqk {
+
+constexpr int kStWaves = 16;
+constexpr int kStQ = 8;              // 128-channel units of packed words in flight per wave
+constexpr int kStMetaPer = 8;        // staged (step, zero point) pairs per thread
+constexpr int kStMaxPieces = 8;      // staged 8-channel activation pieces per thread
+constexpr size_t kStLdsMax = 160 * 1024;
+
+template <int YDT>
+__device__ __forceinline__ void store_yst(void* y, int64_t idx, float v) {
+  if constexpr (YDT == DT_F32) reinterpret_cast<float*>(y)[idx] = v;
+  else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)from_f32<YDT>(v);
+}
+
+// One packed word -> its 8 codes as fp16 subnormals, in the order
+// (0,4 | 2,6 | 1,5 | 3,7): q 2^-24 for the even nibbles, q 2^-20 for the odd.
+__device__ __forceinline__ u32x4 st_unpack(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  return u32x4{w & 0x000F000Fu, w8 & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x00F000F0u};
+}
+
+// This wave's LDS operations done, then every wave of the block at this point.
+__device__ __forceinline__ void st_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Byte offsets of the LDS regions.
+struct StLayout {
+  size_t sums, pinv, meta, total;
+  int meta_pitch;   // (step, zero) pairs per staged row
+};
+
+inline StLayout st_layout(int64_t M, int64_t K, int64_t rows_max, int glog) {
+  StLayout L;
+  const size_t xs = (size_t)M * (size_t)(K + 8) * 2;           // X [M][K + 8]
+  const size_t red = (size_t)kStWaves * 256 * 4;              // slices' 16 x 16 tiles (reuses X)
+  const int64_t gw = K >> glog;
+  L.meta_pitch = (int)gw + 2;                                 // rows 16 B apart across banks
+  L.sums = awq::align_up(xs > red ? xs : red, 16);
+  L.pinv = L.sums + (size_t)(glog == 6 ? K / 64 : K / 128) * 16 * 4;
+  L.meta = L.pinv + (size_t)(K / 128) * 16 * 4;
+  L.total = L.meta + (size_t)rows_max * L.meta_pitch * 8;
+  return L;
+}
+
+// Activation pieces per thread for (M, K): 1024 / (K/8) token phases of K/8
+// threads; 0 if K > 8192 or over 8 pieces.
+inline int st_pieces(int64_t M, int64_t K) {
+  const int64_t K8 = K >> 3;
+  if (K8 < 1 || K8 > 1024) return 0;
+  const int64_t per = (M + (1024 / K8) - 1) / (1024 / K8);
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= kStMaxPieces ? 8 : 0;
+}
+
+template <int DT, int YDT, bool HAS_R, int NP, bool G64>
+__global__ __launch_bounds__(1024) void k_gemm_skinny_st(
+    const uint16_t* __restrict__ x, int M, int64_t K, int64_t ldx, const float* __restrict__ r,
+    const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, int64_t N, void* __restrict__ y, int64_t ldy, int glog,
+    uint32_t o_sums, uint32_t o_pinv, uint32_t o_meta, int mp) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_st[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rl = lane & 15;
+  const int b = lane >> 4;
+  const uint32_t K8 = (uint32_t)(K >> 3);
+  const int G = (int)(K >> 7);
+  const int GW = (int)(K >> glog);
+  const int64_t KP = K + 8;
+  const int64_t r0 = (int64_t)blockIdx.x * N / gridDim.x;
+  const int nrows = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x - r0);
+  const int ntile = (nrows + 15) / 16;
+  int ksl = kStWaves / (ntile > 0 ? ntile : 1);
+  ksl = ksl < 1 ? 1 : (ksl > G ? G : ksl);
+  const int nitems = ntile * ksl;
+
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds_st);
+  float* red = reinterpret_cast<float*>(lds_st);                        // after the items
+  float* sums = reinterpret_cast<float*>(lds_st + o_sums);              // [piece][16 tokens]
+  float* pinv = reinterpret_cast<float*>(lds_st + o_pinv);              // [unit][16 tokens]
+  float2* meta = reinterpret_cast<float2*>(lds_st + o_meta);            // [row][mp]
+
+  // ---- staging loads.  Thread t takes piece k8 = t mod K/8 of the tokens
+  // t / (K/8), t / (K/8) + T, ... (T = 1024 / (K/8) token phases).  Threads
+  // past the last phase load piece 0 of token 0 and drop it (no branch around
+  // the loads).  The steps and zero points come 8 per thread: one 128-bit and
+  // one 64-bit load.
+  const uint32_t T = 1024u / K8;
+  const uint32_t tph = (uint32_t)tid / K8;
+  const uint32_t k8 = tph < T ? (uint32_t)tid - tph * K8 : 0u;
+  const uint32_t ntok = tph < T && (uint32_t)M > tph ? ((uint32_t)M - tph + T - 1) / T : 0u;
+  u32x4 sx[NP];
+  f32x4 sr0, sr1;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const uint32_t m = tph + (uint32_t)i * T;
+    sx[i] = ldg128(x + (int64_t)((uint32_t)i < ntok ? m : 0u) * ldx + (int64_t)k8 * 8);
+  }
+  if constexpr (HAS_R) {
+    sr0 = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8);
+    sr1 = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8 + 4);
+  }
+  const int nmeta = nrows * GW;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scales + r0 * GW), (short)0, nmeta * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(zeros + r0 * GW), (short)0, nmeta, kBufferWord3);
+  // thread t takes entries [e0, e0 + 8) with e0 = min(8 t, nmeta - 8), so
+  // every load lies wholly inside the block's range (nmeta >= 8); the last
+  // window overlaps its neighbour's and writes the same values
+  const bool mlive = tid * kStMetaPer < nmeta;
+  const int e0 = mlive ? (tid * kStMetaPer < nmeta - kStMetaPer ? tid * kStMetaPer : nmeta - kStMetaPer) : 0;
+  const u32x4 mst = __builtin_amdgcn_raw_buffer_load_b128(srs, mlive ? (uint32_t)e0 * 2 : kBufferOob, 0, 0);
+  const auto mze = __builtin_amdgcn_raw_buffer_load_b64(zrs, mlive ? (uint32_t)e0 : kBufferOob, 0, 0);
+
+  // ---- the first item's packed words in flight
+  const uint32_t KW = (uint32_t)(K >> 3);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qw + r0 * KW), (short)0, nrows * (int)KW * 4, kBufferWord3);
+  int it = wv;
+  int tile = 0, g0 = 0, g1 = 0;
+  auto set_item = [&](int item) {
+    tile = item / ksl;
+    const int ks = item - tile * ksl;
+    g0 = (int)((int64_t)ks * G / ksl);
+    g1 = (int)((int64_t)(ks + 1) * G / ksl);
+  };
+  const bool have = it < nitems;                 // wave-uniform
+  u32x4 wq[kStQ];
+  // unit g of the item's tile: one 128-bit chunk b of the lane's row (words
+  // 4b .. 4b + 3), or with groups of 64 the words 2b, 2b + 1 of each half
+  auto load_unit = [&](int slot, int g) {
+    const int row = tile * 16 + rl;
+    const bool ok = have && g < g1 && row < nrows;
+    const uint32_t base = (uint32_t)row * KW * 4 + (uint32_t)g * 64;
+    if constexpr (!G64) {
+      wq[slot] = __builtin_amdgcn_raw_buffer_load_b128(wrs, ok ? base + (uint32_t)b * 16 : kBufferOob, 0, kBufferNt);
+    } else {
+      const auto lo = __builtin_amdgcn_raw_buffer_load_b64(wrs, ok ? base + (uint32_t)b * 8 : kBufferOob, 0, kBufferNt);
+      const auto hi = __builtin_amdgcn_raw_buffer_load_b64(wrs, ok ? base + 32 + (uint32_t)b * 8 : kBufferOob, 0, kBufferNt);
+      wq[slot] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+  set_item(have ? it : 0);
+#pragma unroll
+  for (int d = 0; d < kStQ; ++d) load_unit(d, g0 + d);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- the block's steps (times 2^24, exact: it undoes the codes' 2^-24)
+  // and zero points
+#pragma unroll
+  for (int j = 0; j < kStMetaPer; ++j) {
+    const int e = e0 + j;
+    if (mlive) {
+      const int row = e / GW;
+      const uint32_t sb = (mst[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      const uint32_t zb = (mze[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+      meta[row * mp + (e - row * GW)] = make_float2(ldexpf(f16_to_f32(sb), 24), (float)zb);
+    }
+  }
+
+  // ---- X = fp16(x r 2^p), p per (token, 128-channel unit) from the unit's
+  // max |x r| (max |X| in [2^13, 2^14)); the odd nibbles' channels get
+  // 2^(p - 4).  The 16 pieces of a unit sit in 16 consecutive lanes.  Beside
+  // X: 2^-24 sum X per piece of the zero point's granularity, and 2^-p.
+  const int npl = (int)(((uint32_t)M + T - 1) / T);   // pieces any thread stages
+  const f16x2 one2 = as_f16x2(0x3C003C00u), sixteen2 = as_f16x2(0x4C004C00u);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    if (i >= npl) break;                         // uniform
+    const uint32_t m = tph + (uint32_t)i * T;
+    const bool live = (uint32_t)i < ntok;
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = lo_f32<DT>(sx[i][q]);
+      v[2 * q + 1] = hi_f32<DT>(sx[i][q]);
+    }
+    if constexpr (HAS_R) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] *= sr0[q];
+        v[4 + q] *= sr1[q];
+      }
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(v[q]));
+    am = fmaxf(am, quad_xor1(am));
+    am = fmaxf(am, quad_xor2(am));
+    am = fmaxf(am, dpp_f<0x141>(am));            // row_half_mirror
+    am = fmaxf(am, dpp_f<0x140>(am));            // row_mirror: the unit's max
+    const int p = pow2_exp_for(am);
+    uint32_t h[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) h[c] = f32_to_f16_bits(ldexpf(v[c], (c & 1) ? p - 4 : p));
+    u32x4 o;
+    o[0] = h[0] | (h[4] << 16);
+    o[1] = h[2] | (h[6] << 16);
+    o[2] = h[1] | (h[5] << 16);
+    o[3] = h[3] | (h[7] << 16);
+    // sum X of the piece, exactly as the products see the operands
+    float sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[0]), one2, 0.0f, false);
+    sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[1]), one2, sx8, false);
+    sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[2]), sixteen2, sx8, false);
+    sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[3]), sixteen2, sx8, false);
+    float s = live ? ldexpf(sx8, -24) : 0.0f;
+    s += quad_xor1(s);
+    s += quad_xor2(s);
+    s += dpp_f<0x141>(s);                        // 8 channels x 8 lanes: a 64-channel half unit
+    if constexpr (!G64) s += dpp_f<0x140>(s);     // 16 lanes: the 128-channel unit
+    if (live) {
+      *reinterpret_cast<u32x4*>(xs + (int64_t)m * KP + (int64_t)k8 * 8) = o;
+      if ((lane & (G64 ? 7 : 15)) == 0) sums[(k8 >> (G64 ? 3 : 4)) * 16 + m] = s;
+      if ((lane & 15) == 0) pinv[(k8 >> 4) * 16 + m] = ldexpf(1.0f, -p);
+    }
+  }
+  st_sync();
+
+  // ---- items
+  const int tok = rl < M ? rl : M - 1;           // rows past M repeat a token; dropped
+  const uint8_t* xrow = reinterpret_cast<const uint8_t*>(xs) + (size_t)tok * (size_t)KP * 2;
+  const int gsh = glog - 7;                       // unit -> group (groups of 128, 256)
+  // one item on the ring already in flight; refills run past its end (out of
+  // range, no traffic).  Per unit: part = -z 2^-24 sum X + sum X q 2^-24 on
+  // the matrix cores, then acc += (D 2^24) 2^-p part.
+  auto run_item = [&]() {
+    const int rowc = tile * 16 + rl < nrows ? tile * 16 + rl : nrows - 1;
+    const float2* mrow = meta + rowc * mp;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int gb = g0; gb < g1; gb += kStQ) {
+#pragma unroll
+      for (int d = 0; d < kStQ; ++d) {
+        const int g = gb + d;
+        if (g < g1) {                             // wave-uniform
+          u32x4 xa[4];
+          const f32x4 pv = *reinterpret_cast<const f32x4*>(pinv + g * 16 + 4 * b);
+          if constexpr (!G64) {
+            const uint8_t* p = xrow + (size_t)(128 * g + 32 * b) * 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4*>(p + 16 * i);
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(sums + g * 16 + 4 * b);
+            const float2 md = mrow[g >> gsh];
+            f32x4 part;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) part[v] = -md.y * sv[v];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part = mfma16h(xa[i], st_unpack(wq[d][i]), part);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(md.x * pv[v], part[v], acc[v]);
+          } else {
+            const uint8_t* p = xrow + (size_t)(128 * g + 16 * b) * 2;
+            xa[0] = *reinterpret_cast<const u32x4*>(p);
+            xa[1] = *reinterpret_cast<const u32x4*>(p + 16);
+            xa[2] = *reinterpret_cast<const u32x4*>(p + 128);
+            xa[3] = *reinterpret_cast<const u32x4*>(p + 144);
+            const f32x4 sv0 = *reinterpret_cast<const f32x4*>(sums + (2 * g) * 16 + 4 * b);
+            const f32x4 sv1 = *reinterpret_cast<const f32x4*>(sums + (2 * g + 1) * 16 + 4 * b);
+            const f32x4 md = *reinterpret_cast<const f32x4*>(mrow + 2 * g);   // (D0, z0, D1, z1)
+            f32x4 p0, p1;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              p0[v] = -md[1] * sv0[v];
+              p1[v] = -md[3] * sv1[v];
+            }
+            p0 = mfma16h(xa[0], st_unpack(wq[d][0]), p0);
+            p0 = mfma16h(xa[1], st_unpack(wq[d][1]), p0);
+            p1 = mfma16h(xa[2], st_unpack(wq[d][2]), p1);
+            p1 = mfma16h(xa[3], st_unpack(wq[d][3]), p1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[v] = __builtin_fmaf(md[2] * pv[v], p1[v], __builtin_fmaf(md[0] * pv[v], p0[v], acc[v]));
+          }
+        }
+        load_unit(d, g + kStQ);
+      }
+    }
+    return acc;
+  };
+  // 16 x 16 result layout: weight row = lane % 16, tokens 4 (lane / 16) + v
+  auto store_direct = [&](const f32x4& a) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = 4 * b + v;
+      if (t < M && tile * 16 + rl < nrows) store_yst<YDT>(y, (int64_t)t * ldy + r0 + tile * 16 + rl, a[v]);
+    }
+  };
+  // The first item runs on the words loaded before the staging; later items
+  // (only when ksl == 1) load their own.  Two copies of the item code keep the
+  // ring in the same registers from the loads to the products.
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (have) {
+    acc = run_item();
+    if (ksl == 1) store_direct(acc);
+  }
+  if (ksl == 1) {
+    for (it = wv + kStWaves; it < nitems; it += kStWaves) {
+      set_item(it);
+#pragma unroll
+      for (int d = 0; d < kStQ; ++d) load_unit(d, g0 + d);
+      store_direct(run_item());
+    }
+  }
+  if (ksl > 1) {
+    // one item per wave: the slices of a tile meet in LDS in slice order
+    st_sync();                                    // every wave done with X
+    if (wv < nitems) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wv * 256 + (4 * b + v) * 16 + rl] = acc[v];
+    }
+    st_sync();
+    for (int t = tid; t < ntile * 256; t += 1024) {
+      const int tl = t >> 8, tk = (t >> 4) & 15, row = t & 15;
+      float tot = 0.0f;
+      for (int ks = 0; ks < ksl; ++ks) tot += red[(tl * ksl + ks) * 256 + tk * 16 + row];
+      if (tk < M && tl * 16 + row < nrows) store_yst<YDT>(y, (int64_t)tk * ldy + r0 + tl * 16 + row, tot);
+    }
+  }
+}
+
+template <int DT, int YDT, bool HAS_R>
+hipError_t st_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint32_t* qw,
+                       const uint16_t* scales, const uint8_t* zeros, int64_t N, int glog, const float* r,
+                       void* y, int64_t ldy, int nblk, hipStream_t st) {
+  const int64_t rows_max = (N + nblk - 1) / nblk;
+  const StLayout L = st_layout(M, K, rows_max, glog);
+  size_t lds = L.total;
+  if (lds < 81 * 1024) lds = 81 * 1024;           // one block per compute unit
+  const int np = st_pieces(M, K);
+  const dim3 grid((unsigned)nblk), block(1024);
+#define AWQ_ST(NP, G64)                                                                              \
+  hipLaunchKernelGGL((k_gemm_skinny_st<DT, YDT, HAS_R, NP, G64>), grid, block, lds, st, x, (int)M, K, ldx, \
+                     r, qw, scales, zeros, N, y, ldy, glog, (uint32_t)L.sums, (uint32_t)L.pinv,       \
+                     (uint32_t)L.meta, L.meta_pitch)
+#define AWQ_STG(NP) \
+  if (glog == 6) AWQ_ST(NP, true); else AWQ_ST(NP, false)
+  if (np == 1) AWQ_STG(1);
+  else if (np == 2) AWQ_STG(2);
+  else if (np == 4) AWQ_STG(4);
+  else AWQ_STG(8);
+#undef AWQ_STG
+#undef AWQ_ST
+  return hipGetLastError();
+}
+
+}  // namespace awqk
+
+namespace awq {
+
+int skinny_st_blocks(int64_t M, int64_t N, int64_t K, int group) {
+  using namespace awqk;
+  const int glog = group == 64 ? 6 : group == 128 ? 7 : group == 256 ? 8 : -1;
+  if (glog < 0 || M < 2 || M > 16 || N < 1 || K % 128 != 0 || K % group != 0 || st_pieces(M, K) == 0)
+    return 0;
+  const int64_t cus = device_cus();
+  const int64_t nblk = N < cus ? N : cus;
+  const int64_t rows_max = (N + nblk - 1) / nblk;
+  // every block stages between 8 and 8192 (step, zero point) pairs
+  if (rows_max * (K >> glog) > 1024 * kStMetaPer || (N / nblk) * (K >> glog) < kStMetaPer) return 0;
+  if (rows_max * (K >> 1) >= (int64_t(1) << 31)) return 0;
+  if (st_layout(M, K, rows_max, glog).total > kStLdsMax) return 0;
+  return (int)nblk;
+}
+
+hipError_t launch_skinny_st(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx,
+                            const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros,
+                            int64_t N, int group, const float* inv_s, void* y, int ydt, int64_t ldy,
+                            hipStream_t st) {
+  using namespace awqk;
+  const int nblk = skinny_st_blocks(M, N, K, group);
+  if (nblk == 0) return hipErrorInvalidValue;
+  const int glog = group == 64 ? 6 : group == 128 ? 7 : 8;
+  const uint16_t* xp = (const uint16_t*)x;
+#define AWQ_SD(XT, YT)                                                                                \
+  return inv_s ? st_dispatch<XT, YT, true>(xp, M, K, ldx, qw, scales, zeros, N, glog, inv_s, y, ldy, nblk, st) \
+               : st_dispatch<XT, YT, false>(xp, M, K, ldx, qw, scales, zeros, N, glog, inv_s, y, ldy, nblk, st)
+  if (xdt == DT_F16) {
+    if (ydt == DT_F16) AWQ_SD(DT_F16, DT_F16);
+    if (ydt == DT_BF16) AWQ_SD(DT_F16, DT_BF16);
+    AWQ_SD(DT_F16, DT_F32);
+  }
+  if (ydt == DT_F16) AWQ_SD(DT_BF16, DT_F16);
+  if (ydt == DT_BF16) AWQ_SD(DT_BF16, DT_BF16);
+  AWQ_SD(DT_BF16, DT_F32);
+#undef AWQ_SD
+}
+
+}  // namespace awq
