@@ -28,8 +28,15 @@
 //  * The block stages once, in LDS: X = fp16(x r 2^p) with one power of two per
 //    (token, 128-channel unit) (max |X| in [2^13, 2^14)), in the order the
 //    unpack yields (k0,k4,k2,k6,k1,k5,k3,k7 per word); the sums and 2^-p; and
-//    the block's steps and zero points as fp32 pairs.  K <= 8192, so that every thread stages pieces
-//    of one 8-channel column and holds one 1/s vector.
+//    the block's steps and zero points as fp32 pairs.  K <= 8192, so that
+//    every thread stages pieces of one 8-channel column and holds one 1/s
+//    vector.
+//  * A wave's instructions issue in order, and the memory pipeline holds a
+//    wave at a load's issue while the weight stream flows, so a wave that
+//    issues its weight loads first cannot stage until the stream has mostly
+//    passed.  For blocks of two or more tiles, waves 8..15 therefore issue
+//    their weight loads at once and stage nothing, while waves 0..7 stage
+//    everything and then issue theirs.
 #include "awq_device.h"
 #include "awq_internal.h"
 #include "k_rows_f16.h"
@@ -87,16 +94,24 @@ inline StLayout st_layout(int64_t M, int64_t K, int64_t rows_max, int glog) {
   return L;
 }
 
-// Activation pieces per thread for (M, K): 1024 / (K/8) token phases of K/8
-// threads; 0 if K > 8192 or over 8 pieces.
-inline int st_pieces(int64_t M, int64_t K) {
+// Activation pieces per staging thread for (M, K) with nthr staging threads:
+// nthr / (K/8) token phases of K/8 threads; 0 if K/8 > nthr or over 8 pieces.
+inline int st_pieces(int64_t M, int64_t K, int64_t nthr = 1024) {
   const int64_t K8 = K >> 3;
-  if (K8 < 1 || K8 > 1024) return 0;
-  const int64_t per = (M + (1024 / K8) - 1) / (1024 / K8);
+  if (K8 < 1 || K8 > nthr) return 0;
+  const int64_t per = (M + (nthr / K8) - 1) / (nthr / K8);
   return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= kStMaxPieces ? 8 : 0;
 }
 
-template <int DT, int YDT, bool HAS_R, int NP, bool G64>
+// Whether waves 8..15 only load weights while waves 0..7 stage: blocks of more
+// than one 16-row tile (with one tile the 16 waves' items are short and the
+// staging on half the waves costs more than it hides), groups of 128 or 256,
+// the pieces fit 512 threads, at most 4096 (step, zero point) pairs.
+inline bool st_split(int64_t M, int64_t K, int64_t rows_max, int glog) {
+  return rows_max > 16 && glog != 6 && st_pieces(M, K, 512) != 0 && rows_max * (K >> glog) <= 512 * kStMetaPer;
+}
+
+template <int DT, int YDT, bool HAS_R, int NP, bool G64, bool SPLIT>
 __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
     const uint16_t* __restrict__ x, int M, int64_t K, int64_t ldx, const float* __restrict__ r,
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
@@ -125,40 +140,12 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   float* pinv = reinterpret_cast<float*>(lds_st + o_pinv);              // [unit][16 tokens]
   float2* meta = reinterpret_cast<float2*>(lds_st + o_meta);            // [row][mp]
 
-  // ---- staging loads.  Thread t takes piece k8 = t mod K/8 of the tokens
-  // t / (K/8), t / (K/8) + T, ... (T = 1024 / (K/8) token phases).  Threads
-  // past the last phase load piece 0 of token 0 and drop it (no branch around
-  // the loads).  The steps and zero points come 8 per thread: one 128-bit and
-  // one 64-bit load.
-  const uint32_t T = 1024u / K8;
+  const int nmeta = nrows * GW;
+  const uint32_t T = (SPLIT ? 512u : 1024u) / K8;
   const uint32_t tph = (uint32_t)tid / K8;
   const uint32_t k8 = tph < T ? (uint32_t)tid - tph * K8 : 0u;
   const uint32_t ntok = tph < T && (uint32_t)M > tph ? ((uint32_t)M - tph + T - 1) / T : 0u;
-  u32x4 sx[NP];
-  f32x4 sr0, sr1;
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const uint32_t m = tph + (uint32_t)i * T;
-    sx[i] = ldg128(x + (int64_t)((uint32_t)i < ntok ? m : 0u) * ldx + (int64_t)k8 * 8);
-  }
-  if constexpr (HAS_R) {
-    sr0 = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8);
-    sr1 = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8 + 4);
-  }
-  const int nmeta = nrows * GW;
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(scales + r0 * GW), (short)0, nmeta * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(zeros + r0 * GW), (short)0, nmeta, kBufferWord3);
-  // thread t takes entries [e0, e0 + 8) with e0 = min(8 t, nmeta - 8), so
-  // every load lies wholly inside the block's range (nmeta >= 8); the last
-  // window overlaps its neighbour's and writes the same values
-  const bool mlive = tid * kStMetaPer < nmeta;
-  const int e0 = mlive ? (tid * kStMetaPer < nmeta - kStMetaPer ? tid * kStMetaPer : nmeta - kStMetaPer) : 0;
-  const u32x4 mst = __builtin_amdgcn_raw_buffer_load_b128(srs, mlive ? (uint32_t)e0 * 2 : kBufferOob, 0, 0);
-  const auto mze = __builtin_amdgcn_raw_buffer_load_b64(zrs, mlive ? (uint32_t)e0 : kBufferOob, 0, 0);
-
-  // ---- the first item's packed words in flight
+  // ---- the first item's packed words
   const uint32_t KW = (uint32_t)(K >> 3);
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(qw + r0 * KW), (short)0, nrows * (int)KW * 4, kBufferWord3);
@@ -174,91 +161,146 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   u32x4 wq[kStQ];
   // unit g of the item's tile: one 128-bit chunk b of the lane's row (words
   // 4b .. 4b + 3), or with groups of 64 the words 2b, 2b + 1 of each half
+  // Rows past the block's last lie past the descriptor's range and read as
+  // zeros by themselves, so the only choice left is the wave-uniform one (a
+  // unit outside the item), which keeps the loads free of branches.
+  const uint32_t lane_off = (uint32_t)rl * KW * 4 + (uint32_t)b * (G64 ? 8 : 16);
   auto load_unit = [&](int slot, int g) {
-    const int row = tile * 16 + rl;
-    const bool ok = have && g < g1 && row < nrows;
-    const uint32_t base = (uint32_t)row * KW * 4 + (uint32_t)g * 64;
+    // the unit's wave-uniform offset, or 2^31 (past any range) outside the
+    // item: a scalar choice, the load itself unconditional
+    const bool ok = have && g < g1;
+    const uint32_t uoff = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)(tile * 16) * KW * 4 + (uint32_t)g * 64 : kBufferOob);
+    const uint32_t off = lane_off + uoff;
     if constexpr (!G64) {
-      wq[slot] = __builtin_amdgcn_raw_buffer_load_b128(wrs, ok ? base + (uint32_t)b * 16 : kBufferOob, 0, kBufferNt);
+      wq[slot] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, kBufferNt);
     } else {
-      const auto lo = __builtin_amdgcn_raw_buffer_load_b64(wrs, ok ? base + (uint32_t)b * 8 : kBufferOob, 0, kBufferNt);
-      const auto hi = __builtin_amdgcn_raw_buffer_load_b64(wrs, ok ? base + 32 + (uint32_t)b * 8 : kBufferOob, 0, kBufferNt);
+      const auto lo = __builtin_amdgcn_raw_buffer_load_b64(wrs, off, 0, kBufferNt);
+      const auto hi = __builtin_amdgcn_raw_buffer_load_b64(wrs, off + 32, 0, kBufferNt);
       wq[slot] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   };
-  set_item(have ? it : 0);
+  auto issue_weights = [&]() {
+    set_item(have ? it : 0);
 #pragma unroll
-  for (int d = 0; d < kStQ; ++d) load_unit(d, g0 + d);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- the block's steps (times 2^24, exact: it undoes the codes' 2^-24)
-  // and zero points
+    for (int d = 0; d < kStQ; ++d) load_unit(d, g0 + d);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // ---- staging: its loads, then mid() (the weights' issue when every wave
+  // stages), then the conversion.  Thread t takes piece k8 = t mod K/8 of the
+  // tokens t / (K/8), t / (K/8) + T, ... (T = 1024 / (K/8) token phases, or
+  // 512 / (K/8) when only waves 0..7 stage).  Threads past the last phase load
+  // piece 0 of token 0 and drop it (no branch around the loads).  The steps
+  // and zero points come 8 per thread: one 128-bit and one 64-bit load.
+  auto stage = [&](auto mid) {
+    u32x4 sx[NP];
+    f32x4 sr0, sr1;
 #pragma unroll
-  for (int j = 0; j < kStMetaPer; ++j) {
-    const int e = e0 + j;
-    if (mlive) {
-      const int row = e / GW;
-      const uint32_t sb = (mst[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      const uint32_t zb = (mze[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-      meta[row * mp + (e - row * GW)] = make_float2(ldexpf(f16_to_f32(sb), 24), (float)zb);
-    }
-  }
-
-  // ---- X = fp16(x r 2^p), p per (token, 128-channel unit) from the unit's
-  // max |x r| (max |X| in [2^13, 2^14)); the odd nibbles' channels get
-  // 2^(p - 4).  The 16 pieces of a unit sit in 16 consecutive lanes.  Beside
-  // X: 2^-24 sum X per piece of the zero point's granularity, and 2^-p.
-  const int npl = (int)(((uint32_t)M + T - 1) / T);   // pieces any thread stages
-  const f16x2 one2 = as_f16x2(0x3C003C00u), sixteen2 = as_f16x2(0x4C004C00u);
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    if (i >= npl) break;                         // uniform
-    const uint32_t m = tph + (uint32_t)i * T;
-    const bool live = (uint32_t)i < ntok;
-    float v[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = lo_f32<DT>(sx[i][q]);
-      v[2 * q + 1] = hi_f32<DT>(sx[i][q]);
+    for (int i = 0; i < NP; ++i) {
+      const uint32_t m = tph + (uint32_t)i * T;
+      sx[i] = ldg128(x + (int64_t)((uint32_t)i < ntok ? m : 0u) * ldx + (int64_t)k8 * 8);
     }
     if constexpr (HAS_R) {
+      sr0 = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8);
+      sr1 = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8 + 4);
+    }
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(scales + r0 * GW), (short)0, nmeta * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(zeros + r0 * GW), (short)0, nmeta, kBufferWord3);
+    // thread t takes entries [e0, e0 + 8) with e0 = min(8 t, nmeta - 8), so
+    // every load lies wholly inside the block's range (nmeta >= 8); the last
+    // window overlaps its neighbour's and writes the same values
+    const bool mlive = tid * kStMetaPer < nmeta;
+    const int e0 = mlive ? (tid * kStMetaPer < nmeta - kStMetaPer ? tid * kStMetaPer : nmeta - kStMetaPer) : 0;
+    const u32x4 mst = __builtin_amdgcn_raw_buffer_load_b128(srs, mlive ? (uint32_t)e0 * 2 : kBufferOob, 0, 0);
+    const auto mze = __builtin_amdgcn_raw_buffer_load_b64(zrs, mlive ? (uint32_t)e0 : kBufferOob, 0, 0);
+
+    mid();
+
+
+    // ---- the block's steps (times 2^24, exact: it undoes the codes' 2^-24)
+    // and zero points
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[q] *= sr0[q];
-        v[4 + q] *= sr1[q];
+    for (int j = 0; j < kStMetaPer; ++j) {
+      const int e = e0 + j;
+      if (mlive) {
+        const int row = e / GW;
+        const uint32_t sb = (mst[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        const uint32_t zb = (mze[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+        meta[row * mp + (e - row * GW)] = make_float2(ldexpf(f16_to_f32(sb), 24), (float)zb);
       }
     }
-    float am = 0.0f;
+
+    // ---- X = fp16(x r 2^p), p per (token, 128-channel unit) from the unit's
+    // max |x r| (max |X| in [2^13, 2^14)); the odd nibbles' channels get
+    // 2^(p - 4).  The 16 pieces of a unit sit in 16 consecutive lanes.  Beside
+    // X: 2^-24 sum X per piece of the zero point's granularity, and 2^-p.
+    const int npl = (int)(((uint32_t)M + T - 1) / T);   // pieces any thread stages
+    const f16x2 one2 = as_f16x2(0x3C003C00u), sixteen2 = as_f16x2(0x4C004C00u);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(v[q]));
-    am = fmaxf(am, quad_xor1(am));
-    am = fmaxf(am, quad_xor2(am));
-    am = fmaxf(am, dpp_f<0x141>(am));            // row_half_mirror
-    am = fmaxf(am, dpp_f<0x140>(am));            // row_mirror: the unit's max
-    const int p = pow2_exp_for(am);
-    uint32_t h[8];
+    for (int i = 0; i < NP; ++i) {
+      if (i >= npl) break;                         // uniform
+      const uint32_t m = tph + (uint32_t)i * T;
+      const bool live = (uint32_t)i < ntok;
+      float v[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) h[c] = f32_to_f16_bits(ldexpf(v[c], (c & 1) ? p - 4 : p));
-    u32x4 o;
-    o[0] = h[0] | (h[4] << 16);
-    o[1] = h[2] | (h[6] << 16);
-    o[2] = h[1] | (h[5] << 16);
-    o[3] = h[3] | (h[7] << 16);
-    // sum X of the piece, exactly as the products see the operands
-    float sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[0]), one2, 0.0f, false);
-    sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[1]), one2, sx8, false);
-    sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[2]), sixteen2, sx8, false);
-    sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[3]), sixteen2, sx8, false);
-    float s = live ? ldexpf(sx8, -24) : 0.0f;
-    s += quad_xor1(s);
-    s += quad_xor2(s);
-    s += dpp_f<0x141>(s);                        // 8 channels x 8 lanes: a 64-channel half unit
-    if constexpr (!G64) s += dpp_f<0x140>(s);     // 16 lanes: the 128-channel unit
-    if (live) {
-      *reinterpret_cast<u32x4*>(xs + (int64_t)m * KP + (int64_t)k8 * 8) = o;
-      if ((lane & (G64 ? 7 : 15)) == 0) sums[(k8 >> (G64 ? 3 : 4)) * 16 + m] = s;
-      if ((lane & 15) == 0) pinv[(k8 >> 4) * 16 + m] = ldexpf(1.0f, -p);
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = lo_f32<DT>(sx[i][q]);
+        v[2 * q + 1] = hi_f32<DT>(sx[i][q]);
+      }
+      if constexpr (HAS_R) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] *= sr0[q];
+          v[4 + q] *= sr1[q];
+        }
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(v[q]));
+      am = fmaxf(am, quad_xor1(am));
+      am = fmaxf(am, quad_xor2(am));
+      am = fmaxf(am, dpp_f<0x141>(am));            // row_half_mirror
+      am = fmaxf(am, dpp_f<0x140>(am));            // row_mirror: the unit's max
+      const int p = pow2_exp_for(am);
+      uint32_t h[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) h[c] = f32_to_f16_bits(ldexpf(v[c], (c & 1) ? p - 4 : p));
+      u32x4 o;
+      o[0] = h[0] | (h[4] << 16);
+      o[1] = h[2] | (h[6] << 16);
+      o[2] = h[1] | (h[5] << 16);
+      o[3] = h[3] | (h[7] << 16);
+      // sum X of the piece, exactly as the products see the operands
+      float sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[0]), one2, 0.0f, false);
+      sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[1]), one2, sx8, false);
+      sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[2]), sixteen2, sx8, false);
+      sx8 = __builtin_amdgcn_fdot2(as_f16x2(o[3]), sixteen2, sx8, false);
+      float s = live ? ldexpf(sx8, -24) : 0.0f;
+      s += quad_xor1(s);
+      s += quad_xor2(s);
+      s += dpp_f<0x141>(s);                        // 8 channels x 8 lanes: a 64-channel half unit
+      if constexpr (!G64) s += dpp_f<0x140>(s);     // 16 lanes: the 128-channel unit
+      if (live) {
+        *reinterpret_cast<u32x4*>(xs + (int64_t)m * KP + (int64_t)k8 * 8) = o;
+        if ((lane & (G64 ? 7 : 15)) == 0) sums[(k8 >> (G64 ? 3 : 4)) * 16 + m] = s;
+        if ((lane & 15) == 0) pinv[(k8 >> 4) * 16 + m] = ldexpf(1.0f, -p);
+      }
     }
+  };
+  // With SPLIT, waves 8..15 issue their weight loads at once and stage
+  // nothing, while waves 0..7 stage every activation piece and then issue
+  // theirs: a wave held at a load's issue by the memory pipeline does not
+  // delay the conversion, and half of the weight stream overlaps it.
+  if constexpr (SPLIT) {
+    if (wv < 8) {
+      stage([] {});
+      issue_weights();
+    } else {
+      issue_weights();
+    }
+  } else {
+    stage(issue_weights);
   }
   st_sync();
 
@@ -371,14 +413,15 @@ hipError_t st_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, con
   const StLayout L = st_layout(M, K, rows_max, glog);
   size_t lds = L.total;
   if (lds < 81 * 1024) lds = 81 * 1024;           // one block per compute unit
-  const int np = st_pieces(M, K);
+  const bool split = st_split(M, K, rows_max, glog);
+  const int np = split ? st_pieces(M, K, 512) : st_pieces(M, K);
   const dim3 grid((unsigned)nblk), block(1024);
-#define AWQ_ST(NP, G64)                                                                              \
-  hipLaunchKernelGGL((k_gemm_skinny_st<DT, YDT, HAS_R, NP, G64>), grid, block, lds, st, x, (int)M, K, ldx, \
-                     r, qw, scales, zeros, N, y, ldy, glog, (uint32_t)L.sums, (uint32_t)L.pinv,       \
+#define AWQ_ST(NP, G64, SPLIT)                                                                       \
+  hipLaunchKernelGGL((k_gemm_skinny_st<DT, YDT, HAS_R, NP, G64, SPLIT>), grid, block, lds, st, x, (int)M, K, \
+                     ldx, r, qw, scales, zeros, N, y, ldy, glog, (uint32_t)L.sums, (uint32_t)L.pinv,   \
                      (uint32_t)L.meta, L.meta_pitch)
 #define AWQ_STG(NP) \
-  if (glog == 6) AWQ_ST(NP, true); else AWQ_ST(NP, false)
+  if (glog == 6) AWQ_ST(NP, true, false); else if (split) AWQ_ST(NP, false, true); else AWQ_ST(NP, false, false)
   if (np == 1) AWQ_STG(1);
   else if (np == 2) AWQ_STG(2);
   else if (np == 4) AWQ_STG(4);
