@@ -28,7 +28,11 @@ calibration tokens, quantize + pack) once, timed apart from the steps; layers
 
 value = effective HBM GB/s of the c2 batch-1 GEMV: packed bytes (codes + fp16
         steps + uint8 zero points, 0.5234 B per weight) per launch / average
-        launch time, measured with HIP events on the launch stream.
+        launch time, measured with HIP events on the launch stream.  Beside it,
+        roofline.read_ceiling: a plain streaming read of the same bytes per
+        launch (awq_read_stream), 128 launches over 32 resident buffers in one
+        graph, timed in the same steps: the rate a launch of that size reaches
+        on this chip.
 All inputs are seeded synthetic tensors (workloads module) resident in HBM.
 """
 from __future__ import annotations
@@ -315,6 +319,39 @@ def main() -> int:
             fn()
         graphs[name] = g
 
+    # The ceiling the batch-1 line is compared with: a plain streaming read of
+    # the same bytes per launch (awq_read_stream), over as many resident
+    # buffers and launches per graph; the launch shape is the best of a short
+    # untimed sweep.
+    rd_bytes = packed_bytes(NA, KA)
+    rd_bufs = [torch.empty(rd_bytes // 4, dtype=torch.int32, device=dev) for _ in range(N_ROT)]
+    rd_xor = torch.empty(4096, dtype=torch.int32, device=dev)
+
+    def read_pass(blocks, unroll):
+        for _ in range(N_PASS):
+            for b in rd_bufs:
+                awq.awq_read_stream(b, blocks, unroll, block_xor=rd_xor)
+
+    rd_best = None
+    for blocks in (256, 512, 1024, 2048):
+        for unroll in (2, 4, 8):
+            read_pass(blocks, unroll)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                read_pass(blocks, unroll)
+            ts = []
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            if rd_best is None or min(ts) < rd_best[0]:
+                rd_best = (min(ts), blocks, unroll)
+            del g
+    capture("read_ceiling", lambda: read_pass(rd_best[1], rd_best[2]))
     capture("gemv_m1", lambda: decode_c2(xa1, y1))
     capture("gemv_m8", lambda: decode_c2(xa8, y8))
     for lin in c3:
@@ -325,7 +362,7 @@ def main() -> int:
         capture("c5_decode_inv_s", lambda: decode_c5(False))
     torch.cuda.synchronize()
 
-    phases = ["act_stats", "search", "quantize", "gemv_m1", "gemv_m8"]
+    phases = ["act_stats", "search", "quantize", "gemv_m1", "gemv_m8", "read_ceiling"]
     phases += [f"gemm_prefill_{lin}" for lin in c4]
     if "c1" in sections:
         phases.append("c1_pipeline")
@@ -351,6 +388,8 @@ def main() -> int:
         graphs["gemv_m1"].replay()
         mark()
         graphs["gemv_m8"].replay()
+        mark()
+        graphs["read_ceiling"].replay()
         mark()
         for lin in c4:
             d = c4[lin]
@@ -398,6 +437,8 @@ def main() -> int:
     gemv8_us = avg["gemv_m8"] * 1000.0 / (N_ROT * N_PASS)
     gemv_gbs = bytes_a / (gemv1_us * 1e-6) / 1e9
     gemv8_gbs = bytes_a / (gemv8_us * 1e-6) / 1e9
+    read_us = avg["read_ceiling"] * 1000.0 / (N_ROT * N_PASS)
+    read_gbs = rd_bytes / (read_us * 1e-6) / 1e9
     # matrix-core operations the search executes: the direct form contracts
     # over the tokens per candidate; the Gram form (taken by the library when
     # it needs under half of those, see awq_search_scales in include/awq.h)
@@ -433,8 +474,16 @@ def main() -> int:
                    "loss_rtn": loss_h[0], "loss_awq": loss_h[best_h], "alpha": float(alphas_h[best_h]),
                    "rtn_over_awq": loss_h[0] / loss_h[best_h]},
         "quantize": {"ms": avg["quantize"], "GB/s": quant_bytes / (avg["quantize"] * 1e-3) / 1e9},
-        "gemv_m1": {"us_per_launch": gemv1_us, "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS},
-        "gemv_m8": {"us_per_launch": gemv8_us, "GB/s": gemv8_gbs, "frac_hbm": gemv8_gbs / HBM_PEAK_GBS},
+        "gemv_m1": {"us_per_launch": gemv1_us, "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS,
+                    "frac_read_ceiling": gemv_gbs / read_gbs},
+        "gemv_m8": {"us_per_launch": gemv8_us, "GB/s": gemv8_gbs, "frac_hbm": gemv8_gbs / HBM_PEAK_GBS,
+                    "frac_read_ceiling": gemv8_gbs / read_gbs},
+        "read_ceiling": {"us_per_launch": read_us, "GB/s": read_gbs, "frac_hbm": read_gbs / HBM_PEAK_GBS,
+                         "bytes_per_launch": rd_bytes, "blocks": rd_best[1], "unroll": rd_best[2],
+                         "what": "plain streaming read (awq_read_stream) of the batch-1 line's bytes per "
+                                 f"launch, {N_ROT * N_PASS} launches over {N_ROT} resident buffers in one "
+                                 "graph, the best of 12 launch shapes: the rate a launch of this size "
+                                 "reaches on this chip"},
     }
     if c4:
         stages["gemm_prefill"] = gemm["up"]
@@ -518,7 +567,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": gemv_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gemv_gbs / HBM_PEAK_GBS, "traffic": measured_traffic("k_gemv1_cu"),
                      "kernel": "k_gemv1_cu (batch 1, one block per compute unit)",
-                     "bytes_per_launch": bytes_a},
+                     "bytes_per_launch": bytes_a,
+                     "read_ceiling": read_gbs, "frac_read_ceiling": gemv_gbs / read_gbs},
         "prefill_gemm": None if up is None else {
             "bound": "mfma", "achieved": up["TFLOP/s"], "peak": FP16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": up["frac_fp16_mfma"],

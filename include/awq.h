@@ -358,6 +358,27 @@ awq_status awq_w4a16_gemm_noalloc(const void* x, awq_dtype xdt, int64_t M, int64
 awq_status awq_fold_scales(void* v, awq_dtype dt, int64_t rows, int64_t cols, int64_t ld, const float* s,
                            int axis, void* stream);
 
+/* Diagnostic: a plain streaming read of `bytes` of device memory, the rate the
+ * W4A16 products are measured against at their own sizes.  "AWQ Math",
+ * section "Weight-only quantization and where it breaks": at decode batch
+ * sizes the product is bound by moving the weights, so its ceiling is the rate
+ * at which this chip reads the same number of bytes, not the HBM peak alone.
+ * One launch of `blocks` blocks of 1024 threads; each wave reads `unroll`
+ * whole 1 KB units per step (64 lanes x 16 B, non-temporal loads), striding
+ * over the buffer, and each block writes the XOR of every 32-bit word it read
+ * to block_xor[block] (the XOR over all blocks is the XOR of the buffer).
+ *
+ *   p          device, 16-byte aligned, `bytes` readable
+ *   bytes      > 0, a multiple of 1024
+ *   blocks     1 .. 65535
+ *   unroll     1, 2, 4 or 8
+ *   block_xor  device uint32 [blocks], written
+ * Errors: NULL pointer -> AWQ_ERR_NULL; bytes or blocks out of range ->
+ * AWQ_ERR_SHAPE; unroll -> AWQ_ERR_UNSUPPORTED; p misaligned -> AWQ_ERR_ALIGN.
+ */
+awq_status awq_read_stream(const void* p, int64_t bytes, int blocks, int unroll, uint32_t* block_xor,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

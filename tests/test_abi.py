@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _lib()
-    assert lib.awq_abi_version() == 5
+    assert lib.awq_abi_version() == 6
     for code in range(8):
         assert lib.awq_status_str(code).decode()
     assert lib.awq_status_str(0).decode() == "ok"
@@ -333,3 +333,19 @@ def test_gemm_noalloc_validation():
     # 2048 tokens, 28672 -> 8192, groups of 64: about 147 MB of scratch
     assert call(M=2048, K=28672, ldx=28672, N=8192, ldy=8192, g=64, xdt=E.AWQ_BF16) == 5
     assert abi.AWQ_NOALLOC_SCRATCH_BYTES == 128 << 20
+
+
+def test_read_stream_validation():
+    """awq_read_stream (the streaming-read diagnostic) rejects bad arguments on
+    the host before any launch."""
+    lib = _lib()
+    f = lib.awq_read_stream
+    assert f(NULL, 1024, 256, 4, A, NULL) == 1
+    assert f(A, 1024, 256, 4, NULL, NULL) == 1
+    assert f(A, 0, 256, 4, A, NULL) == 2
+    assert f(A, 1000, 256, 4, A, NULL) == 2
+    assert f(A, 1024, 0, 4, A, NULL) == 2
+    assert f(A, 1024, 65536, 4, A, NULL) == 2
+    assert f(A, 1024, 256, 3, A, NULL) == 5
+    assert f(BAD, 1024, 256, 4, A, NULL) == 4
+

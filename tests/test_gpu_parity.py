@@ -643,3 +643,18 @@ def test_small_batch_product_parity(M, N, K, dtype, ydt, with_r, group):
                        y=again, group_size=group)
     torch.cuda.synchronize()
     assert torch.equal(again.view(torch.uint8), big[:, :N].contiguous().view(torch.uint8))
+
+
+@pytest.mark.parametrize("nbytes,blocks,unroll", [(1024, 1, 1), (23601152, 256, 4), (3 * 1024 * 1037, 300, 8),
+                                                  (64 * 1024, 1000, 2)])
+def test_read_stream_xor(nbytes, blocks, unroll):
+    """The streaming-read diagnostic reads every word once: the XOR over its
+    blocks equals the XOR of the buffer (integer, bit-exact), including a
+    ragged last step and more blocks than units."""
+    g = np.random.Generator(np.random.PCG64(nbytes + blocks))
+    words = g.integers(-2 ** 31, 2 ** 31, nbytes // 4, dtype=np.int64).astype(np.int32)
+    bx = awq.awq_read_stream(gpu(torch.from_numpy(words)), blocks, unroll)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(bx.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words.view(np.uint32))
+

@@ -18,7 +18,7 @@ from ._abi import (AWQ_BF16, AWQ_F16, AWQ_F32, AWQ_GROUP, AWQ_OP_ACT_STATS, AWQ_
                    AWQ_OP_QUANTIZE, AWQ_OP_SEARCH, AwqError, lib)
 
 __all__ = ["awq_act_stats", "awq_search_scales", "awq_search_scales_ex", "awq_quantize_pack", "awq_quantize_codes",
-           "awq_w4a16_gemm", "awq_w4a16_gemm_noalloc", "awq_fold_scales", "awq_salient_channels", "awq_workspace_bytes",
+           "awq_w4a16_gemm", "awq_w4a16_gemm_noalloc", "awq_read_stream", "awq_fold_scales", "awq_salient_channels", "awq_workspace_bytes",
            "AwqError", "lib"]
 
 _DT = {torch.float16: AWQ_F16, torch.bfloat16: AWQ_BF16, torch.float32: AWQ_F32}
@@ -231,6 +231,22 @@ def awq_w4a16_gemm_noalloc(x: torch.Tensor, qweight: torch.Tensor, scales: torch
                                       _DT.get(y.dtype, -1), ldy, _stream(x.device, stream))
     _abi.check("awq_w4a16_gemm_noalloc", st)
     return y
+
+
+def awq_read_stream(buf: torch.Tensor, blocks: int, unroll: int = 4, block_xor: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """A plain streaming read of buf's bytes (a multiple of 1024); returns the
+    per-block XOR of the 32-bit words read (int32 [blocks]).  The rate the
+    products are measured against."""
+    _dev(buf, "buf")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if block_xor is None:
+        block_xor = torch.empty(blocks, dtype=torch.int32, device=buf.device)
+    st = lib().awq_read_stream(_ptr(buf), buf.numel() * buf.element_size(), blocks, unroll,
+                               _ptr(block_xor), _stream(buf.device, stream))
+    _abi.check("awq_read_stream", st)
+    return block_xor
 
 
 def awq_fold_scales(v: torch.Tensor, s: torch.Tensor, axis: int = 1, stream=None) -> torch.Tensor:

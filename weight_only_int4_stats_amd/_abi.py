@@ -40,6 +40,7 @@ SIGNATURES = {
     "awq_fold_scales": (_i, [_p, _i, _i64, _i64, _i64, _p, _i, _p]),
     "awq_w4a16_gemm_noalloc": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _i64, _i, _p, _p, _i, _i64,
                                     _p]),
+    "awq_read_stream": (_i, [_p, _i64, _i, _i, _p, _p]),
 }
 
 _lib = None

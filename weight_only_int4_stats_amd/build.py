@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libawq_gfx950.so")
 SOURCES = ["awq_api.cpp", "k_act_stats.hip", "k_quantize.hip", "k_search.hip", "k_gram.hip", "k_w4a16.hip",
-           "k_gemv1.hip", "k_fold.hip", "k_salient.hip", "awq_noalloc.hip", "k_mid.hip", "k_skinny.hip"]
+           "k_gemv1.hip", "k_fold.hip", "k_salient.hip", "awq_noalloc.hip", "k_mid.hip", "k_skinny.hip", "k_stream.hip"]
 ARCH = "gfx950"
 
 

@@ -23,7 +23,7 @@ bool grid_ok(int bits, int symmetric) {
 
 extern "C" {
 
-int awq_abi_version(void) { return 5; }
+int awq_abi_version(void) { return 6; }
 
 const char* awq_status_str(awq_status st) {
   switch (st) {
@@ -172,3 +172,12 @@ awq_status awq_fold_scales(void* v, awq_dtype dt, int64_t rows, int64_t cols, in
 }
 
 }  // extern "C"
+
+extern "C" awq_status awq_read_stream(const void* p, int64_t bytes, int blocks, int unroll,
+                                      uint32_t* block_xor, void* stream) {
+  if (!p || !block_xor) return AWQ_ERR_NULL;
+  if (bytes <= 0 || bytes % 1024 != 0 || blocks < 1 || blocks > 65535) return AWQ_ERR_SHAPE;
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) return AWQ_ERR_UNSUPPORTED;
+  if (!aligned16(p)) return AWQ_ERR_ALIGN;
+  return from_hip(awq::launch_read_stream(p, bytes, blocks, unroll, block_xor, (hipStream_t)stream));
+}

@@ -86,6 +86,11 @@ hipError_t launch_skinny_st(const void* x, int xdt, int64_t M, int64_t K, int64_
                             int64_t N, int group, const float* inv_s, void* y, int ydt, int64_t ldy,
                             hipStream_t st);
 
+// ---- plain streaming read (k_stream.hip): bytes a multiple of 1024, blocks
+// of 1024 threads, unroll 1, 2, 4 or 8 units in flight per wave
+hipError_t launch_read_stream(const void* p, int64_t bytes, int blocks, int unroll, uint32_t* block_xor,
+                              hipStream_t st);
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Compute units of the current device (cached per device).
