@@ -645,6 +645,22 @@ def test_small_batch_product_parity(M, N, K, dtype, ydt, with_r, group):
     assert torch.equal(again.view(torch.uint8), big[:, :N].contiguous().view(torch.uint8))
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 5000, 2048), (2, 11008, 4096), (16, 9000, 1024)])
+def test_skinny_one_hot_exact_split_path(M, N, K):
+    """Blocks of two or more 16-row tiles take the loader/stager schedule of
+    the 2..16-token product.  A one-hot token is exact there too: the codes
+    enter the matrix cores exactly, the zero point's sum is exact and the
+    step multiplies in fp32, so every output equals step * (q - z)."""
+    words, step, z = _random_packed(N, K, 11 + M)
+    for k in (0, K // 2 + 3, K - 1):
+        x = torch.zeros((M, K), dtype=F16)
+        x[:, k] = 1.0
+        y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                               gpu(torch.from_numpy(z)), out_dtype=torch.float32)
+        ref = O.w4a16_matmul(f32(x), words, step, z)
+        assert np.array_equal(f32(y), ref.astype(np.float32)), (M, N, K, k)
+
+
 @pytest.mark.parametrize("nbytes,blocks,unroll", [(1024, 1, 1), (23601152, 256, 4), (3 * 1024 * 1037, 300, 8),
                                                   (64 * 1024, 1000, 2)])
 def test_read_stream_xor(nbytes, blocks, unroll):
