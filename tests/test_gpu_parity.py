@@ -645,6 +645,31 @@ def test_small_batch_product_parity(M, N, K, dtype, ydt, with_r, group):
     assert torch.equal(again.view(torch.uint8), big[:, :N].contiguous().view(torch.uint8))
 
 
+@pytest.mark.parametrize("M,N,K,dtype,with_r,pad", [
+    (8, 11008, 4096, F16, True, 64),            # loader/stager schedule
+    (5, 4096, 4096, BF16, False, 8),            # one tile per block
+    (16, 3000, 2048, F16, True, 136),           # 16 tokens, odd row pitch in 16-byte units
+])
+def test_skinny_product_strided_activations(M, N, K, dtype, with_r, pad):
+    """2..16 tokens from a strided activation view (row pitch K + pad): the
+    staging reads each token row at its own pitch."""
+    g = np.random.Generator(np.random.PCG64(M * 31 + N + pad))
+    words = g.integers(-2 ** 31, 2 ** 31, (N, K // 8), dtype=np.int64).astype(np.int32)
+    step = g.uniform(2e-4, 4e-3, (N, K // 128)).astype(np.float16)
+    z = g.integers(0, 16, (N, K // 128)).astype(np.uint8)
+    x = _act(M, K, dtype, M + K + pad)
+    big = torch.zeros((M, K + pad), dtype=dtype)
+    big[:, :K] = x
+    r = (np.float32(1) / np.exp(g.uniform(-1.5, 1.5, K)).astype(np.float32)).astype(np.float32) if with_r else None
+    y = awq.awq_w4a16_gemm(gpu(big)[:, :K], gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                           gpu(torch.from_numpy(z)), None if r is None else gpu(torch.from_numpy(r)),
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 300)), np.arange(N - 40, N)]))
+    ref = O.w4a16_matmul_rows(f32(x), words, step, z, rows, r)
+    assert rel_max_err(f32(y)[:, rows], ref) <= GEMM_TOL
+
+
 @pytest.mark.parametrize("M,N,K", [(8, 5000, 2048), (2, 11008, 4096), (16, 9000, 1024)])
 def test_skinny_one_hot_exact_split_path(M, N, K):
     """Blocks of two or more 16-row tiles take the loader/stager schedule of
