@@ -120,22 +120,22 @@ def test_gemv_parity(M, N, K, dtype, ydt, with_r):
     assert err <= GEMM_TOL
 
 
-def _sampled_product(M, N, K, dtype, ydt, with_r, seed):
+def _sampled_product(M, N, K, dtype, ydt, with_r, seed, group=128):
     """Random packed layer (words drawn directly), sampled output channels
     against the oracle (channels are independent)."""
     g = np.random.Generator(np.random.PCG64(seed))
     words = g.integers(-2 ** 31, 2 ** 31, (N, K // 8), dtype=np.int64).astype(np.int32)
-    step = g.uniform(2e-4, 4e-3, (N, K // 128)).astype(np.float16)
-    z = g.integers(0, 16, (N, K // 128)).astype(np.uint8)
+    step = g.uniform(2e-4, 4e-3, (N, K // group)).astype(np.float16)
+    z = g.integers(0, 16, (N, K // group)).astype(np.uint8)
     x = _act(M, K, dtype, seed + 1)
     r = (np.float32(1) / np.exp(g.uniform(-1.5, 1.5, K)).astype(np.float32)).astype(np.float32) if with_r else None
     y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
                            gpu(torch.from_numpy(z)), None if r is None else gpu(torch.from_numpy(r)),
-                           out_dtype=ydt)
+                           out_dtype=ydt, group_size=group)
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 300)), np.arange(N - 40, N),
                                      g.integers(0, N, 100)]))
-    ref = O.w4a16_matmul_rows(f32(x), words, step, z, rows, r)
+    ref = O.w4a16_matmul_rows(f32(x), words, step, z, rows, r, group)
     return rel_max_err(f32(y)[:, rows], ref, ydt), len(rows)
 
 
@@ -146,14 +146,46 @@ def _sampled_product(M, N, K, dtype, ydt, with_r, seed):
     (12, 5000, 2048, BF16, torch.float32, True),  # 3 token phases per thread
     (16, 3000, 4096, F16, F16, False),         # 16 tokens, activations fill LDS
     (5, 11008, 4096, F16, F16, True),
-    (8, 2000, 16384, F16, torch.float32, True),  # activations exceed LDS: pre-pass kernel
-    (16, 700, 11008, BF16, BF16, False),       # ragged K slices, pre-pass kernel
+    (8, 2000, 16384, F16, torch.float32, True),  # activations staged in two passes
+    (16, 700, 11008, BF16, BF16, False),       # ragged K slices, passes of 3712 channels
 ])
 def test_skinny_product_parity(M, N, K, dtype, ydt, with_r):
     """2 <= M <= 16: the skinny matrix-core products."""
     err, nrow = _sampled_product(M, N, K, dtype, ydt, with_r, seed=7 * M + N + K)
     print(f"skinny M={M} N={N} K={K} {dtype} -> {ydt}: rel max err {err:.3e} on {nrow} channels")
     assert err <= GEMM_TOL
+
+
+@pytest.mark.parametrize("M,N,K,dtype,ydt,with_r,group", [
+    (8, 3000, 11008, F16, F16, True, 128),        # two passes of 43 units, one tile per block
+    (16, 3000, 8192, BF16, torch.float32, True, 128),  # K fits the threads, not LDS: two passes
+    (2, 8192, 28672, F16, F16, False, 128),       # four passes, two tiles per block
+    (12, 1500, 20608, F16, torch.float32, True, 64),   # six passes, the last one shorter
+    (5, 2000, 16640, BF16, BF16, True, 256),      # groups of 256 over three passes
+    (4, 63488, 8448, F16, torch.float32, True, 256),   # 16 tiles per block: one item per wave
+])
+def test_skinny_product_passes(M, N, K, dtype, ydt, with_r, group):
+    """2..16 tokens whose activations do not fit LDS (or the block's threads)
+    at once: the 2..16-token product stages them in passes of whole 128-channel
+    units, and every wave runs the units of its slice that fall in the pass."""
+    err, nrow = _sampled_product(M, N, K, dtype, ydt, with_r, seed=3 * M + N + K + group, group=group)
+    print(f"skinny passes M={M} N={N} K={K} g={group}: rel max err {err:.3e} on {nrow} channels")
+    assert err <= GEMM_TOL
+
+
+@pytest.mark.parametrize("M,N,K,ks", [(8, 3000, 11008, (5503, 5504, 5631, 11007)),
+                                      (16, 3000, 8192, (0, 4095, 4096, 8191))])
+def test_skinny_one_hot_exact_passes(M, N, K, ks):
+    """One-hot tokens on either side of a pass boundary are exact on the
+    staged-in-passes product too (every output equals step * (q - z))."""
+    words, step, z = _random_packed(N, K, 23 + M)
+    for k in ks:
+        x = torch.zeros((M, K), dtype=F16)
+        x[:, k] = 1.0
+        y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                               gpu(torch.from_numpy(z)), out_dtype=torch.float32)
+        ref = O.w4a16_matmul(f32(x), words, step, z)
+        assert np.array_equal(f32(y), ref.astype(np.float32)), (M, N, K, k)
 
 
 @pytest.mark.parametrize("N,K,dtype,ydt,with_r", [

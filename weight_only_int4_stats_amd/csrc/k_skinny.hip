@@ -25,12 +25,16 @@
 //    -z 2^-24 sum_k X_k, from per-(token, unit) sums staged with the
 //    activations, and the step is staged as D 2^24:
 //    y = sum_units (D 2^24) 2^-p (sum_k X_k q_k 2^-24 - z 2^-24 sum_k X_k).
-//  * The block stages once, in LDS: X = fp16(x r 2^p) with one power of two per
+//  * The block stages in LDS: X = fp16(x r 2^p) with one power of two per
 //    (token, 128-channel unit) (max |X| in [2^13, 2^14)), in the order the
 //    unpack yields (k0,k4,k2,k6,k1,k5,k3,k7 per word); the sums and 2^-p; and
-//    the block's steps and zero points as fp32 pairs.  K <= 8192, so that
-//    every thread stages pieces of one 8-channel column and holds one 1/s
-//    vector.
+//    the block's steps and zero points as fp32 pairs.  Every thread stages
+//    pieces of one 8-channel column and holds one 1/s vector, so a pass covers
+//    at most 8192 channels.  When the tokens' activations do not fit LDS or
+//    the block's threads at once, they are staged in passes of whole units
+//    (blocks of at most 16 tiles, one item per wave): a wave runs the units of
+//    its slice inside the pass, issues the next pass's first units, and the
+//    block restages once every wave has left X.
 //  * A wave's instructions issue in order, and the memory pipeline holds a
 //    wave at a load's issue while the weight stream flows, so a wave that
 //    issues its weight loads first cannot stage until the stream has mostly
@@ -40,6 +44,8 @@
 #include "awq_device.h"
 #include "awq_internal.h"
 #include "k_rows_f16.h"
+
+#include <type_traits>
 
 namespace awqk {
 
@@ -81,9 +87,9 @@ struct StLayout {
   int meta_pitch;   // (step, zero) pairs per staged row
 };
 
-inline StLayout st_layout(int64_t M, int64_t K, int64_t rows_max, int glog) {
+inline StLayout st_layout(int64_t M, int64_t K, int64_t rows_max, int glog, int64_t kpass) {
   StLayout L;
-  const size_t xs = (size_t)M * (size_t)(K + 8) * 2;           // X [M][K + 8]
+  const size_t xs = (size_t)M * (size_t)(kpass + 8) * 2;       // X [M][kpass + 8]
   const size_t red = (size_t)kStWaves * 256 * 4;              // slices' 16 x 16 tiles (reuses X)
   const int64_t gw = K >> glog;
   L.meta_pitch = (int)gw + 2;                                 // rows 16 B apart across banks
@@ -111,22 +117,47 @@ inline bool st_split(int64_t M, int64_t K, int64_t rows_max, int glog) {
   return rows_max > 16 && glog != 6 && st_pieces(M, K, 512) != 0 && rows_max * (K >> glog) <= 512 * kStMetaPer;
 }
 
-template <int DT, int YDT, bool HAS_R, int NP, bool G64, bool SPLIT>
+// Channels staged per pass: K when every token's activations fit at once;
+// else the fewest passes of equal whole 128-channel units whose pieces fit the
+// block's threads and whose LDS fits, for blocks of at most 16 tiles (one item
+// per wave, so the waves meet at every pass); 0 if none.  Blocks of one
+// nearly full tile (13..16 rows) with 8 or more tokens are left to the other
+// kernels: there each block stages every token's activations for at most 16
+// rows of weights, and the staging passes (loads, conversion, barriers) cost
+// about as much as the row-tile kernel's shared pre-converted activations,
+// which then fill the chip.
+inline int64_t st_kpass(int64_t M, int64_t K, int64_t rows_max, int glog) {
+  if (st_pieces(M, K) != 0 && st_layout(M, K, rows_max, glog, K).total <= kStLdsMax) return K;
+  if (rows_max > 16 * 16 || (rows_max > 12 && rows_max <= 16 && M >= 8)) return 0;
+  const int64_t G = K >> 7;
+  for (int64_t np = 2; np <= G; ++np) {
+    const int64_t kp = (G + np - 1) / np * 128;
+    if (st_pieces(M, kp) != 0 && st_layout(M, K, rows_max, glog, kp).total <= kStLdsMax) return kp;
+  }
+  return 0;
+}
+
+template <int DT, int YDT, bool HAS_R, int NP, bool G64, bool SPLIT, bool MULTI>
 __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
     const uint16_t* __restrict__ x, int M, int64_t K, int64_t ldx, const float* __restrict__ r,
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, int64_t N, void* __restrict__ y, int64_t ldy, int glog,
-    uint32_t o_sums, uint32_t o_pinv, uint32_t o_meta, int mp) {
+    uint32_t o_sums, uint32_t o_pinv, uint32_t o_meta, int mp, int kpass) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_st[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rl = lane & 15;
   const int b = lane >> 4;
-  const uint32_t K8 = (uint32_t)(K >> 3);
+  // MULTI: the activations are staged in passes of kpass channels (the
+  // block's items then hold one item per wave); otherwise in one pass
+  const int kp = MULTI ? kpass : (int)K;
+  const uint32_t K8 = (uint32_t)(kp >> 3);        // 8-channel pieces per token in a full pass
+  const int UPp = kp >> 7;                        // 128-channel units per pass
+  const int npass = MULTI ? (int)((K + kp - 1) / kp) : 1;
   const int G = (int)(K >> 7);
   const int GW = (int)(K >> glog);
-  const int64_t KP = K + 8;
+  const int64_t KP = kp + 8;                      // LDS pitch of a staged token row
   const int64_t r0 = (int64_t)blockIdx.x * N / gridDim.x;
   const int nrows = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x - r0);
   const int ntile = (nrows + 15) / 16;
@@ -165,10 +196,10 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   // zeros by themselves, so the only choice left is the wave-uniform one (a
   // unit outside the item), which keeps the loads free of branches.
   const uint32_t lane_off = (uint32_t)rl * KW * 4 + (uint32_t)b * (G64 ? 8 : 16);
-  auto load_unit = [&](int slot, int g) {
-    // the unit's wave-uniform offset, or 2^31 (past any range) outside the
-    // item: a scalar choice, the load itself unconditional
-    const bool ok = have && g < g1;
+  auto load_unit = [&](int slot, int g, int gend) {
+    // the unit's wave-uniform offset, or 2^31 (past any range) at or past
+    // gend: a scalar choice, the load itself unconditional
+    const bool ok = have && g < gend;
     const uint32_t uoff = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)(tile * 16) * KW * 4 + (uint32_t)g * 64 : kBufferOob);
     const uint32_t off = lane_off + uoff;
     if constexpr (!G64) {
@@ -182,7 +213,7 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   auto issue_weights = [&]() {
     set_item(have ? it : 0);
 #pragma unroll
-    for (int d = 0; d < kStQ; ++d) load_unit(d, g0 + d);
+    for (int d = 0; d < kStQ; ++d) load_unit(d, g0 + d, MULTI ? (g1 < UPp ? g1 : UPp) : g1);
     __builtin_amdgcn_sched_barrier(0);
   };
   // ---- staging: its loads, then mid() (the weights' issue when every wave
@@ -191,17 +222,43 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   // 512 / (K/8) when only waves 0..7 stage).  Threads past the last phase load
   // piece 0 of token 0 and drop it (no branch around the loads).  The steps
   // and zero points come 8 per thread: one 128-bit and one 64-bit load.
-  auto stage = [&](auto mid) {
+  // pass ps covers channels [ps kp, ps kp + kp) (the last pass may be
+  // shorter); with_meta: also the steps and zero points (the first pass)
+  auto stage = [&](auto mid, int ps, auto with_meta) {
+    const int64_t c0 = (int64_t)ps * kp;
+    const uint32_t k8n = (uint32_t)((K - c0 < kp ? K - c0 : kp) >> 3);   // pieces in this pass
+    const bool kin = k8 < k8n;
+    uint32_t k8c = kin ? k8 : 0u, tphc = tph;
+    uint64_t xa = (uint64_t)x, ra = (uint64_t)r;
+    if constexpr (MULTI) {
+      // with passes, opaque copies: the pieces' addresses are formed here, not
+      // kept live across the passes, and the loads stay ahead of the weights'
+      // (a load from a read-only argument may otherwise sink to its use)
+      asm volatile("" : "+v"(k8c), "+v"(tphc));
+      asm volatile("" : "+s"(xa), "+s"(ra));
+    }
+    using gu16 = const __attribute__((address_space(1))) uint16_t;
+    using gu32x4 = const __attribute__((address_space(1))) u32x4;
+    using gf32 = const __attribute__((address_space(1))) float;
+    using gf32x4 = const __attribute__((address_space(1))) f32x4;
     u32x4 sx[NP];
     f32x4 sr0, sr1;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const uint32_t m = tph + (uint32_t)i * T;
-      sx[i] = ldg128(x + (int64_t)((uint32_t)i < ntok ? m : 0u) * ldx + (int64_t)k8 * 8);
+      const uint32_t m = tphc + (uint32_t)i * T;
+      const int64_t off = (int64_t)((uint32_t)i < ntok ? m : 0u) * ldx + c0 + (int64_t)k8c * 8;
+      if constexpr (MULTI) sx[i] = *(gu32x4*)((gu16*)xa + off);
+      else sx[i] = ldg128(x + off);
     }
     if constexpr (HAS_R) {
-      sr0 = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8);
-      sr1 = *reinterpret_cast<const f32x4*>(r + (int64_t)k8 * 8 + 4);
+      const int64_t off = c0 + (int64_t)k8c * 8;
+      if constexpr (MULTI) {
+        sr0 = *(gf32x4*)((gf32*)ra + off);
+        sr1 = *(gf32x4*)((gf32*)ra + off + 4);
+      } else {
+        sr0 = *reinterpret_cast<const f32x4*>(r + off);
+        sr1 = *reinterpret_cast<const f32x4*>(r + off + 4);
+      }
     }
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(scales + r0 * GW), (short)0, nmeta * 2, kBufferWord3);
@@ -210,7 +267,7 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
     // thread t takes entries [e0, e0 + 8) with e0 = min(8 t, nmeta - 8), so
     // every load lies wholly inside the block's range (nmeta >= 8); the last
     // window overlaps its neighbour's and writes the same values
-    const bool mlive = tid * kStMetaPer < nmeta;
+    const bool mlive = decltype(with_meta)::value && tid * kStMetaPer < nmeta;
     const int e0 = mlive ? (tid * kStMetaPer < nmeta - kStMetaPer ? tid * kStMetaPer : nmeta - kStMetaPer) : 0;
     const u32x4 mst = __builtin_amdgcn_raw_buffer_load_b128(srs, mlive ? (uint32_t)e0 * 2 : kBufferOob, 0, 0);
     const auto mze = __builtin_amdgcn_raw_buffer_load_b64(zrs, mlive ? (uint32_t)e0 : kBufferOob, 0, 0);
@@ -241,7 +298,7 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
     for (int i = 0; i < NP; ++i) {
       if (i >= npl) break;                         // uniform
       const uint32_t m = tph + (uint32_t)i * T;
-      const bool live = (uint32_t)i < ntok;
+      const bool live = (uint32_t)i < ntok && kin;
       float v[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -283,8 +340,8 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
       if constexpr (!G64) s += dpp_f<0x140>(s);     // 16 lanes: the 128-channel unit
       if (live) {
         *reinterpret_cast<u32x4*>(xs + (int64_t)m * KP + (int64_t)k8 * 8) = o;
-        if ((lane & (G64 ? 7 : 15)) == 0) sums[(k8 >> (G64 ? 3 : 4)) * 16 + m] = s;
-        if ((lane & 15) == 0) pinv[(k8 >> 4) * 16 + m] = ldexpf(1.0f, -p);
+        if ((lane & (G64 ? 7 : 15)) == 0) sums[((uint32_t)(c0 >> (G64 ? 6 : 7)) + (k8 >> (G64 ? 3 : 4))) * 16 + m] = s;
+        if ((lane & 15) == 0) pinv[((uint32_t)(c0 >> 7) + (k8 >> 4)) * 16 + m] = ldexpf(1.0f, -p);
       }
     }
   };
@@ -294,13 +351,13 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   // delay the conversion, and half of the weight stream overlaps it.
   if constexpr (SPLIT) {
     if (wv < 8) {
-      stage([] {});
+      stage([] {}, 0, std::true_type{});
       issue_weights();
     } else {
       issue_weights();
     }
   } else {
-    stage(issue_weights);
+    stage(issue_weights, 0, std::true_type{});
   }
   st_sync();
 
@@ -308,22 +365,22 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   const int tok = rl < M ? rl : M - 1;           // rows past M repeat a token; dropped
   const uint8_t* xrow = reinterpret_cast<const uint8_t*>(xs) + (size_t)tok * (size_t)KP * 2;
   const int gsh = glog - 7;                       // unit -> group (groups of 128, 256)
-  // one item on the ring already in flight; refills run past its end (out of
-  // range, no traffic).  Per unit: part = -z 2^-24 sum X + sum X q 2^-24 on
-  // the matrix cores, then acc += (D 2^24) 2^-p part.
-  auto run_item = [&]() {
+  // units [ga, ge) of the item, the first kStQ already in flight in slots
+  // 0 .. kStQ - 1; refills run past ge (out of range, no traffic).  ubase: the
+  // first unit of the staged pass.  Per unit: part = -z 2^-24 sum X +
+  // sum X q 2^-24 on the matrix cores, then acc += (D 2^24) 2^-p part.
+  auto run_item = [&](f32x4 acc, int ga, int ge, int ubase) {
     const int rowc = tile * 16 + rl < nrows ? tile * 16 + rl : nrows - 1;
     const float2* mrow = meta + rowc * mp;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int gb = g0; gb < g1; gb += kStQ) {
+    for (int gb = ga; gb < ge; gb += kStQ) {
 #pragma unroll
       for (int d = 0; d < kStQ; ++d) {
         const int g = gb + d;
-        if (g < g1) {                             // wave-uniform
+        if (g < ge) {                             // wave-uniform
           u32x4 xa[4];
           const f32x4 pv = *reinterpret_cast<const f32x4*>(pinv + g * 16 + 4 * b);
           if constexpr (!G64) {
-            const uint8_t* p = xrow + (size_t)(128 * g + 32 * b) * 2;
+            const uint8_t* p = xrow + (size_t)(128 * (g - ubase) + 32 * b) * 2;
 #pragma unroll
             for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4*>(p + 16 * i);
             const f32x4 sv = *reinterpret_cast<const f32x4*>(sums + g * 16 + 4 * b);
@@ -336,7 +393,7 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(md.x * pv[v], part[v], acc[v]);
           } else {
-            const uint8_t* p = xrow + (size_t)(128 * g + 16 * b) * 2;
+            const uint8_t* p = xrow + (size_t)(128 * (g - ubase) + 16 * b) * 2;
             xa[0] = *reinterpret_cast<const u32x4*>(p);
             xa[1] = *reinterpret_cast<const u32x4*>(p + 16);
             xa[2] = *reinterpret_cast<const u32x4*>(p + 128);
@@ -359,7 +416,7 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
               acc[v] = __builtin_fmaf(md[2] * pv[v], p1[v], __builtin_fmaf(md[0] * pv[v], p0[v], acc[v]));
           }
         }
-        load_unit(d, g + kStQ);
+        load_unit(d, g + kStQ, ge);
       }
     }
     return acc;
@@ -376,16 +433,41 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   // (only when ksl == 1) load their own.  Two copies of the item code keep the
   // ring in the same registers from the loads to the products.
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (have) {
-    acc = run_item();
-    if (ksl == 1) store_direct(acc);
-  }
-  if (ksl == 1) {
-    for (it = wv + kStWaves; it < nitems; it += kStWaves) {
-      set_item(it);
+  if constexpr (MULTI) {
+    // one item per wave.  Pass ps runs the item's units inside the staged
+    // channels; before the next pass is staged over it, the wave issues that
+    // pass's first units and every wave leaves X.
+    for (int ps = 0;; ++ps) {
+      const int pa = g0 > ps * UPp ? g0 : ps * UPp;
+      const int pe = g1 < (ps + 1) * UPp ? g1 : (ps + 1) * UPp;
+      if (have) acc = run_item(acc, pa, pe, ps * UPp);
+      if (ps + 1 >= npass) break;
+      const int na = g0 > (ps + 1) * UPp ? g0 : (ps + 1) * UPp;
+      const int ne = g1 < (ps + 2) * UPp ? g1 : (ps + 2) * UPp;
+      stage(
+          [&] {
+            __builtin_amdgcn_sched_barrier(0);    // the activations' loads first
 #pragma unroll
-      for (int d = 0; d < kStQ; ++d) load_unit(d, g0 + d);
-      store_direct(run_item());
+            for (int d = 0; d < kStQ; ++d) load_unit(d, na + d, ne);
+            __builtin_amdgcn_sched_barrier(0);
+            st_sync();                            // every wave done with this pass's X
+          },
+          ps + 1, std::false_type{});
+      st_sync();
+    }
+    if (have && ksl == 1) store_direct(acc);
+  } else {
+    if (have) {
+      acc = run_item(acc, g0, g1, 0);
+      if (ksl == 1) store_direct(acc);
+    }
+    if (ksl == 1) {
+      for (it = wv + kStWaves; it < nitems; it += kStWaves) {
+        set_item(it);
+#pragma unroll
+        for (int d = 0; d < kStQ; ++d) load_unit(d, g0 + d, g1);
+        store_direct(run_item(f32x4{0.0f, 0.0f, 0.0f, 0.0f}, g0, g1, 0));
+      }
     }
   }
   if (ksl > 1) {
@@ -410,18 +492,25 @@ hipError_t st_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, con
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int glog, const float* r,
                        void* y, int64_t ldy, int nblk, hipStream_t st) {
   const int64_t rows_max = (N + nblk - 1) / nblk;
-  const StLayout L = st_layout(M, K, rows_max, glog);
+  const int64_t kp = st_kpass(M, K, rows_max, glog);
+  const bool multi = kp < K;
+  const StLayout L = st_layout(M, K, rows_max, glog, kp);
   size_t lds = L.total;
   if (lds < 81 * 1024) lds = 81 * 1024;           // one block per compute unit
-  const bool split = st_split(M, K, rows_max, glog);
-  const int np = split ? st_pieces(M, K, 512) : st_pieces(M, K);
+  const bool split = !multi && st_split(M, K, rows_max, glog);
+  const int np = split ? st_pieces(M, K, 512) : st_pieces(M, kp);
   const dim3 grid((unsigned)nblk), block(1024);
-#define AWQ_ST(NP, G64, SPLIT)                                                                       \
-  hipLaunchKernelGGL((k_gemm_skinny_st<DT, YDT, HAS_R, NP, G64, SPLIT>), grid, block, lds, st, x, (int)M, K, \
-                     ldx, r, qw, scales, zeros, N, y, ldy, glog, (uint32_t)L.sums, (uint32_t)L.pinv,   \
-                     (uint32_t)L.meta, L.meta_pitch)
-#define AWQ_STG(NP) \
-  if (glog == 6) AWQ_ST(NP, true, false); else if (split) AWQ_ST(NP, false, true); else AWQ_ST(NP, false, false)
+#define AWQ_ST(NP, G64, SPLIT, MULTI)                                                                \
+  hipLaunchKernelGGL((k_gemm_skinny_st<DT, YDT, HAS_R, NP, G64, SPLIT, MULTI>), grid, block, lds, st, x, \
+                     (int)M, K, ldx, r, qw, scales, zeros, N, y, ldy, glog, (uint32_t)L.sums,         \
+                     (uint32_t)L.pinv, (uint32_t)L.meta, L.meta_pitch, (int)kp)
+#define AWQ_STG(NP)                                     \
+  if (multi) {                                          \
+    if (glog == 6) AWQ_ST(NP, true, false, true);       \
+    else AWQ_ST(NP, false, false, true);                \
+  } else if (glog == 6) AWQ_ST(NP, true, false, false); \
+  else if (split) AWQ_ST(NP, false, true, false);       \
+  else AWQ_ST(NP, false, false, false)
   if (np == 1) AWQ_STG(1);
   else if (np == 2) AWQ_STG(2);
   else if (np == 4) AWQ_STG(4);
@@ -438,15 +527,14 @@ namespace awq {
 int skinny_st_blocks(int64_t M, int64_t N, int64_t K, int group) {
   using namespace awqk;
   const int glog = group == 64 ? 6 : group == 128 ? 7 : group == 256 ? 8 : -1;
-  if (glog < 0 || M < 2 || M > 16 || N < 1 || K % 128 != 0 || K % group != 0 || st_pieces(M, K) == 0)
-    return 0;
+  if (glog < 0 || M < 2 || M > 16 || N < 1 || K % 128 != 0 || K % group != 0) return 0;
   const int64_t cus = device_cus();
   const int64_t nblk = N < cus ? N : cus;
   const int64_t rows_max = (N + nblk - 1) / nblk;
   // every block stages between 8 and 8192 (step, zero point) pairs
   if (rows_max * (K >> glog) > 1024 * kStMetaPer || (N / nblk) * (K >> glog) < kStMetaPer) return 0;
   if (rows_max * (K >> 1) >= (int64_t(1) << 31)) return 0;
-  if (st_layout(M, K, rows_max, glog).total > kStLdsMax) return 0;
+  if (st_kpass(M, K, rows_max, glog) == 0) return 0;
   return (int)nblk;
 }
 
