@@ -173,6 +173,20 @@ def test_skinny_product_passes(M, N, K, dtype, ydt, with_r, group):
     assert err <= GEMM_TOL
 
 
+@pytest.mark.parametrize("M,N,K,dtype,ydt,with_r,group", [
+    (2, 40000, 8192, F16, F16, True, 128),        # two row chunks, one pass each
+    (8, 20000, 8192, BF16, torch.float32, True, 64),   # two row chunks, passes, groups of 64
+    (16, 17000, 16384, F16, BF16, False, 128),    # two row chunks, five passes
+])
+def test_skinny_product_row_chunks(M, N, K, dtype, ydt, with_r, group):
+    """2..16 tokens on layers whose rows hold more steps and zero points than
+    one launch of the 2..16-token product stages: it runs on row chunks, one
+    launch each, writing disjoint output columns."""
+    err, nrow = _sampled_product(M, N, K, dtype, ydt, with_r, seed=5 * M + N + K + group, group=group)
+    print(f"skinny row chunks M={M} N={N} K={K} g={group}: rel max err {err:.3e} on {nrow} channels")
+    assert err <= GEMM_TOL
+
+
 @pytest.mark.parametrize("M,N,K,ks", [(8, 3000, 11008, (5503, 5504, 5631, 11007)),
                                       (16, 3000, 8192, (0, 4095, 4096, 8191))])
 def test_skinny_one_hot_exact_passes(M, N, K, ks):

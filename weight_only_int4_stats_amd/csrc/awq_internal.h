@@ -85,6 +85,13 @@ hipError_t launch_skinny_st(const void* x, int xdt, int64_t M, int64_t K, int64_
                             const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros,
                             int64_t N, int group, const float* inv_s, void* y, int ydt, int64_t ldy,
                             hipStream_t st);
+// Layers whose rows exceed one launch's steps and zero points: the kernel on
+// row chunks, one launch each (chunks: 1 = one launch, 0 = not covered).
+int skinny_st_chunks(int64_t M, int64_t N, int64_t K, int group);
+hipError_t launch_skinny_st_chunked(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx,
+                                    const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros,
+                                    int64_t N, int group, const float* inv_s, void* y, int ydt, int64_t ldy,
+                                    hipStream_t st);
 
 // ---- plain streaming read (k_stream.hip): bytes a multiple of 1024, blocks
 // of 1024 threads, unroll 1, 2, 4 or 8 units in flight per wave

@@ -538,6 +538,16 @@ int skinny_st_blocks(int64_t M, int64_t N, int64_t K, int group) {
   return (int)nblk;
 }
 
+// Row chunks that the kernel takes one launch at a time: 1 when one launch
+// covers the layer; else the fewest (2..16) whose every chunk one launch
+// covers (the block's steps and zero points limit its rows); 0 if none.
+int skinny_st_chunks(int64_t M, int64_t N, int64_t K, int group) {
+  if (skinny_st_blocks(M, N, K, group)) return 1;
+  for (int64_t c = 2; c <= 16 && c <= N; ++c)
+    if (skinny_st_blocks(M, N / c, K, group) && skinny_st_blocks(M, (N + c - 1) / c, K, group)) return (int)c;
+  return 0;
+}
+
 hipError_t launch_skinny_st(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx,
                             const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros,
                             int64_t N, int group, const float* inv_s, void* y, int ydt, int64_t ldy,
@@ -559,6 +569,23 @@ hipError_t launch_skinny_st(const void* x, int xdt, int64_t M, int64_t K, int64_
   if (ydt == DT_BF16) AWQ_SD(DT_BF16, DT_BF16);
   AWQ_SD(DT_BF16, DT_F32);
 #undef AWQ_SD
+}
+
+hipError_t launch_skinny_st_chunked(const void* x, int xdt, int64_t M, int64_t K, int64_t ldx,
+                                    const uint32_t* qw, const uint16_t* scales, const uint8_t* zeros,
+                                    int64_t N, int group, const float* inv_s, void* y, int ydt, int64_t ldy,
+                                    hipStream_t st) {
+  const int c = skinny_st_chunks(M, N, K, group);
+  if (c == 0) return hipErrorInvalidValue;
+  const int64_t G = K / group;
+  const int64_t yb = ydt == awqk::DT_F32 ? 4 : 2;
+  for (int i = 0; i < c; ++i) {
+    const int64_t n0 = (int64_t)i * N / c, n1 = (int64_t)(i + 1) * N / c;
+    const hipError_t e = launch_skinny_st(x, xdt, M, K, ldx, qw + n0 * (K >> 3), scales + n0 * G, zeros + n0 * G,
+                                          n1 - n0, group, inv_s, (uint8_t*)y + n0 * yb, ydt, ldy, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace awq

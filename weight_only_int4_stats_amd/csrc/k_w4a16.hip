@@ -935,6 +935,8 @@ hipError_t w4a16_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
     return awq::launch_mid(x, DT, M, K, ldx, qw, scales, zeros, N, 1 << glog, r, y, YDT, ldy, ws, st);
   if (awq::skinny_st_blocks(M, N, K, 1 << glog))
     return awq::launch_skinny_st(x, DT, M, K, ldx, qw, scales, zeros, N, 1 << glog, r, y, YDT, ldy, st);
+  if (awq::skinny_st_chunks(M, N, K, 1 << glog))
+    return awq::launch_skinny_st_chunked(x, DT, M, K, ldx, qw, scales, zeros, N, 1 << glog, r, y, YDT, ldy, st);
   if (const int nblk = skinny_cu_blocks(M, N, K)) {
     // deeper ring for long K slices (few rows per block)
     const int64_t rows = (N + nblk - 1) / nblk, tiles = (rows + 15) / 16;
@@ -959,7 +961,7 @@ namespace awq {
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int group) {
   if (M <= 0 || N <= 0 || K <= 0 || group <= 0 || (M == 1 && gemv1_supported(K, N))) return 0;
   if (mid_supported(M, N, K)) return mid_ws_bytes(M, N, K);
-  if (skinny_st_blocks(M, N, K, group) || awqk::skinny_cu_blocks(M, N, K)) return 0;
+  if (skinny_st_chunks(M, N, K, group) || awqk::skinny_cu_blocks(M, N, K)) return 0;
   return awqk::gemm_ws(nullptr, M, N, K, group).bytes;
 }
 
