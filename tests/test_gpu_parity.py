@@ -160,7 +160,7 @@ def test_skinny_product_parity(M, N, K, dtype, ydt, with_r):
     (8, 3000, 11008, F16, F16, True, 128),        # two passes of 43 units, one tile per block
     (16, 3000, 8192, BF16, torch.float32, True, 128),  # K fits the threads, not LDS: two passes
     (2, 8192, 28672, F16, F16, False, 128),       # four passes, two tiles per block
-    (12, 1500, 20608, F16, torch.float32, True, 64),   # six passes, the last one shorter
+    (12, 1500, 20608, F16, torch.float32, True, 64),   # eight passes, the last one shorter
     (5, 2000, 16640, BF16, BF16, True, 256),      # groups of 256 over three passes
     (4, 63488, 8448, F16, torch.float32, True, 256),   # 16 tiles per block: one item per wave
 ])

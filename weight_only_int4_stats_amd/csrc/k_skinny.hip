@@ -32,9 +32,9 @@
 //    pieces of one 8-channel column and holds one 1/s vector, so a pass covers
 //    at most 8192 channels.  When the tokens' activations do not fit LDS or
 //    the block's threads at once, they are staged in passes of whole units
-//    (blocks of at most 16 tiles, one item per wave): a wave runs the units of
-//    its slice inside the pass, issues the next pass's first units, and the
-//    block restages once every wave has left X.
+//    (blocks of at most 16 tiles, one item per wave): in every pass each wave
+//    runs its slice of the pass's units, issues its first units of the next
+//    pass, and the block restages once every wave has left X.
 //  * A wave's instructions issue in order, and the memory pipeline holds a
 //    wave at a load's issue while the weight stream flows, so a wave that
 //    issues its weight loads first cannot stage until the stream has mostly
@@ -130,9 +130,11 @@ inline int64_t st_kpass(int64_t M, int64_t K, int64_t rows_max, int glog) {
   if (st_pieces(M, K) != 0 && st_layout(M, K, rows_max, glog, K).total <= kStLdsMax) return K;
   if (rows_max > 16 * 16 || (rows_max > 12 && rows_max <= 16 && M >= 8)) return 0;
   const int64_t G = K >> 7;
+  const int maxp = glog == 6 ? 4 : kStMaxPieces;   // groups of 64: at most 4 pieces (registers)
   for (int64_t np = 2; np <= G; ++np) {
     const int64_t kp = (G + np - 1) / np * 128;
-    if (st_pieces(M, kp) != 0 && st_layout(M, K, rows_max, glog, kp).total <= kStLdsMax) return kp;
+    const int pc = st_pieces(M, kp);
+    if (pc != 0 && pc <= maxp && st_layout(M, K, rows_max, glog, kp).total <= kStLdsMax) return kp;
   }
   return 0;
 }
@@ -181,12 +183,19 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(qw + r0 * KW), (short)0, nrows * (int)KW * 4, kBufferWord3);
   int it = wv;
-  int tile = 0, g0 = 0, g1 = 0;
+  int tile = 0, ksi = 0, g0 = 0, g1 = 0;
   auto set_item = [&](int item) {
     tile = item / ksl;
-    const int ks = item - tile * ksl;
-    g0 = (int)((int64_t)ks * G / ksl);
-    g1 = (int)((int64_t)(ks + 1) * G / ksl);
+    ksi = item - tile * ksl;
+    g0 = (int)((int64_t)ksi * G / ksl);
+    g1 = (int)((int64_t)(ksi + 1) * G / ksl);
+  };
+  // with passes, the item's units in pass ps: slice ksi of the pass's units
+  auto pass_range = [&](int ps, int& a, int& e) {
+    const int p0 = ps * UPp;
+    const int up = G - p0 < UPp ? G - p0 : UPp;
+    a = p0 + ksi * up / ksl;
+    e = p0 + (ksi + 1) * up / ksl;
   };
   const bool have = it < nitems;                 // wave-uniform
   u32x4 wq[kStQ];
@@ -212,8 +221,10 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   };
   auto issue_weights = [&]() {
     set_item(have ? it : 0);
+    int a = g0, e = g1;
+    if constexpr (MULTI) pass_range(0, a, e);
 #pragma unroll
-    for (int d = 0; d < kStQ; ++d) load_unit(d, g0 + d, MULTI ? (g1 < UPp ? g1 : UPp) : g1);
+    for (int d = 0; d < kStQ; ++d) load_unit(d, a + d, e);
     __builtin_amdgcn_sched_barrier(0);
   };
   // ---- staging: its loads, then mid() (the weights' issue when every wave
@@ -434,16 +445,17 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   // ring in the same registers from the loads to the products.
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (MULTI) {
-    // one item per wave.  Pass ps runs the item's units inside the staged
-    // channels; before the next pass is staged over it, the wave issues that
-    // pass's first units and every wave leaves X.
+    // one item per wave.  In pass ps the item runs slice ksi of the pass's
+    // units (so every wave works in every pass); before the next pass is
+    // staged over X, the wave issues that pass's first units and every wave
+    // leaves X.
     for (int ps = 0;; ++ps) {
-      const int pa = g0 > ps * UPp ? g0 : ps * UPp;
-      const int pe = g1 < (ps + 1) * UPp ? g1 : (ps + 1) * UPp;
+      int pa, pe;
+      pass_range(ps, pa, pe);
       if (have) acc = run_item(acc, pa, pe, ps * UPp);
       if (ps + 1 >= npass) break;
-      const int na = g0 > (ps + 1) * UPp ? g0 : (ps + 1) * UPp;
-      const int ne = g1 < (ps + 2) * UPp ? g1 : (ps + 2) * UPp;
+      int na, ne;
+      pass_range(ps + 1, na, ne);
       stage(
           [&] {
             __builtin_amdgcn_sched_barrier(0);    // the activations' loads first
@@ -506,7 +518,7 @@ hipError_t st_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, con
                      (uint32_t)L.pinv, (uint32_t)L.meta, L.meta_pitch, (int)kp)
 #define AWQ_STG(NP)                                     \
   if (multi) {                                          \
-    if (glog == 6) AWQ_ST(NP, true, false, true);       \
+    if (glog == 6) AWQ_ST(NP < 4 ? NP : 4, true, false, true); \
     else AWQ_ST(NP, false, false, true);                \
   } else if (glog == 6) AWQ_ST(NP, true, false, false); \
   else if (split) AWQ_ST(NP, false, true, false);       \
@@ -539,10 +551,16 @@ int skinny_st_blocks(int64_t M, int64_t N, int64_t K, int group) {
 }
 
 // Row chunks that the kernel takes one launch at a time: 1 when one launch
-// covers the layer; else the fewest (2..16) whose every chunk one launch
-// covers (the block's steps and zero points limit its rows); 0 if none.
+// covers the layer; when only the block's steps and zero points (at most 8192
+// pairs) keep one launch from covering it, the fewest chunks (2..16) whose
+// every chunk one launch covers; else 0.
 int skinny_st_chunks(int64_t M, int64_t N, int64_t K, int group) {
   if (skinny_st_blocks(M, N, K, group)) return 1;
+  if (group <= 0 || K % group != 0 || N < 1) return 0;
+  const int64_t cus = device_cus();
+  const int64_t nblk = N < cus ? N : cus;
+  const int64_t rows_max = (N + nblk - 1) / nblk;
+  if (rows_max * (K / group) <= 1024 * awqk::kStMetaPer) return 0;
   for (int64_t c = 2; c <= 16 && c <= N; ++c)
     if (skinny_st_blocks(M, N / c, K, group) && skinny_st_blocks(M, (N + c - 1) / c, K, group)) return (int)c;
   return 0;
