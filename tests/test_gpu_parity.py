@@ -732,6 +732,22 @@ def test_skinny_one_hot_exact_split_path(M, N, K):
         assert np.array_equal(f32(y), ref.astype(np.float32)), (M, N, K, k)
 
 
+@pytest.mark.parametrize("M,N,K", [(4, 4096, 4096), (2, 8192, 8192), (8, 3000, 4224), (5, 11008, 3968)])
+def test_skinny_one_hot_exact_lds_ring(M, N, K):
+    """The 2..16-token product with the packed words copied through LDS in
+    whole 128-byte row pieces (unit pairs): one-hot tokens stay exact, also
+    where the unit count is odd (the last pair holds one unit) and where the
+    loader/stager split is on (K = 3968)."""
+    words, step, z = _random_packed(N, K, 41 + M)
+    for k in (0, 127, 128, K - 129, K - 1):
+        x = torch.zeros((M, K), dtype=F16)
+        x[:, k] = 1.0
+        y = awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                               gpu(torch.from_numpy(z)), out_dtype=torch.float32)
+        ref = O.w4a16_matmul(f32(x), words, step, z)
+        assert np.array_equal(f32(y), ref.astype(np.float32)), (M, N, K, k)
+
+
 @pytest.mark.parametrize("nbytes,blocks,unroll", [(1024, 1, 1), (23601152, 256, 4), (3 * 1024 * 1037, 300, 8),
                                                   (64 * 1024, 1000, 2)])
 def test_read_stream_xor(nbytes, blocks, unroll):

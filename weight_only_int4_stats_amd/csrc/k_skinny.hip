@@ -35,6 +35,12 @@
 //    (blocks of at most 16 tiles, one item per wave): in every pass each wave
 //    runs its slice of the pass's units, issues its first units of the next
 //    pass, and the block restages once every wave has left X.
+//  * When LDS has room beside the staged activations (one pass, groups of 128
+//    or 256), the packed words come through a per-wave LDS ring: each copy
+//    moves 8 rows x 128 bytes (whole lines, two units) by LDS DMA, and a lane
+//    reads its row's 16 bytes of a unit back in the matrix-core layout.  A
+//    load of 16 rows x 64 bytes straight into registers (the other path)
+//    streams the same bytes markedly slower.
 //  * A wave's instructions issue in order, and the memory pipeline holds a
 //    wave at a load's issue while the weight stream flows, so a wave that
 //    issues its weight loads first cannot stage until the stream has mostly
@@ -54,6 +60,8 @@ constexpr int kStQ = 8;              // 128-channel units of packed words in fli
 constexpr int kStMetaPer = 8;        // staged (step, zero point) pairs per thread
 constexpr int kStMaxPieces = 8;      // staged 8-channel activation pieces per thread
 constexpr size_t kStLdsMax = 160 * 1024;
+constexpr int kStPQ = 2;             // unit pairs in flight per wave when the words come through LDS
+constexpr size_t kStRing = (size_t)kStWaves * kStPQ * 2048;   // those pairs' LDS ring
 
 template <int YDT>
 __device__ __forceinline__ void store_yst(void* y, int64_t idx, float v) {
@@ -85,6 +93,7 @@ __device__ __forceinline__ float dpp_f(float v) {
 struct StLayout {
   size_t sums, pinv, meta, total;
   int meta_pitch;   // (step, zero) pairs per staged row
+  size_t ring, total_lw;   // the words' LDS ring after the rest, and the total with it
 };
 
 inline StLayout st_layout(int64_t M, int64_t K, int64_t rows_max, int glog, int64_t kpass) {
@@ -97,6 +106,8 @@ inline StLayout st_layout(int64_t M, int64_t K, int64_t rows_max, int glog, int6
   L.pinv = L.sums + (size_t)(glog == 6 ? K / 64 : K / 128) * 16 * 4;
   L.meta = L.pinv + (size_t)(K / 128) * 16 * 4;
   L.total = L.meta + (size_t)rows_max * L.meta_pitch * 8;
+  L.ring = awq::align_up(L.total, 16);
+  L.total_lw = L.ring + kStRing;
   return L;
 }
 
@@ -139,12 +150,22 @@ inline int64_t st_kpass(int64_t M, int64_t K, int64_t rows_max, int glog) {
   return 0;
 }
 
-template <int DT, int YDT, bool HAS_R, int NP, bool G64, bool SPLIT, bool MULTI>
+// 16 bytes per lane into LDS (LDS DMA, non-temporal; an offset past the
+// buffer's range writes 0).  Issued from asm, so the compiler adds no wait of
+// its own before the LDS reads: the caller waits on the vector memory counter.
+__device__ __forceinline__ void st_dma16(const i32x4& rs, uint32_t lds, uint32_t voff) {
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "s"(lds), "v"(voff), "s"(rs) : "memory");
+}
+
+template <int DT, int YDT, bool HAS_R, int NP, bool G64, bool SPLIT, bool MULTI, bool LW>
 __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
     const uint16_t* __restrict__ x, int M, int64_t K, int64_t ldx, const float* __restrict__ r,
     const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, int64_t N, void* __restrict__ y, int64_t ldy, int glog,
-    uint32_t o_sums, uint32_t o_pinv, uint32_t o_meta, int mp, int kpass) {
+    uint32_t o_sums, uint32_t o_pinv, uint32_t o_meta, int mp, int kpass, uint32_t o_ring) {
+  static_assert(!LW || (!MULTI && !G64), "words through LDS: one pass, groups >= 128");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_st[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,8 +208,16 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
   auto set_item = [&](int item) {
     tile = item / ksl;
     ksi = item - tile * ksl;
-    g0 = (int)((int64_t)ksi * G / ksl);
-    g1 = (int)((int64_t)(ksi + 1) * G / ksl);
+    if constexpr (LW) {
+      // slices of whole unit pairs (the last pair of an odd G holds one unit)
+      const int G2 = (G + 1) >> 1;
+      g0 = 2 * (int)((int64_t)ksi * G2 / ksl);
+      g1 = 2 * (int)((int64_t)(ksi + 1) * G2 / ksl);
+      g1 = g1 < G ? g1 : G;
+    } else {
+      g0 = (int)((int64_t)ksi * G / ksl);
+      g1 = (int)((int64_t)(ksi + 1) * G / ksl);
+    }
   };
   // with passes, the item's units in pass ps: slice ksi of the pass's units
   auto pass_range = [&](int ps, int& a, int& e) {
@@ -219,12 +248,36 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
       wq[slot] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   };
+  // With LW the words come through a per-wave LDS ring of kStPQ unit pairs:
+  // a pair is two 1 KB copies (rows 0..7 and 8..15 of the tile, 128 bytes =
+  // both units of each row, so every copy reads whole 128-byte lines), with
+  // chunk c of row r' of half h at 16-byte slot 8 r' + (c ^ (r'/2 + 4h)); a
+  // lane then reads its row's 16 bytes of a unit with one conflict-free
+  // 128-bit LDS read.  (Loads of 16 rows x 64 bytes each, the register path,
+  // read the same bytes markedly slower.)
+  const uint32_t rowb = KW * 4;
+  const i32x4 wrs4 = rsrc4(qw + r0 * KW, (uint32_t)nrows * rowb);
+  const uint32_t ring_w = __builtin_amdgcn_readfirstlane(lds_addr(lds_st) + o_ring + (uint32_t)wv * kStPQ * 2048);
+  const int dq = lane >> 3, ds = lane & 7;
+  const uint32_t dv0 = (uint32_t)dq * rowb + (uint32_t)((ds ^ (dq >> 1)) * 16);
+  const uint32_t dv1 = (uint32_t)(dq + 8) * rowb + (uint32_t)((ds ^ ((dq >> 1) | 4)) * 16);
+  auto issue_pair = [&](int slot, int q, int qend) {
+    const bool ok = have && q < qend;
+    const uint32_t uo = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)(tile * 16) * rowb + (uint32_t)q * 128 : kBufferOob);
+    st_dma16(wrs4, ring_w + (uint32_t)slot * 2048, dv0 + uo);
+    st_dma16(wrs4, ring_w + (uint32_t)slot * 2048 + 1024, dv1 + uo);
+  };
   auto issue_weights = [&]() {
     set_item(have ? it : 0);
-    int a = g0, e = g1;
-    if constexpr (MULTI) pass_range(0, a, e);
+    if constexpr (LW) {
 #pragma unroll
-    for (int d = 0; d < kStQ; ++d) load_unit(d, a + d, e);
+      for (int d = 0; d < kStPQ; ++d) issue_pair(d, (g0 >> 1) + d, (g1 + 1) >> 1);
+    } else {
+      int a = g0, e = g1;
+      if constexpr (MULTI) pass_range(0, a, e);
+#pragma unroll
+      for (int d = 0; d < kStQ; ++d) load_unit(d, a + d, e);
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   // ---- staging: its loads, then mid() (the weights' issue when every wave
@@ -367,6 +420,11 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
     } else {
       issue_weights();
     }
+  } else if constexpr (LW) {
+    // the copies after the conversion: the compiler's waits for the staging
+    // loads would otherwise wait for the copies issued after them too
+    stage([] {}, 0, std::true_type{});
+    issue_weights();
   } else {
     stage(issue_weights, 0, std::true_type{});
   }
@@ -432,6 +490,49 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
     }
     return acc;
   };
+  // The item through the LDS ring: per pair, wait for its copies (the later
+  // pairs' may stay in flight), run its units, wait for the LDS reads, then
+  // copy pair q + kStPQ into the slot.
+  const uint8_t* wrow = lds_st + o_ring + (uint32_t)wv * kStPQ * 2048 + (rl >> 3) * 1024 + (rl & 7) * 128;
+  const int wsw = ((rl & 7) >> 1) | ((rl >> 3) << 2);
+  auto run_item_lw = [&](f32x4 acc) {
+    const int rowc = tile * 16 + rl < nrows ? tile * 16 + rl : nrows - 1;
+    const float2* mrow = meta + rowc * mp;
+    const int qa = g0 >> 1, qe = (g1 + 1) >> 1;
+    for (int qb = qa; qb < qe; qb += kStPQ) {
+#pragma unroll
+      for (int d = 0; d < kStPQ; ++d) {
+        const int q = qb + d;
+        if (q < qe) {                             // wave-uniform
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (kStPQ - 1)) : "memory");
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int g = 2 * q + u;
+            if (g < g1) {                         // wave-uniform
+              const u32x4 w = *reinterpret_cast<const u32x4*>(wrow + d * 2048 + (((4 * u + b) ^ wsw) * 16));
+              u32x4 xa[4];
+              const f32x4 pv = *reinterpret_cast<const f32x4*>(pinv + g * 16 + 4 * b);
+              const uint8_t* p = xrow + (size_t)(128 * g + 32 * b) * 2;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4*>(p + 16 * i);
+              const f32x4 sv = *reinterpret_cast<const f32x4*>(sums + g * 16 + 4 * b);
+              const float2 md = mrow[g >> gsh];
+              f32x4 part;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) part[v] = -md.y * sv[v];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) part = mfma16h(xa[i], st_unpack(w[i]), part);
+#pragma unroll
+              for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(md.x * pv[v], part[v], acc[v]);
+            }
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        issue_pair(d, q + kStPQ, qe);
+      }
+    }
+    return acc;
+  };
   // 16 x 16 result layout: weight row = lane % 16, tokens 4 (lane / 16) + v
   auto store_direct = [&](const f32x4& a) {
 #pragma unroll
@@ -468,6 +569,20 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny_st(
       st_sync();
     }
     if (have && ksl == 1) store_direct(acc);
+  } else if constexpr (LW) {
+    if (have) {
+      acc = run_item_lw(acc);
+      if (ksl == 1) store_direct(acc);
+    }
+    if (ksl == 1) {
+      for (it = wv + kStWaves; it < nitems; it += kStWaves) {
+        set_item(it);
+#pragma unroll
+        for (int d = 0; d < kStPQ; ++d) issue_pair(d, (g0 >> 1) + d, (g1 + 1) >> 1);
+        store_direct(run_item_lw(f32x4{0.0f, 0.0f, 0.0f, 0.0f}));
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the ring's last (empty) copies
   } else {
     if (have) {
       acc = run_item(acc, g0, g1, 0);
@@ -507,22 +622,25 @@ hipError_t st_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, con
   const int64_t kp = st_kpass(M, K, rows_max, glog);
   const bool multi = kp < K;
   const StLayout L = st_layout(M, K, rows_max, glog, kp);
-  size_t lds = L.total;
-  if (lds < 81 * 1024) lds = 81 * 1024;           // one block per compute unit
   const bool split = !multi && st_split(M, K, rows_max, glog);
+  const bool lw = glog != 6 && !multi && L.total_lw <= kStLdsMax;
+  size_t lds = lw ? L.total_lw : L.total;
+  if (lds < 81 * 1024) lds = 81 * 1024;           // one block per compute unit
   const int np = split ? st_pieces(M, K, 512) : st_pieces(M, kp);
   const dim3 grid((unsigned)nblk), block(1024);
-#define AWQ_ST(NP, G64, SPLIT, MULTI)                                                                \
-  hipLaunchKernelGGL((k_gemm_skinny_st<DT, YDT, HAS_R, NP, G64, SPLIT, MULTI>), grid, block, lds, st, x, \
+#define AWQ_ST(NP, G64, SPLIT, MULTI, LW)                                                            \
+  hipLaunchKernelGGL((k_gemm_skinny_st<DT, YDT, HAS_R, NP, G64, SPLIT, MULTI, LW>), grid, block, lds, st, x, \
                      (int)M, K, ldx, r, qw, scales, zeros, N, y, ldy, glog, (uint32_t)L.sums,         \
-                     (uint32_t)L.pinv, (uint32_t)L.meta, L.meta_pitch, (int)kp)
+                     (uint32_t)L.pinv, (uint32_t)L.meta, L.meta_pitch, (int)kp, (uint32_t)L.ring)
 #define AWQ_STG(NP)                                     \
   if (multi) {                                          \
-    if (glog == 6) AWQ_ST(NP < 4 ? NP : 4, true, false, true); \
-    else AWQ_ST(NP, false, false, true);                \
-  } else if (glog == 6) AWQ_ST(NP, true, false, false); \
-  else if (split) AWQ_ST(NP, false, true, false);       \
-  else AWQ_ST(NP, false, false, false)
+    if (glog == 6) AWQ_ST(NP < 4 ? NP : 4, true, false, true, false); \
+    else AWQ_ST(NP, false, false, true, false);         \
+  } else if (glog == 6) AWQ_ST(NP, true, false, false, false); \
+  else if (split && lw) AWQ_ST(NP, false, true, false, true); \
+  else if (split) AWQ_ST(NP, false, true, false, false); \
+  else if (lw) AWQ_ST(NP, false, false, false, true);   \
+  else AWQ_ST(NP, false, false, false, false)
   if (np == 1) AWQ_STG(1);
   else if (np == 2) AWQ_STG(2);
   else if (np == 4) AWQ_STG(4);
