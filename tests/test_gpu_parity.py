@@ -229,6 +229,23 @@ def test_gemm_parity(M, N, K, dtype, ydt, with_r):
     assert err <= GEMM_TOL
 
 
+@pytest.mark.parametrize("M,N,K,dtype,ydt,with_r,group", [
+    (2048, 8092, 256, BF16, torch.float32, True, 128),   # 256-wide tiles only, ragged last tile
+    (2000, 25000, 256, F16, BF16, False, 128),           # 768 wide + 32 half-width tiles, ragged m and n
+    (2048, 28672, 128, BF16, F16, True, 128),            # the 70B up-projection's cut, K of one group
+    (1100, 14000, 512, F16, torch.float32, True, 64),    # groups of 64 across the cut
+    (300, 5000, 1024, BF16, BF16, False, 256),           # few tiles: half-width tiles only
+])
+def test_gemm_tile_widths(M, N, K, dtype, ydt, with_r, group):
+    """The tiled GEMM cuts the columns into 256-wide tiles and 128-wide ones
+    so that the last round of tiles on the compute units is not left half
+    empty; sampled output channels on both sides of the cut and in the ragged
+    tails against the oracle."""
+    err, nrow = _sampled_product(M, N, K, dtype, ydt, with_r, seed=3 * M + N + K, group=group)
+    print(f"gemm M={M} N={N} K={K} g={group} {dtype} -> {ydt}: rel max err {err:.3e} on {nrow} channels")
+    assert err <= GEMM_TOL
+
+
 def test_product_special_cases():
     """q == z gives 0; a one-hot x picks the dequantized column.  The GEMV
     accumulates exact int4 x activation products, so the one-hot column is

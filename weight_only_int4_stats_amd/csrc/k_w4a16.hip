@@ -123,18 +123,25 @@ __device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, f16x2 c24, f16x2 c
   return out;
 }
 
+// The same from the constant table's two words: cx = D' 2^24 | D' 2^20 << 16
+// and nzd = -D' z twice (the broadcasts of cx's halves fold into the packed
+// fma's operand selection).
+__device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, uint32_t cx, uint32_t nzd) {
+  const f16x2 c = as_f16x2(cx);
+  return dequant_word_f16(w, __builtin_shufflevector(c, c, 0, 0), __builtin_shufflevector(c, c, 1, 1),
+                          as_f16x2(nzd));
+}
 // 256 x 256 output tile per block of 8 waves (2 along m x 4 along n, each wave
 // 128 x 64 = 8 x 4 blocks of 16 x 16: the 16 x 16 x 32 product moves half the
 // accumulator data per flop of the 32 x 32 x 16 one and runs at a higher clock
-// under the chip's power limit), 64 k per stage, three LDS stages
+// under the chip's power limit; 256 x 128 tiles, 128 x 32 per wave, fill a
+// last round of tiles), 64 k per stage, three LDS stages
 // filled by LDS DMA (buffer_load ... lds) two stages ahead of the matrix-core
 // work:
 //   A  256 rows x 64 k of fp16 activations, row r's 16-byte chunk c stored at
-//      chunk c ^ ((r / 2) mod 8): a 128-byte row is half the width of the 64
-//      banks, so the 16 rows that one 16-lane pass of a 128-bit read touches
-//      land on 16 different 16-byte bank slots
+//      chunk c ^ a_swz(r)
 //   B  256 columns x 8 packed words; per 32 columns the first 16 bytes of
-//      each column, then the last 16 (again 16 lanes -> 16 bank slots)
+//      each column, then the last 16
 //   C  256 columns of dequantization constants (8 bytes each)
 // Operand k order: in k32 step st, lane group h (lanes 16 h .. 16 h + 15) holds
 // packed word 2 h + st of its column (8 k), so that its two words are one
@@ -159,38 +166,79 @@ __global__ __launch_bounds__(256) void k_gemm_prep(const uint16_t* __restrict__ 
   else gemm_consts_block((int64_t)blockIdx.x - M, scales, zeros, N, G, en, ctab);
 }
 
+// Position of an A row's 16-byte chunks in LDS: chunk c of row r at
+// c ^ a_swz(r) = c ^ ((r / 2) mod 8): the 16 rows one 16-lane group reads
+// land on 16 different 16-byte slots of a 256-byte span.  The bank-conflict
+// counter shows that a 128-bit read is served 8 lanes per 128 bytes, so this
+// layout is 2-way conflicted within each 8-lane group; (r ^ (r / 8)) mod 8
+// removes the conflicts (counter at 0.6 % of the LDS busy cycles, from 44 %)
+// but measured 0.3-1 % slower on the 70B prefill shapes (the LDS is not what
+// limits this loop), so the layout stays.
+__device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
+
 constexpr int kMT = 256;                // tile rows (m)
-constexpr int kNT = 256;                // tile columns (n)
 constexpr int kBK = 64;                 // k per stage
 constexpr int kXcds = 8;                // L2 slices (block i -> slice i mod 8)
 constexpr int kAStage = kMT * kBK * 2;  // 32 KB
-constexpr int kBStage = kNT * 8 * 4;    // 8 KB
-constexpr int kCStage = kNT * 8;        // 2 KB
-constexpr int kStage = kAStage + kBStage + kCStage;
 
-inline int64_t gemm_blocks(int64_t M, int64_t N) {
-  const int64_t T = ((N + kNT - 1) / kNT) * ((M + kMT - 1) / kMT);
-  return kXcds * ((T + kXcds - 1) / kXcds);
+// A tile of 256 rows x 64 NB columns: each of the 8 waves takes 128 rows x
+// 16 NB columns (NB = 4: 256-wide tiles; NB = 2: 128-wide tiles, same k loop)
+template <int NB>
+struct GemmTile {
+  static constexpr int NT = 64 * NB;             // tile columns
+  static constexpr int BStage = NT * 8 * 4;      // packed words
+  static constexpr int CStage = NT * 8;          // dequantization constants
+  static constexpr int Stage = kAStage + BStage + CStage;
+  static constexpr int BWaves = NT / 32;         // waves copying packed columns (32 each)
+  static constexpr int CWaves = NT / 128;        // waves copying constants (128 columns each)
+};
+constexpr int kStageMax = GemmTile<4>::Stage;
+
+// How the columns are cut: [0, nsplit) in 256-wide tiles, [nsplit, N) in
+// 128-wide ones.  A compute unit holds one block, so the launch runs in rounds
+// of one tile per unit; a 128-wide tile takes about half as long as a 256-wide
+// one.  The cut is chosen to minimise the estimated rounds, so that a last
+// round that would be partly empty (896 tiles of the 2048 x 28672 product on
+// 256 units: 3.5 rounds) is spread over twice as many half-width tiles.
+struct GemmPlan {
+  int64_t nsplit, wide_tiles, narrow_tiles, wide_blocks, blocks;
+};
+
+inline GemmPlan gemm_plan(int64_t M, int64_t N) {
+  const int64_t cus = awq::device_cus() > 0 ? awq::device_cus() : 256;
+  const int64_t mt = (M + kMT - 1) / kMT, ntw = (N + 255) / 256;
+  auto rounds = [&](int64_t t) { return (double)((t + cus - 1) / cus); };
+  GemmPlan best{};
+  double best_cost = 1e300;
+  for (int64_t a = ntw; a >= 0; --a) {
+    const int64_t ns = a * 256 < N ? a * 256 : N;
+    const int64_t tw = mt * a, th = mt * ((N - ns + 127) / 128);
+    const double cost = rounds(tw) + 0.55 * rounds(th) + (tw > 0 && th > 0 ? 0.02 : 0.0);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best.nsplit = ns;
+      best.wide_tiles = tw;
+      best.narrow_tiles = th;
+    }
+  }
+  best.wide_blocks = kXcds * ((best.wide_tiles + kXcds - 1) / kXcds);
+  best.blocks = best.wide_blocks + kXcds * ((best.narrow_tiles + kXcds - 1) / kXcds);
+  return best;
 }
 
-template <int YDT>
-__global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, int64_t M, int64_t K,
-                                             const int* __restrict__ pm,
-                                             const uint32_t* __restrict__ qw,
-                                             const uint32_t* __restrict__ ctab,
-                                             const int* __restrict__ en, int64_t N,
-                                             void* __restrict__ y, int64_t ldy, int glog, int vec_ok) {
-  // three LDS arrays, the loop unrolled by three: each stage is a known array
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[kStage];
-
-  // ---- tile of this block
-  const int64_t ntile = (N + kNT - 1) / kNT, mtile = (M + kMT - 1) / kMT, T = ntile * mtile;
-  const int64_t per = (T + kXcds - 1) / kXcds;
-  const int64_t slot = blockIdx.x / kXcds;
-  const int64_t t = (int64_t)(blockIdx.x % kXcds) * per + slot;
-  if (slot >= per || t >= T) return;
+// One output tile of width 64 NB over the columns [nb, ne): tile t of that
+// region in grouped order.
+template <int YDT, int NB>
+__device__ __forceinline__ void gemm_tile(uint8_t* __restrict__ lds0, uint8_t* __restrict__ lds1,
+                                          uint8_t* __restrict__ lds2, int64_t t,
+                                          const uint16_t* __restrict__ xq, int64_t M, int64_t K,
+                                          const int* __restrict__ pm, const uint32_t* __restrict__ qw,
+                                          const uint32_t* __restrict__ ctab, const int* __restrict__ en,
+                                          int64_t N, int64_t nb, int64_t ne, void* __restrict__ y,
+                                          int64_t ldy, int glog, int vec_ok) {
+  using Tl = GemmTile<NB>;
+  constexpr int NT = Tl::NT;
+  const int64_t ntile = (ne - nb + NT - 1) / NT, mtile = (M + kMT - 1) / kMT;
   // tile t in grouped order: 4 m-tiles at a time, m fastest, so the ~32
   // blocks a slice runs at once cover about 4 x 8 tiles and share both
   // operands in its L2
@@ -199,7 +247,7 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
   const int64_t gm = mtile - g * 4 < 4 ? mtile - g * 4 : 4;
   const int64_t mt = g * 4 + rr % gm;
   const int64_t m0 = mt * kMT;
-  const int64_t n0 = (rr / gm) * kNT;
+  const int64_t n0 = nb + (rr / gm) * NT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -208,76 +256,81 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
   const int64_t G = K >> glog;                 // groups of 2^glog >= kBK channels per row
   const int64_t S = K / kBK;
   const int rows = (int)(M - m0 < kMT ? M - m0 : kMT);
-  const int cols = (int)(N - n0 < kNT ? N - n0 : kNT);
+  const int cols = (int)(ne - n0 < NT ? ne - n0 : NT);
   const i32x4 ars = rsrc4(xq + m0 * K, (uint32_t)(rows * K * 2));
   const i32x4 brs = rsrc4(qw + n0 * (K >> 3), (uint32_t)(cols * (K >> 1)));
   const i32x4 crs = rsrc4(ctab + n0 * 2, (uint32_t)(((G - 1) * N + cols) * 8));
+  // copies per stage issued by this wave: 4 A, 1 B (waves < BWaves), 1 C (waves < CWaves)
+  const int nops = 4 + (wv < Tl::BWaves ? 1 : 0) + (wv < Tl::CWaves ? 1 : 0);
 
   // A copy j (0..31) fills LDS bytes [1024 j, 1024 j + 1024) = rows 8 j .. 8 j + 7;
   // wave w issues j = 4 w + u.  Lane i: row r = 8 j + i / 8 at LDS chunk i % 8,
-  // which holds global chunk (i % 8) ^ ((r / 2) % 8).
+  // which holds global chunk (i % 8) ^ a_swz(r).
   uint32_t aoff[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 8 * (4 * wv + u) + (lane >> 3);
-    aoff[u] = (uint32_t)(r * K * 2 + (((lane & 7) ^ ((r >> 1) & 7)) * 16));
+    aoff[u] = (uint32_t)(r * K * 2 + (((lane & 7) ^ a_swz(r)) * 16));
   }
   // B: wave w copies columns 32 w .. 32 w + 31; lane i takes half i / 32 of
   // column 32 w + i % 32
   const uint32_t boff = (uint32_t)((32 * wv + (lane & 31)) * (K >> 1) + (lane >> 5) * 16);
-  // C: waves 0 and 1 copy 128 columns each (two columns per lane)
+  // C: wave w copies columns 128 w .. 128 w + 127 (two columns per lane)
   const uint32_t coff = (uint32_t)((wv * 128 + lane * 2) * 8);
 
   // copy u of stage s into the stage array at base: u 0..3 the wave's A rows,
-  // 4 its B columns and (waves 0, 1) its constants
+  // 4 its B columns and constants
   auto copy = [&](int64_t s, const uint8_t* base, int u) {
     const uint32_t k0 = (uint32_t)(s * kBK);
     const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(base));
     if (u < 4) {
       dma16(ars, lb + (4 * wv + u) * 1024, aoff[u], k0 * 2);
     } else {
-      dma16(brs, lb + kAStage + wv * 1024, boff, k0 >> 1);
-      if (wv < 2) dma16(crs, lb + kAStage + kBStage + wv * 1024, coff, (uint32_t)((k0 >> glog) * N * 8));
+      if (wv < Tl::BWaves) dma16(brs, lb + kAStage + wv * 1024, boff, k0 >> 1);
+      if (wv < Tl::CWaves)
+        dma16(crs, lb + kAStage + Tl::BStage + wv * 1024, coff, (uint32_t)((k0 >> glog) * N * 8));
     }
   };
   auto issue = [&](int64_t s, const uint8_t* base) {
 #pragma unroll
     for (int u = 0; u < 5; ++u) copy(s, base, u);
   };
+  // wait until only the copies of the newest stage are in flight (and, with
+  // lgkm, every LDS access of the wave has completed)
+  auto wait_stage = [&](bool lgkm) {
+    if (lgkm) {
+      if (nops == 6) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(6));
+      else if (nops == 5) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(5));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4));
+    } else {
+      if (nops == 6) __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));
+      else if (nops == 5) __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+    }
+  };
 
-  f32x4 acc[8][4];
+  f32x4 acc[8][NB];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[a][b][v] = 0.0f;
 
   // 16 x 16 x 32 products.  Operand k order: lane group h = lane / 16 holds
   // packed words 2 h (step 0) and 2 h + 1 (step 1) of its column, one 8-byte
   // LDS read per stage, and A chunk 2 h + st to match.  Sub-step q = 2 st + hh
-  // multiplies the row blocks 4 hh .. 4 hh + 3 with the four column blocks; the
+  // multiplies the row blocks 4 hh .. 4 hh + 3 with the NB column blocks; the
   // next sub-step's four A fragments are read meanwhile.
-  struct Frag { f16x2 c24[4], c20[4], nzd[4]; uint2 bw[4]; };
-  struct Raw { uint2 c[4]; uint2 w[4]; };
+  struct Raw { uint2 c[NB]; uint2 w[NB]; };
   auto load_raw = [&](const uint8_t* base, Raw& w) {
     const int h = lane >> 4;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int col = wn * 64 + nb * 16 + (lane & 15);
-      w.c[nb] = *reinterpret_cast<const uint2*>(base + kAStage + kBStage + col * 8);
-      w.w[nb] = *reinterpret_cast<const uint2*>(base + kAStage + (col >> 5) * 1024 + (h >> 1) * 512 +
-                                                (col & 31) * 16 + (h & 1) * 8);
-    }
-  };
-  auto decode = [&](const Raw& w, Frag& f) {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const f16x2 cx = as_f16x2(w.c[nb].x);
-      f.c24[nb] = __builtin_shufflevector(cx, cx, 0, 0);
-      f.c20[nb] = __builtin_shufflevector(cx, cx, 1, 1);
-      f.nzd[nb] = as_f16x2(w.c[nb].y);
-      f.bw[nb] = w.w[nb];
+    for (int nbk = 0; nbk < NB; ++nbk) {
+      const int col = wn * 16 * NB + nbk * 16 + (lane & 15);
+      w.c[nbk] = *reinterpret_cast<const uint2*>(base + kAStage + Tl::BStage + col * 8);
+      w.w[nbk] = *reinterpret_cast<const uint2*>(base + kAStage + (col >> 5) * 1024 + (h >> 1) * 512 +
+                                                 (col & 31) * 16 + (h & 1) * 8);
     }
   };
   auto load_a = [&](const uint8_t* base, int q, u32x4 (&a)[4]) {
@@ -285,23 +338,29 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 128 + (hh * 4 + i) * 16 + (lane & 15);
-      a[i] = *reinterpret_cast<const u32x4*>(base + r * 128 + (((2 * (lane >> 4) + st) ^ ((r >> 1) & 7)) * 16));
+      a[i] = *reinterpret_cast<const u32x4*>(base + r * 128 + (((2 * (lane >> 4) + st) ^ a_swz(r)) * 16));
     }
   };
-  const bool six = wv < 2;
 
-  Frag F;
-  Raw R;
+  Raw R;                // a stage's packed words and constants, straight from LDS
   u32x4 aE[4], aO[4];   // fragments of even and odd sub-steps
-  u32x4 bq[4];          // dequantized column blocks of the current k32 step
+  u32x4 bq[NB];         // dequantized column blocks of the current k32 step
   issue(0, lds0);
   issue(1, lds1);
-  if (six) __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));
-  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
+  wait_stage(false);
   lds_barrier();
   load_a(lds0, 0, aE);
   load_raw(lds0, R);
+#pragma unroll
+  for (int nbk = 0; nbk < NB; ++nbk) bq[nbk] = dequant_word_f16(R.w[nbk].x, R.c[nbk].x, R.c[nbk].y);
 
+  // One stage (64 k) in four sub-steps q = 2 st + hh.  The operands of k32
+  // step 0 are ready when the stage starts.  In sub-step 1 each column block's
+  // operands are replaced by step 1's as soon as its last product has been
+  // issued, and in sub-step 3 by the next stage's step 0 (its words and
+  // constants read right after the barrier), so the dequantization runs
+  // between the matrix products, three vector instructions after each from
+  // the fourth on, instead of ahead of them.
   auto stage = [&](int64_t s, const uint8_t* cur, const uint8_t* nxt, const uint8_t* nxt2) {
     const bool cp = s + 2 < S;
 #pragma unroll
@@ -310,21 +369,11 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
         copy(s + 2, nxt2, q);
         if (q == 3) copy(s + 2, nxt2, 4);
       }
-      if (q == 0) decode(R, F);
-      if ((q & 1) == 0) {
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          bq[nb] = dequant_word_f16(q ? F.bw[nb].y : F.bw[nb].x, F.c24[nb], F.c20[nb], F.nzd[nb]);
-      }
       if (q < 3) {
         load_a(cur, q + 1, (q & 1) ? aE : aO);
       } else {
-        if (cp) {
-          if (six) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(6));
-          else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(5));
-        } else {
-          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-        }
+        if (cp) wait_stage(true);
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
         lds_barrier();
         load_a(nxt, 0, aE);
         load_raw(nxt, R);
@@ -333,9 +382,18 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
       const u32x4 (&a)[4] = (q & 1) ? aO : aE;
       const int hh = q & 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int nbk = 0; nbk < NB; ++nbk) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[hh * 4 + i][nb] = mfma16h(a[i], bq[nb], acc[hh * 4 + i][nb]);
+        for (int i = 0; i < 4; ++i) acc[hh * 4 + i][nbk] = mfma16h(a[i], bq[nbk], acc[hh * 4 + i][nbk]);
+        if (q & 1) bq[nbk] = dequant_word_f16(q == 1 ? R.w[nbk].y : R.w[nbk].x, R.c[nbk].x, R.c[nbk].y);
+      }
+      if (q & 1) {
+#pragma unroll
+        for (int i = 0; i < 4 * NB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix product
+          if (i >= 3) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three vector instructions
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -346,34 +404,36 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
   }
 
   // 16x16 accumulator layout: column = lane % 16, row = 4 (lane / 16) + v.
-  // Each wave stages its 128 x 64 outputs through a private LDS area, 32 rows
-  // at a time, and stores whole 128-byte (fp32: 256-byte) row pieces with
-  // 16-byte stores; the row pitch is padded so that the writes of the four
-  // lane groups (rows 4 apart) and the 16-lane read passes hit distinct banks.
-  // Unaligned outputs, and columns of a ragged last tile, are stored one by one.
+  // Each wave stages its 128 x 16 NB outputs through a private LDS area, 32
+  // rows at a time, and stores whole row pieces with 16-byte stores; the row
+  // pitch is padded by 16 bytes so that the writes of the four lane groups
+  // (rows 4 apart) fall on different banks.  Unaligned outputs, and columns
+  // of a ragged last tile, are stored one by one.
+  constexpr int kWc = 16 * NB;                            // columns per wave
   constexpr int kEs = YDT == DT_F32 ? 4 : 2;              // output bytes
-  constexpr int kRowB = 64 * kEs;                         // bytes of a 64-column row piece
-  constexpr int kLd = kRowB + (YDT == DT_F32 ? 16 : 16);  // padded LDS pitch
-  constexpr int kLpr = kRowB / 16;                        // lanes per row (8 or 16)
-  constexpr int kRpi = 64 / kLpr;                         // rows per read pass (8 or 4)
-  static_assert(4 * 32 * kLd <= kStage, "four waves' staging in one stage array");
-  int en_l[4];
+  constexpr int kRowB = kWc * kEs;                        // bytes of a row piece
+  constexpr int kLd = kRowB + 16;                         // padded LDS pitch
+  constexpr int kLpr = kRowB / 16;                        // lanes per row
+  constexpr int kRpi = 64 / kLpr;                         // rows per read pass
+  static_assert(4 * 32 * kLd <= Tl::Stage, "four waves' staging in one stage array");
+  static_assert(32 % kRpi == 0, "read passes cover the 32 staged rows");
+  int en_l[NB];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int64_t n = n0 + wn * 64 + nb * 16 + (lane & 15);
-    en_l[nb] = n < N ? en[n] : 0;
+  for (int nbk = 0; nbk < NB; ++nbk) {
+    const int64_t n = n0 + wn * kWc + nbk * 16 + (lane & 15);
+    en_l[nbk] = n < ne ? en[n] : 0;
   }
   if (!vec_ok) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int64_t n = n0 + wn * 64 + nb * 16 + (lane & 15);
-      if (n >= N) continue;
+    for (int nbk = 0; nbk < NB; ++nbk) {
+      const int64_t n = n0 + wn * kWc + nbk * 16 + (lane & 15);
+      if (n >= ne) continue;
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int64_t m = m0 + wm * 128 + mb * 16 + 4 * (lane >> 4) + v;
-          if (m < M) store_y<YDT>(y, m * ldy + n, ldexpf(acc[mb][nb][v], -(pm[m] + en_l[nb])));
+          if (m < M) store_y<YDT>(y, m * ldy + n, ldexpf(acc[mb][nbk][v], -(pm[m] + en_l[nbk])));
         }
     }
     return;
@@ -391,9 +451,9 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
         const int64_t m = m0 + wm * 128 + mb * 16 + 4 * (lane >> 4) + v;
         const int pmm = m < M ? pm[m] : 0;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const float o = ldexpf(acc[mb][nb][v], -(pmm + en_l[nb]));
-          uint8_t* dst = stg + r * kLd + (nb * 16 + (lane & 15)) * kEs;
+        for (int nbk = 0; nbk < NB; ++nbk) {
+          const float o = ldexpf(acc[mb][nbk][v], -(pmm + en_l[nbk]));
+          uint8_t* dst = stg + r * kLd + (nbk * 16 + (lane & 15)) * kEs;
           if constexpr (YDT == DT_F32) *reinterpret_cast<float*>(dst) = o;
           else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)from_f32<YDT>(o);
         }
@@ -407,15 +467,15 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
       const int cb = (lane % kLpr) * 16;                  // byte offset in the row piece
       const u32x4 val = *reinterpret_cast<const u32x4*>(stg + r * kLd + cb);
       const int64_t m = m0 + wm * 128 + hp * 32 + r;
-      const int64_t n = n0 + wn * 64 + cb / kEs;
+      const int64_t n = n0 + wn * kWc + cb / kEs;
       if (m < M) {
         uint8_t* out = reinterpret_cast<uint8_t*>(y) + (m * ldy + n) * kEs;
-        if (n + 16 / kEs <= N) {
+        if (n + 16 / kEs <= ne) {
           *reinterpret_cast<u32x4*>(out) = val;
         } else {
 #pragma unroll
           for (int j = 0; j < 16 / kEs; ++j)
-            if (n + j < N) {
+            if (n + j < ne) {
               if constexpr (YDT == DT_F32) reinterpret_cast<uint32_t*>(out)[j] = val[j];
               else reinterpret_cast<uint16_t*>(out)[j] = (uint16_t)(val[j >> 1] >> (16 * (j & 1)));
             }
@@ -423,6 +483,38 @@ __global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, i
       }
     }
     __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// The whole product in one launch: blocks [0, wide_blocks) take the 256-wide
+// tiles of columns [0, nsplit), the rest the 128-wide tiles of [nsplit, N).
+// Within each part, block i runs on L2 slice i mod 8, and slice x takes the
+// x-th eighth of that part's tiles.
+template <int YDT>
+__global__ __launch_bounds__(512) void k_gemm(const uint16_t* __restrict__ xq, int64_t M, int64_t K,
+                                             const int* __restrict__ pm,
+                                             const uint32_t* __restrict__ qw,
+                                             const uint32_t* __restrict__ ctab,
+                                             const int* __restrict__ en, int64_t N,
+                                             void* __restrict__ y, int64_t ldy, int glog, int vec_ok,
+                                             int64_t nsplit, int64_t wide_tiles, int64_t wide_blocks,
+                                             int64_t narrow_tiles) {
+  // three LDS arrays, the loop unrolled by three: each stage is a known array
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kStageMax];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kStageMax];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[kStageMax];
+  const int64_t b = blockIdx.x;
+  if (b < wide_blocks) {
+    const int64_t per = (wide_tiles + kXcds - 1) / kXcds, slot = b / kXcds;
+    const int64_t t = (b % kXcds) * per + slot;
+    if (slot >= per || t >= wide_tiles) return;
+    gemm_tile<YDT, 4>(lds0, lds1, lds2, t, xq, M, K, pm, qw, ctab, en, N, 0, nsplit, y, ldy, glog, vec_ok);
+  } else {
+    const int64_t bn = b - wide_blocks;
+    const int64_t per = (narrow_tiles + kXcds - 1) / kXcds, slot = bn / kXcds;
+    const int64_t t = (bn % kXcds) * per + slot;
+    if (slot >= per || t >= narrow_tiles) return;
+    gemm_tile<YDT, 2>(lds0, lds1, lds2, t, xq, M, K, pm, qw, ctab, en, N, nsplit, N, y, ldy, glog, vec_ok);
   }
 }
 
@@ -602,8 +694,10 @@ hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
   // 16-byte output stores need a 16-byte aligned y and row pitch
   const int es = YDT == DT_F32 ? 4 : 2;
   const int vec_ok = ((uintptr_t)y % 16 == 0) && ((ldy * es) % 16 == 0);
-  hipLaunchKernelGGL((k_gemm<YDT>), dim3((unsigned)gemm_blocks(M, N)), dim3(512), 0, st, w.xq, M, K, w.pm,
-                     qw, w.ctab, w.en, N, y, ldy, glog, vec_ok);
+  const GemmPlan pl = gemm_plan(M, N);
+  hipLaunchKernelGGL((k_gemm<YDT>), dim3((unsigned)pl.blocks), dim3(512), 0, st, w.xq, M, K, w.pm,
+                     qw, w.ctab, w.en, N, y, ldy, glog, vec_ok, pl.nsplit, pl.wide_tiles, pl.wide_blocks,
+                     pl.narrow_tiles);
   return hipGetLastError();
 }
 
