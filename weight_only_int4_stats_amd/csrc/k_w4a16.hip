@@ -40,66 +40,42 @@ __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
 // fp16; then, for every group g, the fp16 constants of the packed-fma
 // dequantization, group-major so a block's columns are contiguous:
 //   ctab[g][n] = (fp16(D' 2^24) | fp16(D' 2^20) << 16, fp16(-D' z) twice).
+constexpr int kConstRows = 16;   // weight rows per block of the constants pre-pass
 __device__ __forceinline__ void gemm_consts_block(int64_t bid, const uint16_t* __restrict__ scales,
                                                   const uint8_t* __restrict__ zeros, int64_t N,
                                                   int64_t G, int* __restrict__ en,
                                                   uint32_t* __restrict__ ctab) {
-  // A block takes 64 rows; 64 groups at a time are staged in LDS (reads along
-  // the groups, all issued together).  Thread r < 64 takes row r's maximum
-  // from LDS; the constants are written with the rows fastest, so that every
-  // group's 64 entries form one 512-byte run.  With G <= 64 the one staged
-  // chunk serves both passes.
-  __shared__ float step_s[64][65];
-  __shared__ uint8_t zero_s[64][65];
-  __shared__ int e_s[64];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t n0 = bid * 64;
-  const int rows = (int)(N - n0 < 64 ? N - n0 : 64);
-  auto stage = [&](int64_t g0, int gc) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int i = wv + 4 * u;
-      if (i < rows && lane < gc) {
-        step_s[i][lane] = f16_to_f32(scales[(n0 + i) * G + g0 + lane]);
-        zero_s[i][lane] = zeros[(n0 + i) * G + g0 + lane];
-      }
-    }
-  };
+  // 16 rows per block of 256 threads, 16 consecutive lanes per row: lane p
+  // of a row takes its groups [p G / 16, (p + 1) G / 16), first for the row's
+  // largest step (combined over the 16 lanes with shuffles), then for the
+  // constants.  Every block is one short round of loads and stores, so the
+  // pass keeps up with the activation rows beside it.
+  const int tid = threadIdx.x;
+  const int rl = tid >> 4, p = tid & 15;
+  const int64_t n = bid * kConstRows + rl;
+  const bool ok = n < N;
+  const int64_t g0 = p * G / 16, g1 = (p + 1) * G / 16;
+  const uint16_t* sr = scales + (ok ? n : 0) * G;
+  const uint8_t* zr = zeros + (ok ? n : 0) * G;
   float mx = 0.0f;
-  for (int64_t g0 = 0; g0 < G; g0 += 64) {
-    const int gc = (int)(G - g0 < 64 ? G - g0 : 64);
-    __syncthreads();
-    stage(g0, gc);
-    __syncthreads();
-    if (tid < rows)
-      for (int gl = 0; gl < gc; ++gl) mx = fmaxf(mx, step_s[tid][gl]);
+  if (ok)
+    for (int64_t g = g0; g < g1; ++g) mx = fmaxf(mx, f16_to_f32(sr[g]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  int e = 0;
+  if (mx > 0.0f) {
+    int ex;
+    frexpf(mx, &ex);          // mx < 2^ex
+    e = -9 - ex;              // mx 2^e in [2^-10, 2^-9)
   }
-  if (tid < rows) {
-    int e = 0;
-    if (mx > 0.0f) {
-      int ex;
-      frexpf(mx, &ex);        // mx < 2^ex
-      e = -9 - ex;            // mx 2^e in [2^-10, 2^-9)
-    }
-    en[n0 + tid] = e;
-    e_s[tid] = e;
-  }
-  for (int64_t g0 = 0; g0 < G; g0 += 64) {
-    const int gc = (int)(G - g0 < 64 ? G - g0 : 64);
-    if (G > 64) {
-      __syncthreads();
-      stage(g0, gc);
-    }
-    __syncthreads();
-    if (lane < rows)
-      for (int gl = wv; gl < gc; gl += 4) {
-        const float D = ldexpf(step_s[lane][gl], e_s[lane]);   // exact: power-of-two scaling
-        const uint32_t h24 = f32_to_f16_bits(D * 16777216.0f);
-        const uint32_t h20 = f32_to_f16_bits(D * 1048576.0f);
-        const uint32_t hz = f32_to_f16_bits(-(D * (float)zero_s[lane][gl]));
-        *reinterpret_cast<uint2*>(ctab + ((g0 + gl) * N + n0 + lane) * 2) =
-            make_uint2(h24 | (h20 << 16), hz | (hz << 16));
-      }
+  if (!ok) return;
+  if (p == 0) en[n] = e;
+  for (int64_t g = g0; g < g1; ++g) {
+    const float D = ldexpf(f16_to_f32(sr[g]), e);   // exact: power-of-two scaling
+    const uint32_t h24 = f32_to_f16_bits(D * 16777216.0f);
+    const uint32_t h20 = f32_to_f16_bits(D * 1048576.0f);
+    const uint32_t hz = f32_to_f16_bits(-(D * (float)zr[g]));
+    *reinterpret_cast<uint2*>(ctab + (g * N + n) * 2) = make_uint2(h24 | (h20 << 16), hz | (hz << 16));
   }
 }
 
@@ -152,8 +128,9 @@ __device__ __forceinline__ u32x4 dequant_word_f16(uint32_t w, uint32_t cx, uint3
 // ordered for the chip's eight L2 slices: block i runs on slice i mod 8, and
 // slice x takes the x-th eighth of the tiles in a grouped order (4 m-tiles,
 // m fastest, then n), so its ~32 concurrent blocks cover about 4 x 8 tiles.
-// The GEMM's two pre-passes in one launch (they are independent): blocks
-// 0 .. M - 1 convert activation rows, the rest build the constants.
+// The GEMM's two pre-passes in one launch (they are independent): the first
+// ceil(N / 16) blocks build the constants, the other M convert one activation
+// row each.
 // KEEP: activation chunks per thread held in registers (16: rows up to 32768).
 template <int DT, bool HAS_R, int KEEP>
 __global__ __launch_bounds__(256) void k_gemm_prep(const uint16_t* __restrict__ x, int64_t M, int64_t K,
@@ -162,8 +139,9 @@ __global__ __launch_bounds__(256) void k_gemm_prep(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros, int64_t N, int64_t G,
                                                    int* __restrict__ en, uint32_t* __restrict__ ctab) {
-  if ((int64_t)blockIdx.x < M) rows_f16_block<DT, HAS_R, true, KEEP>(blockIdx.x, x, K, ldx, r, xq, pm);
-  else gemm_consts_block((int64_t)blockIdx.x - M, scales, zeros, N, G, en, ctab);
+  const int64_t nc = (N + kConstRows - 1) / kConstRows;
+  if ((int64_t)blockIdx.x < nc) gemm_consts_block(blockIdx.x, scales, zeros, N, G, en, ctab);
+  else rows_f16_block<DT, HAS_R, true, KEEP>((int64_t)blockIdx.x - nc, x, K, ldx, r, xq, pm);
 }
 
 // Position of an A row's 16-byte chunks in LDS: chunk c of row r at
@@ -684,7 +662,7 @@ hipError_t gemm_dispatch(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
                          const uint16_t* scales, const uint8_t* zeros, int64_t N, int glog,
                          const float* r, void* y, int64_t ldy, void* ws, hipStream_t st) {
   const GemmWs w = gemm_ws(ws, M, N, K, 1 << glog);
-  const dim3 pgrid((unsigned)(M + (N + 63) / 64));
+  const dim3 pgrid((unsigned)(M + (N + kConstRows - 1) / kConstRows));
   if (K > 256 * 8 * kRowsKeep)
     hipLaunchKernelGGL((k_gemm_prep<DT, HAS_R, 2 * kRowsKeep>), pgrid, dim3(256), 0, st, x, M, K, ldx, r,
                        w.xq, w.pm, scales, zeros, N, K >> glog, w.en, w.ctab);
