@@ -19,15 +19,16 @@ constexpr int kRowsKeep = 8;   // 8-element chunks per thread kept in registers 
 // row's max so the row sits in fp16's normal range.  One block per row.  With
 // PERMUTE each 8-element chunk is stored as (k0,k4,k2,k6,k1,k5,k3,k7), the
 // order in which the packed-nibble unpack yields weight pairs.  A row of up to
-// 256 KEEP chunks stays in registers, as loaded, between its max and its
-// conversion (read once from memory); a longer one is read twice.
+// 256 KEEP chunks stays in registers between its max and its conversion (read
+// once); a longer one is read twice.
 template <int DT, bool HAS_R, bool PERMUTE, int KEEP = kRowsKeep>
 __device__ __forceinline__ void rows_f16_block(int64_t row, const uint16_t* __restrict__ src, int64_t K,
                                                int64_t ld, const float* __restrict__ r,
                                                uint16_t* __restrict__ dst, int* __restrict__ pexp) {
   const uint16_t* s = src + row * ld;
   const int64_t nch = K >> 3;
-  auto conv8 = [&](int64_t c, const u32x4& raw, float v[8]) {
+  auto load8 = [&](int64_t c, float v[8]) {
+    const u32x4 raw = ldg128(s + c * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v[2 * j] = lo_f32<DT>(raw[j]);
@@ -43,7 +44,6 @@ __device__ __forceinline__ void rows_f16_block(int64_t row, const uint16_t* __re
       }
     }
   };
-  auto load8 = [&](int64_t c, float v[8]) { conv8(c, ldg128(s + c * 8), v); };
   uint16_t* d = dst + row * K;
   auto store8 = [&](int64_t c, const float v[8], int p) {
     uint32_t h[8];
@@ -73,33 +73,22 @@ __device__ __forceinline__ void rows_f16_block(int64_t row, const uint16_t* __re
   };
   float amax = 0.0f;
   if (nch <= 256 * KEEP) {
-    // the row stays in registers, as loaded, between the max and the
-    // conversion (converted, and multiplied by r, once for each)
-    u32x4 raw[KEEP];
-#pragma unroll
-    for (int i = 0; i < KEEP; ++i) {
-      const int64_t c = threadIdx.x + 256 * i;
-      if (c < nch) raw[i] = ldg128(s + c * 8);
-    }
+    // the row stays in registers between the max and the conversion
+    float v[KEEP][8];
 #pragma unroll
     for (int i = 0; i < KEEP; ++i) {
       const int64_t c = threadIdx.x + 256 * i;
       if (c < nch) {
-        float v[8];
-        conv8(c, raw[i], v);
+        load8(c, v[i]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
       }
     }
     const int p = row_exp(amax);
 #pragma unroll
     for (int i = 0; i < KEEP; ++i) {
       const int64_t c = threadIdx.x + 256 * i;
-      if (c < nch) {
-        float v[8];
-        conv8(c, raw[i], v);
-        store8(c, v, p);
-      }
+      if (c < nch) store8(c, v[i], p);
     }
     return;
   }
