@@ -192,13 +192,15 @@ def test_binding_argument_counts_match_the_header():
 
 def _direct_search_ws(N, K, T, n_alpha):
     """Bytes of the direct-form search workspace for bf16 tokens (the larger
-    layout): candidate scales and reciprocals, row exponents, one error row
-    set, losses, tile partials, the tokens rounded to fp16 and their
-    exponents, each piece rounded up to 256 bytes."""
+    layout): candidate scales and reciprocals, then for the candidates scored
+    per launch (as many as fit 64 MiB of error rows, at least one) their row
+    exponents and error rows, the losses, their tile partials, the tokens
+    rounded to fp16 and their exponents, each piece rounded up to 256 bytes."""
     up = lambda b: (b + 255) // 256 * 256  # noqa: E731
     tiles = -(-N // 256) * -(-T // 256)
-    return (2 * up(n_alpha * K * 4) + up(N * 4) + up(N * K * 2) + up(n_alpha * 8) + up(tiles * 8) +
-            up(T * K * 2) + up(T * 4))
+    nc = max(1, min(n_alpha, (64 << 20) // (N * K * 2)))
+    return (2 * up(n_alpha * K * 4) + up(nc * N * 4) + up(nc * N * K * 2) + up(n_alpha * 8) +
+            up(nc * tiles * 8) + up(T * K * 2) + up(T * 4))
 
 
 def test_gram_form_token_limit():

@@ -394,6 +394,60 @@ def test_determinism():
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
+def test_pipeline_graph_replay():
+    """The whole path (statistic, search, quantize + pack, batch-1 and 64-token
+    products on the 512 x 512 linear) captured in one HIP graph with
+    preallocated outputs and workspaces: every replay, with eager work and
+    synchronisations between them, gives bit-identical outputs to the eager
+    run (no call allocates, synchronises or records a memset)."""
+    w = WL.workload(1)
+    W, X = gpu(WL.weight(w)), gpu(WL.calibration(w))
+    al = gpu(torch.from_numpy(WL.alpha_grid(20)))
+    xx = gpu(WL.prefill_input(w, 64))
+    N, K, T = w.N, w.K, w.T
+    dev = W.device
+    ws_st = torch.empty(awq.awq_workspace_bytes(awq.AWQ_OP_ACT_STATS, 0, N, K, T), dtype=torch.uint8, device=dev)
+    ws_se = torch.empty(awq.awq_workspace_bytes(awq.AWQ_OP_SEARCH, 0, N, K, T, 20), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(max(1, awq.awq_workspace_bytes(awq.AWQ_OP_GEMM, 64, N, K)), dtype=torch.uint8, device=dev)
+    m = torch.empty(K, dtype=torch.float32, device=dev)
+    s = torch.empty(K, dtype=torch.float32, device=dev)
+    inv = torch.empty(K, dtype=torch.float32, device=dev)
+    L = torch.empty(20, dtype=torch.float64, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    q = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    sc = torch.empty((N, K // 128), dtype=torch.float16, device=dev)
+    z = torch.empty((N, K // 128), dtype=torch.uint8, device=dev)
+    y = torch.empty((64, N), dtype=torch.float16, device=dev)
+    y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+
+    def run():
+        awq.awq_act_stats(X, m, ws=ws_st)
+        awq.awq_search_scales(W, X, m, al, s_out=s, inv_s_out=inv, loss_out=L, best_idx_out=best, ws=ws_se)
+        awq.awq_quantize_pack(W, s, qweight=q, scales=sc, zeros=z)
+        awq.awq_w4a16_gemm(xx, q, sc, z, inv, y=y, ws=ws_g)
+        awq.awq_w4a16_gemm(xx[:1], q, sc, z, inv, y=y1)
+
+    outs = (m, s, inv, L, best, q, sc, z, y, y1)
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    st = torch.cuda.Stream()
+    run()                                     # warm-up on the capture stream's device
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()                         # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}"
+
+
 # ---------------------------------------------------------------------------
 # folding 1/s into the producer of x ("AWQ Math", "The equivalent transform:
 # scale up W, scale down x") and the shared-input search of q, k and v

@@ -23,6 +23,9 @@
 //                   fp16 with their own power-of-two scale (exact unless a
 //                   value falls 2^24 below its token's largest).
 //   3. k_sum_partials  fixed-order double sum of the tile partials -> L_i.
+// Each step runs for a batch of candidates per launch (blockIdx.y, or the
+// block of k_sum_partials, is the candidate's slot in the workspace): small
+// layers score all candidates in three launches.
 // Finally k_select picks the lowest index among the minimal finite losses and
 // writes s, 1/s, the losses and the index.  Every sum has a fixed order, so
 // the result is bit-reproducible.
@@ -30,6 +33,8 @@
 #include "awq_internal.h"
 #include "k_contract.h"
 #include "k_rows_f16.h"
+
+#include <algorithm>
 
 namespace awqk {
 
@@ -110,6 +115,12 @@ __global__ __launch_bounds__(256) void k_err_gen(const uint16_t* __restrict__ W,
                                                  const float* __restrict__ is, QSpec q,
                                                  const uint8_t* __restrict__ kept,
                                                  uint16_t* __restrict__ E, int* __restrict__ pexp) {
+  // candidate slot blockIdx.y of a batched launch: its scales and error rows
+  const int64_t cy = blockIdx.y;
+  s += cy * K;
+  is += cy * K;
+  E += cy * N * K;
+  pexp += cy * N;
   const int64_t n = blockIdx.x;
   const uint16_t* wrow = W + n * K;
   const int64_t wpr = K >> 3;
@@ -217,8 +228,11 @@ __global__ __launch_bounds__(256) void k_err_contract(const uint16_t* __restrict
   __shared__ __attribute__((aligned(16))) uint8_t lds3[kCStage];
   __shared__ double wsum[kCWaves];
 
-  // ---- tile of this block
+  // ---- tile of this block (candidate slot blockIdx.y of a batched launch)
   const int64_t gx = (N + kCT - 1) / kCT, gy = (T + kCT - 1) / kCT, tiles = gx * gy;
+  E += (int64_t)blockIdx.y * N * K;
+  pexp += (int64_t)blockIdx.y * N;
+  partial += (int64_t)blockIdx.y * tiles;
   const int64_t per = (tiles + kCXcds - 1) / kCXcds;
   const int64_t slot = blockIdx.x / kCXcds;
   const int64_t o = (int64_t)(blockIdx.x % kCXcds) * per + slot;
@@ -316,6 +330,9 @@ __global__ __launch_bounds__(256) void k_err_contract(const uint16_t* __restrict
 // Fixed-order sum of n doubles by one block of 256 threads -> out[0] = sum / denom.
 __global__ __launch_bounds__(256) void k_sum_partials(const double* __restrict__ part, int64_t n,
                                                       double denom, double* __restrict__ out) {
+  // block b: the b-th of a batch of partial sets, n apart
+  part += (int64_t)blockIdx.x * n;
+  out += blockIdx.x;
   __shared__ double red[256];
   double s = 0.0;
   for (int64_t i = threadIdx.x; i < n; i += 256) s += part[i];
@@ -369,6 +386,11 @@ namespace {
 // compute units better.
 constexpr int kGramBatch = 4;
 
+// Direct form: candidates per launch, as many as fit their error rows in this
+// many bytes of workspace (small layers, where each candidate alone would be a
+// launch of a few blocks: the 512 x 512 layer scores all 20 in one launch).
+constexpr int64_t kDirectBatchBytes = int64_t(64) << 20;
+
 // The Gram form (G = X^T X once, then per candidate a contraction with G
 // carried as two fp16 parts, over the blocks on and below the diagonal only)
 // replaces the T-long contraction when it costs well under half as many
@@ -415,7 +437,8 @@ SearchWs carve(void* ws, int dt, int64_t N, int64_t K, int64_t T, int n_alpha) {
     return p;
   };
   w.gram = search_uses_gram(N, K, T, n_alpha);
-  w.nc = w.gram ? (n_alpha < kGramBatch ? n_alpha : kGramBatch) : 1;
+  const int direct_nc = (int)std::max<int64_t>(1, std::min<int64_t>(n_alpha, kDirectBatchBytes / (N * K * 2)));
+  w.nc = w.gram ? (n_alpha < kGramBatch ? n_alpha : kGramBatch) : direct_nc;
   w.S = (float*)take((size_t)n_alpha * K * 4);
   w.IS = (float*)take((size_t)n_alpha * K * 4);
   w.pexp = (int*)take((size_t)w.nc * N * 4);
@@ -432,7 +455,7 @@ SearchWs carve(void* ws, int dt, int64_t N, int64_t K, int64_t T, int n_alpha) {
   } else {
     const int64_t gx = (N + awqk::kCT - 1) / awqk::kCT;
     const int64_t gy = (T + awqk::kCT - 1) / awqk::kCT;
-    w.partial = (double*)take((size_t)gx * gy * 8);
+    w.partial = (double*)take((size_t)w.nc * gx * gy * 8);
     if (dt == awqk::DT_BF16) {
       w.Xh = (uint16_t*)take((size_t)T * K * 2);
       w.px = (int*)take((size_t)T * 4);
@@ -457,19 +480,21 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
   hipLaunchKernelGGL(k_cand_scales, dim3((unsigned)((nS + 255) / 256)), dim3(256), 0, st, mean_abs,
                      alphas, n_alpha, K, sw.S, sw.IS);
   const double tn = (double)T * (double)N;
-  // error rows of candidate i into slot c of the workspace
+  // error rows of candidates cand .. cand + nb - 1 into slots 0 .. nb - 1 of
+  // the workspace, one launch (blockIdx.y = slot)
   const QSpec q = qspec(qv.bits, qv.sym);
-  auto err_gen = [&](int cand, int c) {
+  auto err_gen = [&](int cand, int nb) {
     const float* s_i = sw.S + (int64_t)cand * K;
     const float* is_i = sw.IS + (int64_t)cand * K;
-    uint16_t* E = sw.E + (int64_t)c * N * K;
-    int* pe = sw.pexp + (int64_t)c * N;
+    uint16_t* E = sw.E;
+    int* pe = sw.pexp;
     const uint16_t* W = (const uint16_t*)w;
+    const dim3 grid((unsigned)N, (unsigned)nb);
 #define AWQ_EG3(GL, GR, KP)                                                                         \
   if (dt == DT_F16)                                                                                 \
-    hipLaunchKernelGGL((k_err_gen<DT_F16, GL, GR, KP>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, is_i, q, kept, E, pe); \
+    hipLaunchKernelGGL((k_err_gen<DT_F16, GL, GR, KP>), grid, dim3(256), 0, st, W, N, K, s_i, is_i, q, kept, E, pe); \
   else                                                                                              \
-    hipLaunchKernelGGL((k_err_gen<DT_BF16, GL, GR, KP>), dim3((unsigned)N), dim3(256), 0, st, W, N, K, s_i, is_i, q, kept, E, pe)
+    hipLaunchKernelGGL((k_err_gen<DT_BF16, GL, GR, KP>), grid, dim3(256), 0, st, W, N, K, s_i, is_i, q, kept, E, pe)
 #define AWQ_EG2(GL, GR) \
   if (kept) { AWQ_EG3(GL, GR, true); } else { AWQ_EG3(GL, GR, false); }
 #define AWQ_EG(GL)                                                                                  \
@@ -490,12 +515,10 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
     const int64_t nt = gram_loss_tiles(N, K);
     for (int i0 = 0; i0 < n_alpha; i0 += sw.nc) {
       const int nc = n_alpha - i0 < sw.nc ? n_alpha - i0 : sw.nc;
-      for (int c = 0; c < nc; ++c) err_gen(i0 + c, c);
+      err_gen(i0, nc);
       const hipError_t el = launch_gram_loss(sw.E, N, K, sw.pexp, sw.P, sw.sk, sw.partial, nc, st);
       if (el != hipSuccess) return el;
-      for (int c = 0; c < nc; ++c)
-        hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial + (int64_t)c * nt, nt, tn,
-                           sw.losses + i0 + c);
+      hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)nc), dim3(256), 0, st, sw.partial, nt, tn, sw.losses + i0);
     }
   } else {
     const uint16_t* Xop = (const uint16_t*)x;
@@ -510,12 +533,13 @@ hipError_t launch_search(const void* w, int dt, int64_t N, int64_t K, const void
     }
     const int64_t gx = (N + kCT - 1) / kCT;
     const int64_t gy = (T + kCT - 1) / kCT;
-    for (int i = 0; i < n_alpha; ++i) {
-      err_gen(i, 0);
-      hipLaunchKernelGGL(k_err_contract, dim3((unsigned)contract_blocks(T, N)), dim3(256), 0, st, Xop, T,
-                         ldop, px, sw.E, N, K, sw.pexp, sw.partial);
-      hipLaunchKernelGGL(k_sum_partials, dim3(1), dim3(256), 0, st, sw.partial, gx * gy, tn,
-                         sw.losses + i);
+    for (int i0 = 0; i0 < n_alpha; i0 += sw.nc) {
+      const int nc = n_alpha - i0 < sw.nc ? n_alpha - i0 : sw.nc;
+      err_gen(i0, nc);
+      hipLaunchKernelGGL(k_err_contract, dim3((unsigned)contract_blocks(T, N), (unsigned)nc), dim3(256), 0, st,
+                         Xop, T, ldop, px, sw.E, N, K, sw.pexp, sw.partial);
+      hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)nc), dim3(256), 0, st, sw.partial, gx * gy, tn,
+                         sw.losses + i0);
     }
   }
   hipLaunchKernelGGL(k_select, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, sw.losses,
