@@ -12,10 +12,12 @@
 //         precondition (column sums below 2^29), so the double sum is exact and
 //         equal to the integer one; bf16's shift-heavy integer path was the
 //         slower one (79 against 35 us on 2048 x 28672).
-// Across the block the sums are 64-bit integers, and across blocks they are
-// added with 64-bit integer atomics (exact and order-free).  The finalisation
-// divides once in double and rounds once to float, so the result does not
-// depend on the grid.
+// Across the block the sums are 64-bit integers; each row range writes its
+// column sums to a slot of its own in the workspace (no atomics, nothing to
+// clear first), and the finalisation adds a column's slots in 64-bit integers
+// (exact and order-free), divides once in double and rounds once to float,
+// so the result does not depend on the grid.  The calibration rows are read
+// with non-temporal loads: each is read once.
 //
 // Layout: X is [T][ldx] row-major.  A thread owns 8 consecutive columns (one
 // 128-bit load per row); a wave covers 512 columns of a row, the four waves of
@@ -27,14 +29,12 @@
 
 namespace awqk {
 
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kStatsThreads = 256;
 constexpr int kStatsCols = 512;      // columns per block (64 lanes x 8)
 constexpr int kStatsUnroll = 16;     // rows per wave per loop trip (loads in flight)
 
-__global__ void k_fill_u64(unsigned long long* p, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0ull;
-}
 
 // floor(|x| 2^24) of one 16-bit value, as an integer.  fp16: a subnormal is
 // m 2^-24 -> m; a normal (1024 + m) 2^(e - 25) -> (1024 + m) 2^(e - 1).  bf16:
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __r
                                                              int64_t T, int64_t K, int64_t ldx,
                                                              int64_t rows_per_block, int64_t slabs,
                                                              int64_t chunks,
-                                                             unsigned long long* __restrict__ acc) {
+                                                             unsigned long long* __restrict__ part) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   // Block i runs on L2 slice i mod 8; slice x takes chunks x, x + 8, ... with
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __r
     for (; r + 4 * (kStatsUnroll - 1) < r1; r += 4 * kStatsUnroll) {
       u32x4 v[kStatsUnroll];
 #pragma unroll
-      for (int u = 0; u < kStatsUnroll; ++u) v[u] = ldg128(base + (r + 4 * u) * ldx);
+      for (int u = 0; u < kStatsUnroll; ++u) v[u] = ldg128_stream(base + (r + 4 * u) * ldx);
 #pragma unroll
       for (int u = 0; u < kStatsUnroll; ++u) {
         accum_word<DT>(v[u][0], s[0], s[1]);
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __r
       }
     }
     for (; r < r1; r += 4) {
-      u32x4 v = ldg128(base + r * ldx);
+      u32x4 v = ldg128_stream(base + r * ldx);
       accum_word<DT>(v[0], s[0], s[1]);
       accum_word<DT>(v[1], s[2], s[3]);
       accum_word<DT>(v[2], s[4], s[5]);
@@ -122,20 +122,44 @@ __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __r
   for (int j = 0; j < 8; ++j) red[wv][j][lane] = (uint64_t)s[j];   // an integer below 2^53
   __syncthreads();
   if (wv == 0 && col < K) {
+    // this row range's column sums, one slot per range (no atomics, nothing to clear)
+    u64x2 o[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint64_t t = red[0][j][lane] + red[1][j][lane] + red[2][j][lane] + red[3][j][lane];
-      if (t != 0) atomicAdd(&acc[col + j], (unsigned long long)t);
-    }
+    for (int j = 0; j < 8; ++j)
+      o[j >> 1][j & 1] = red[0][j][lane] + red[1][j][lane] + red[2][j][lane] + red[3][j][lane];
+    u64x2* dst = reinterpret_cast<u64x2*>(part + chunk * K + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = o[i];
   }
 }
 
-__global__ void k_act_finalize(const unsigned long long* __restrict__ acc, int64_t K, int64_t T,
-                               float* __restrict__ mean_abs) {
-  int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Column j: the row ranges' integer sums added (exact, any order), then one
+// double division and one float rounding.  A block takes 64 columns; its four
+// waves take every fourth row range, eight loads in flight per lane.
+__global__ __launch_bounds__(256) void k_act_finalize(const unsigned long long* __restrict__ part,
+                                                      int64_t chunks, int64_t K, int64_t T,
+                                                      float* __restrict__ mean_abs) {
+  __shared__ unsigned long long red[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+  unsigned long long acc = 0;
   if (j < K) {
-    const double sum = (double)acc[j] * 0x1p-24;    // exact: acc < 2^53
-    mean_abs[j] = (float)(sum / (double)T);        // one double rounding, one float rounding
+    int64_t c = wv;
+    for (; c + 4 * 7 < chunks; c += 4 * 8) {
+      unsigned long long v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(c + 4 * u) * K + j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; c < chunks; c += 4) acc += part[c * K + j];
+  }
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0 && j < K) {
+    acc = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+    const double sum = (double)acc * 0x1p-24;       // exact: acc < 2^53
+    mean_abs[j] = (float)(sum / (double)T);         // one double rounding, one float rounding
   }
 }
 
@@ -143,16 +167,19 @@ __global__ void k_act_finalize(const unsigned long long* __restrict__ acc, int64
 
 namespace awq {
 
-size_t act_stats_ws_bytes(int64_t K) { return align_up((size_t)K * 8, 256); }
+// at most ceil(1024 / slabs) row ranges (stats_chunks), each a uint64 per column
+size_t act_stats_ws_bytes(int64_t K) {
+  const int64_t slabs = (K + awqk::kStatsCols - 1) / awqk::kStatsCols;
+  return align_up((size_t)((1024 + slabs - 1) / slabs) * (size_t)K * 8, 256);
+}
 
 hipError_t launch_act_stats(const void* x, int dt, int64_t T, int64_t K, int64_t ldx,
                             float* mean_abs, void* ws, hipStream_t st) {
   using namespace awqk;
-  unsigned long long* acc = reinterpret_cast<unsigned long long*>(ws);
-  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, acc, K);
+  unsigned long long* part = reinterpret_cast<unsigned long long*>(ws);
   const int64_t slabs = (K + kStatsCols - 1) / kStatsCols;
   // about 1024 blocks (four per compute unit), each row range a multiple of
-  // 4 rows x unroll: longer row ranges mean fewer 64-bit atomics per column
+  // 4 rows x unroll: longer row ranges mean fewer partial sums per column
   // (4096 blocks measured 125 against 108 us on 65536 x 4096)
   int64_t chunks = (1024 + slabs - 1) / slabs;
   const int64_t quantum = 4 * kStatsUnroll;
@@ -167,12 +194,12 @@ hipError_t launch_act_stats(const void* x, int dt, int64_t T, int64_t K, int64_t
   const dim3 grid((unsigned)(slabs * ((chunks + 7) / 8) * 8));
   if (dt == DT_F16)
     hipLaunchKernelGGL(k_act_accum<DT_F16>, grid, dim3(kStatsThreads), 0, st,
-                       (const uint16_t*)x, T, K, ldx, rpb, slabs, chunks, acc);
+                       (const uint16_t*)x, T, K, ldx, rpb, slabs, chunks, part);
   else
     hipLaunchKernelGGL(k_act_accum<DT_BF16>, grid, dim3(kStatsThreads), 0, st,
-                       (const uint16_t*)x, T, K, ldx, rpb, slabs, chunks, acc);
-  hipLaunchKernelGGL(k_act_finalize, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, acc, K,
-                     T, mean_abs);
+                       (const uint16_t*)x, T, K, ldx, rpb, slabs, chunks, part);
+  hipLaunchKernelGGL(k_act_finalize, dim3((unsigned)((K + 63) / 64)), dim3(256), 0, st, part, chunks, K, T,
+                     mean_abs);
   return hipGetLastError();
 }
 
