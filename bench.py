@@ -455,7 +455,7 @@ def main() -> int:
     gblk = (KA + 255) // 256
     direct_flop = 2.0 * wa.T * NA * KA * 20
     gram_flop = 2.0 * Tp * KA * KA + 20 * 2.0 * NA * 256 * 256 * gblk * (gblk + 1)
-    search_gram = KA <= 16384 and gram_flop < 0.5 * direct_flop
+    search_gram = KA <= 32768 and gram_flop < 0.5 * direct_flop
     search_flop = gram_flop if search_gram else direct_flop
     loss_h = [float(v) for v in loss.cpu()]
     best_h = int(best.cpu()[0])

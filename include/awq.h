@@ -170,7 +170,7 @@ awq_status awq_act_stats(const void* x, awq_dtype xdt, int64_t T, int64_t K, int
  * parts (22 significant bits); with G symmetric, a candidate contracts only
  * over the 256 x 256 blocks of G on and below the diagonal (off-diagonal
  * blocks counted twice), 2 N 256^2 g (g + 1) operations for g = ceil(K / 256),
- * about 2 N K^2.  The Gram form is taken when K <= 16384, Tp < 2^23 (its
+ * about 2 N K^2.  The Gram form is taken when K <= 32768, Tp < 2^23 (its
  * token rows are addressed with 32-bit offsets) and its total is under half
  * of the direct one's.
  * Linears that read the same input may be searched together by passing their

@@ -291,3 +291,64 @@ def test_full_decoder_layer_7b():
             err = rel_max_err(f32(y)[:, rows], ref, torch.float16)
             print(f"7B layer {lin} {w.K}->{w.N} M={M}: alpha index {b}, rel max err {err:.3e}")
             assert err <= GEMM_TOL, (lin, M)
+
+
+def _uses_gram(N, K, T, n_alpha=20):
+    """The library's rule for the loss form (awq_search_scales in include/awq.h):
+    the Gram form for K <= 32768 and Tp < 2^23 when it needs under half the
+    direct form's matrix-core operations."""
+    Tp = -(-T // 256) * 256
+    g = -(-K // 256)
+    direct = n_alpha * 2.0 * T * N * K
+    gram = 2.0 * Tp * K * K + n_alpha * 2.0 * N * 256 * 256 * g * (g + 1)
+    return K <= 32768 and Tp < 2 ** 23 and gram < 0.5 * direct
+
+
+@pytest.mark.parametrize("N,K,T", [(4096, 16896, 65536), (5376, 28672, 131072)])
+def test_gram_form_wide_input_matches_direct_form_by_row_slices(N, K, T):
+    """Past 16384 input channels (the Llama-70B down-projection reads 28672)
+    the search takes the Gram form when the calibration set is long.  Its
+    losses are compared with the direct form's, which the oracle pins in the
+    other search tests: the loss is a mean over weight rows, so the whole
+    layer's loss is the row-weighted mean of the losses of its row slices, each
+    searched alone (64 rows take the direct form).
+
+    Both forms contract the same fp16 error rows (written by the same error
+    generator); they differ only in the contraction: tokens times error rows
+    accumulated in fp32 per tile and in double across tiles (direct), against
+    G = X^T X in double carried as two fp16 parts of 22 significant bits
+    (Gram).  For these random tokens the Gram form's worst case is about 1e-5
+    relative (2^-22 times the ratio of sum |e_i| |G_ij| |e_j| to e^T G e, about
+    40 at T = 65536, K = 16896); the tolerance leaves a factor 10 above it.
+    The chosen index must agree unless the two best losses lie within twice
+    the tolerance of each other.  The second shape is the 70B down-projection's
+    input width over its 131072 calibration tokens."""
+    assert _uses_gram(N, K, T) and not _uses_gram(64, K, T)
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(K)
+    W = (torch.randn((N, K), device=dev, generator=gen, dtype=torch.float16) * 0.02)
+    X = torch.randn((T, K), device=dev, generator=gen, dtype=torch.float16)
+    cols = torch.randperm(K, device=dev, generator=gen)[: K // 100]
+    X[:, cols] *= 20.0
+    al = torch.from_numpy(WL.alpha_grid(20)).to(dev)
+    m = awq.awq_act_stats(X)
+    s, inv, L, best = awq.awq_search_scales(W, X, m, al)
+    L = L.cpu().numpy()
+    Ls = np.zeros(20)
+    rows = 64
+    for r0 in range(0, N, rows):
+        _, _, Li, _ = awq.awq_search_scales(W[r0:r0 + rows], X, m, al)
+        Ls += Li.cpu().numpy() * (rows / N)
+    torch.cuda.synchronize()
+    rel = np.abs(L - Ls) / Ls
+    tol = 1e-4
+    print(f"Gram form at K={K}: max relative difference to the direct form {rel.max():.3e}")
+    assert np.all(np.isfinite(L)) and rel.max() <= tol
+    order = np.argsort(Ls, kind="stable")
+    gap = (Ls[order[1]] - Ls[order[0]]) / Ls[order[0]]
+    if gap > 2 * tol:
+        assert int(best.cpu()[0]) == int(order[0])
+    else:
+        print(f"ill-posed seed: the two best losses are {gap:.2e} apart")
+        assert int(best.cpu()[0]) in (int(order[0]), int(order[1]))

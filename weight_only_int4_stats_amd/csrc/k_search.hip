@@ -394,12 +394,13 @@ constexpr int64_t kDirectBatchBytes = int64_t(64) << 20;
 // The Gram form (G = X^T X once, then per candidate a contraction with G
 // carried as two fp16 parts, over the blocks on and below the diagonal only)
 // replaces the T-long contraction when it costs well under half as many
-// matrix-core operations and G (K^2 doubles) is small.
+// matrix-core operations and G (K^2 doubles, 6.6 GB at K = 28672, the widest
+// Llama-70B input) stays within a few GB: K <= 32768.
 // The Gram build addresses 256 token rows of the transposed tokens with
 // 32-bit buffer offsets, so Tp stays below 2^23; longer calibration sets take
 // the direct form.
 bool search_uses_gram(int64_t N, int64_t K, int64_t T, int n_alpha) {
-  if (K > 16384 || gram_tokens_padded(T) >= (int64_t(1) << 23)) return false;
+  if (K > 32768 || gram_tokens_padded(T) >= (int64_t(1) << 23)) return false;
   const double Tp = (double)gram_tokens_padded(T);
   const double g = (double)((K + awqk::kCT - 1) / awqk::kCT);
   const double direct = (double)n_alpha * 2.0 * (double)T * (double)N * (double)K;
