@@ -246,6 +246,30 @@ def test_gemm_tile_widths(M, N, K, dtype, ydt, with_r, group):
     assert err <= GEMM_TOL
 
 
+@pytest.mark.parametrize("M,N,K,ydt", [
+    (100, 300, 1024, F16),          # half-width tiles only
+    (130, 700, 512, torch.float32),
+    (2048, 8092, 256, BF16),        # 256-wide tiles, ragged last tile
+])
+def test_gemm_unaligned_output(M, N, K, ydt):
+    """The tiled GEMM into an output whose start is not 16-byte aligned (one
+    element into a wider buffer): every element is stored on its own, the
+    neighbours stay untouched; sampled channels against the oracle."""
+    words, step, z = _random_packed_g(N, K, M + N + K, 128)
+    x = _act(M, K, BF16, M + 7)
+    big = torch.full((M, N + 9), 5.0, dtype=ydt, device="cuda")
+    y = big[:, 1:N + 1]
+    awq.awq_w4a16_gemm(gpu(x), gpu(torch.from_numpy(words)), gpu(torch.from_numpy(step)),
+                       gpu(torch.from_numpy(z)), y=y)
+    torch.cuda.synchronize()
+    g = np.random.Generator(np.random.PCG64(N))
+    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 200)), np.arange(N - 20, N),
+                                     g.integers(0, N, 50)]))
+    ref = O.w4a16_matmul_rows(f32(x), words, step, z, rows, None, 128)
+    assert rel_max_err(f32(y.cpu())[:, rows], ref, ydt) <= GEMM_TOL
+    assert torch.all(big[:, 0] == 5.0).item() and torch.all(big[:, N + 1:] == 5.0).item()
+
+
 def test_product_special_cases():
     """q == z gives 0; a one-hot x picks the dequantized column.  The GEMV
     accumulates exact int4 x activation products, so the one-hot column is
