@@ -19,7 +19,9 @@ One step = one pass of the whole hot path over every single-GPU workload:
       8192->1024): one batch-1 decode pass over its 35.83 GB of packed weights
       (q|k|v and gate|up, which read one input each, as one product each: 320
       launches), with 1/s folded into the producers of x (the deployed form)
-      and, separately, applied inside the products.
+      and, separately, applied inside the products; beside it, the same 320
+      launches as plain streaming reads of the packed codes (the pass's
+      read ceiling on this chip).
 The products run from captured HIP graphs.  The c5 stack's layer 0 is
 quantized by the full path (statistics, shared-input searches over 131072
 calibration tokens, quantize + pack) once, timed apart from the steps; layers
@@ -365,6 +367,40 @@ def main() -> int:
     for lin in c3:
         for M in C3_MS:
             capture(f"c3_{lin}_m{M}", lambda lin=lin, M=M: decode_c3(lin, M))
+    # The decode pass's ceiling: the same 320 launches as plain streaming reads
+    # of each product's packed codes, with each product kind's launch shape the
+    # best of a short untimed sweep over all 80 layers.
+    c5_rd = {}
+    if c5 is not None:
+        c5_xor = torch.empty(4096, dtype=torch.int32, device=dev)
+        for i in range(len(c5["layers"][0])):
+            pick = None
+            for blocks in (256, 512, 1024, 2048):
+                for unroll in (2, 4, 8):
+                    def kind_pass(i=i, blocks=blocks, unroll=unroll):
+                        for L in c5["layers"]:
+                            awq.awq_read_stream(L[i]["q"], blocks, unroll, block_xor=c5_xor)
+                    kind_pass()
+                    torch.cuda.synchronize()
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=stream):
+                        kind_pass()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    g.replay()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    t = e0.elapsed_time(e1)
+                    if pick is None or t < pick[0]:
+                        pick = (t, blocks, unroll)
+                    del g
+            c5_rd[i] = pick[1:]
+
+        def read_c5():
+            for L in c5["layers"]:
+                for i, part in enumerate(L):
+                    awq.awq_read_stream(part["q"], *c5_rd[i], block_xor=c5_xor)
+        capture("c5_read_ceiling", read_c5)
     if c5 is not None:
         capture("c5_decode_folded", lambda: decode_c5(True))
         capture("c5_decode_inv_s", lambda: decode_c5(False))
@@ -376,7 +412,7 @@ def main() -> int:
         phases.append("c1_pipeline")
     phases += [f"c3_{lin}_m{M}" for lin in c3 for M in C3_MS]
     if c5 is not None:
-        phases += ["c5_decode_folded", "c5_decode_inv_s"]
+        phases += ["c5_decode_folded", "c5_decode_inv_s", "c5_read_ceiling"]
 
     def step(ev):
         k = 0
@@ -413,6 +449,8 @@ def main() -> int:
             graphs["c5_decode_folded"].replay()
             mark()
             graphs["c5_decode_inv_s"].replay()
+            mark()
+            graphs["c5_read_ceiling"].replay()
             mark()
 
     def new_events():
@@ -523,6 +561,17 @@ def main() -> int:
             ms = avg[f"c5_decode_{form}"]
             out5[f"decode_{form}"] = {"ms": ms, "GB/s": c5["bytes"] / (ms * 1e-3) / 1e9,
                                       "frac_hbm": c5["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        codes = sum(part["q"].numel() * 4 for L in c5["layers"] for part in L)
+        ms = avg["c5_read_ceiling"]
+        rd_gbs = codes / (ms * 1e-3) / 1e9
+        out5["read_ceiling"] = {
+            "ms": ms, "GB/s": rd_gbs, "frac_hbm": rd_gbs / HBM_PEAK_GBS, "bytes": codes,
+            "launch_shapes": {k: list(v) for k, v in zip(("qkv", "o", "gateup", "down"), c5_rd.values())},
+            "what": "the same 320 launches as plain streaming reads (awq_read_stream) of each product's "
+                    "packed codes, each product kind's launch shape (blocks, unroll) the best of a short "
+                    "sweep: the rate one launch per product reaches on this chip"}
+        for form in ("folded", "inv_s"):
+            out5[f"decode_{form}"]["frac_read_ceiling"] = out5[f"decode_{form}"]["GB/s"] / rd_gbs
         out5["what"] = ("batch-1 decode pass of the 80-layer stack: per layer q|k|v (10240 x 8192), "
                         "o (8192 x 8192), gate|up (57344 x 8192), down (8192 x 28672); folded = 1/s "
                         "folded into the producers of x, inv_s = applied inside the products")
