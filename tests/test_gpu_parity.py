@@ -749,17 +749,21 @@ def test_product_single_group_64(M, N):
 
 
 @pytest.mark.parametrize("M,N,K,dtype,ydt,with_r,group", [
-    (17, 4096, 4096, F16, F16, True, 128),        # 4 K slices meet in the last-arriving block
-    (24, 11008, 4096, BF16, torch.float32, True, 128),   # 172 row blocks
-    (32, 4096, 11008, F16, torch.float32, True, 128),    # 86 units: uneven slices
-    (48, 1000, 2560, BF16, BF16, False, 64),       # ragged last row block, groups of 64
-    (64, 777, 8192, F16, torch.float32, True, 256),     # four token groups, groups of 256
-    (33, 64, 128, F16, torch.float32, False, 128),  # one unit, one row block
-    (40, 3000, 28672, BF16, F16, True, 128),       # long K: 224 units over the slices
+    (17, 4096, 4096, F16, F16, True, 128),        # one 16-row tile per block, 256 blocks
+    (24, 11008, 4096, BF16, torch.float32, True, 128),   # 43 rows in 3 tiles per block
+    (20, 13000, 1024, F16, F16, True, 128),        # 50 or 51 rows in 4 tiles per block
+    (56, 9000, 1024, BF16, torch.float32, False, 128),   # four token groups, two rounds of blocks
+    (32, 4096, 11008, F16, torch.float32, True, 128),    # 4-tile blocks, 86 units over 4 uneven slices
+    (48, 1000, 2560, BF16, BF16, False, 64),       # 2 K slices, groups of 64
+    (64, 777, 8192, F16, torch.float32, True, 256),     # 8 K slices of 2-tile blocks, groups of 256
+    (33, 64, 128, F16, torch.float32, False, 128),  # one unit, four row blocks
+    (17, 10, 256, BF16, torch.float32, True, 128),   # fewer rows than one tile
+    (40, 3000, 28672, BF16, F16, True, 128),       # long K: 224 units over 4 slices, 2-tile blocks
 ])
 def test_small_batch_product_parity(M, N, K, dtype, ydt, with_r, group):
-    """17 <= M <= 64: the memory-bound small-batch product (split over K, the
-    partial sums added by the last block of each row block)."""
+    """17 <= M <= 64: the memory-bound small-batch product (row blocks of up to
+    four tiles; small layers split over K, the slices' partial sums added in
+    slice order by a second kernel)."""
     words, step, z = _random_packed_g(N, K, M * 31 + N + K + group, group)
     x = _act(M, K, dtype, M + N)
     r = None

@@ -18,10 +18,14 @@ constexpr int kRowsKeep = 8;   // 8-element chunks per thread kept in registers 
 // Activation rows -> fp16: y_row = fp16(x_row * r * 2^p_row), p_row from the
 // row's max so the row sits in fp16's normal range.  One block per row.  With
 // PERMUTE each 8-element chunk is stored as (k0,k4,k2,k6,k1,k5,k3,k7), the
-// order in which the packed-nibble unpack yields weight pairs.  A row of up to
+// order in which the packed-nibble unpack yields weight pairs; with UNIT_T
+// (K a multiple of 128) the 16 pieces of each 128-channel unit are also
+// transposed 4 x 4, piece 4 b + i stored at 4 i + b, so that the pieces a
+// 16 x 16 x 32 product's four 32-channel lane blocks read together (one i,
+// b = 0..3) are adjacent.  A row of up to
 // 256 KEEP chunks stays in registers between its max and its conversion (read
 // once); a longer one is read twice.
-template <int DT, bool HAS_R, bool PERMUTE, int KEEP = kRowsKeep>
+template <int DT, bool HAS_R, bool PERMUTE, int KEEP = kRowsKeep, bool UNIT_T = false>
 __device__ __forceinline__ void rows_f16_block(int64_t row, const uint16_t* __restrict__ src, int64_t K,
                                                int64_t ld, const float* __restrict__ r,
                                                uint16_t* __restrict__ dst, int* __restrict__ pexp) {
@@ -59,7 +63,8 @@ __device__ __forceinline__ void rows_f16_block(int64_t row, const uint16_t* __re
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = h[2 * j] | (h[2 * j + 1] << 16);
     }
-    *reinterpret_cast<u32x4*>(d + c * 8) = o;
+    const int64_t pos = UNIT_T ? ((c & ~(int64_t)15) | ((c & 3) << 2) | ((c >> 2) & 3)) : c;
+    *reinterpret_cast<u32x4*>(d + pos * 8) = o;
   };
   __shared__ float wmax[4];
   auto row_exp = [&](float amax) {
@@ -105,12 +110,12 @@ __device__ __forceinline__ void rows_f16_block(int64_t row, const uint16_t* __re
     store8(c, v, p);
   }
 }
-template <int DT, bool HAS_R, bool PERMUTE>
+template <int DT, bool HAS_R, bool PERMUTE, bool UNIT_T = false>
 __global__ __launch_bounds__(256) void k_rows_f16(const uint16_t* __restrict__ src, int64_t K,
                                                   int64_t ld, const float* __restrict__ r,
                                                   uint16_t* __restrict__ dst,
                                                   int* __restrict__ pexp) {
-  rows_f16_block<DT, HAS_R, PERMUTE>(blockIdx.x, src, K, ld, r, dst, pexp);
+  rows_f16_block<DT, HAS_R, PERMUTE, kRowsKeep, UNIT_T>(blockIdx.x, src, K, ld, r, dst, pexp);
 }
 
 }  // namespace awqk
