@@ -32,11 +32,10 @@
 #include "awq_internal.h"
 #include "k_rows_f16.h"
 
-
 namespace awqk {
 
 constexpr int kMidWaves = 8;                       // waves per block, each 1/8 of the slice's units
-constexpr int kMidP = 2;                           // units of operands in flight per wave
+constexpr int kMidP = 2;                           // units of operands in flight per wave (4: slower)
 constexpr int kMidPad = 17;                        // floats per token row of a partial tile in LDS
 constexpr int64_t kMidWholeX = 256 * 1024;         // activation bytes every block of a small layer may read
 // Below 17 tokens the single-launch product that stages the whole activation
@@ -69,8 +68,9 @@ __device__ __forceinline__ u32x4 mid_dequant(uint32_t w, f16x2 c24, f16x2 c20, f
 
 // TG: 16-token groups (1..4); T: 16-row tiles per block (every wave runs all
 // of them, so one load of an activation operand serves T tiles); SPLIT: S > 1.
-// Block (s, b) takes rows [16 T b, 16 T b + 16 T) and the s-th of S slices of
-// the 128-channel units; wave w takes the w-th eighth of the slice's units.
+// Block (s, b) takes rows [b N / nb, (b + 1) N / nb) (at most 16 T) and the
+// s-th of S slices of the 128-channel units; each wave takes an eighth of the
+// slice's units.
 // Lane (rl, b4) = (lane % 16, lane / 16) holds, per unit, the 32-channel block
 // b4 of weight row rl of each tile (one 128-bit chunk) and of token rl of each
 // token group (four 128-bit chunks of x_q, read straight from memory: x_q is a
@@ -98,8 +98,8 @@ __global__ __launch_bounds__(64 * kMidWaves) void k_gemm_mid(
   const int u0 = bs * U / S, u1 = (bs + 1) * U / S;            // U <= 1024, S <= U
   const int us = u1 - u0;
   // the wave's eighth of the slice and the unit it starts from both turn with
-  // the block, so that at any moment the blocks read different activation
-  // columns rather than all the same ones
+  // the block, so that the blocks do not all read the same activation columns
+  // at once (measured neutral to 1.5 % faster)
   const int ks = (wv + (int)(blockIdx.x % (unsigned)kMidWaves)) % kMidWaves;
   const int w0 = u0 + ks * us / kMidWaves;
   const int nw = u0 + (ks + 1) * us / kMidWaves - w0;          // the wave's units
