@@ -57,6 +57,29 @@ def test_workspace_sizes():
     assert lib.awq_workspace_bytes(abi.AWQ_OP_SEARCH, 0, -1, 4096, 64, 20) == 0
 
 
+def test_small_batch_product_workspace():
+    """17..64 tokens: fp16 activations, row and weight-row exponents, and fp32
+    partial sums only where the layer is split over K (256 compute units when
+    no device is visible): layers with more 16-row tiles than compute units
+    are never split; smaller ones only when the activations exceed 256 KB."""
+    lib = _lib()
+
+    def a(n):
+        return (n + 255) // 256 * 256
+
+    def expect(M, N, K, S):
+        return a(2 * M * K) + a(4 * M) + a(4 * N) + (a(4 * S * M * N) if S > 1 else 0)
+
+    for M, N, K, S in ((32, 4096, 4096, 1),      # 256 KB of activations: whole, one tile per block
+                       (32, 11008, 4096, 1),     # 688 tiles: whole rounds of balanced row blocks
+                       (17, 57344, 8192, 1),
+                       (32, 4096, 11008, 4),     # 688 KB: 64-row blocks over 4 slices
+                       (48, 4096, 4096, 2),      # 384 KB: 32-row blocks over 2 slices
+                       (64, 777, 8192, 8),       # 25 blocks of 32 rows, 8 slices of 8 units
+                       (40, 65, 128, 1)):        # a single unit: no slices
+        assert lib.awq_workspace_bytes(abi.AWQ_OP_GEMM, M, N, K, 0, 0) == expect(M, N, K, S), (M, N, K)
+
+
 # fake device addresses: validation must fail before anything dereferences them
 A = ctypes.c_void_p(0x10000)       # 16-byte aligned
 A2 = ctypes.c_void_p(0x20000)
