@@ -4,14 +4,13 @@
 // activation magnitude over a calibration set).
 //
 // The column sums are exact.  Each |x| is taken in fixed point with LSB 2^-24
-// (floor(|x| * 2^24), exact for every fp16 value) and summed per thread:
-//   fp16: built from the 16-bit pattern with integer operations (the
-//         significand shifted by the exponent), summed in 64-bit integers;
-//   bf16: |x| converted to double, times 2^24, floored, summed in double --
-//         every term and partial sum is an integer below 2^53 under the
-//         precondition (column sums below 2^29), so the double sum is exact and
-//         equal to the integer one; bf16's shift-heavy integer path was the
-//         slower one (79 against 35 us on 2048 x 28672).
+// (floor(|x| * 2^24), exact for every fp16 value) and summed per thread in
+// double: every term and partial sum is an integer number of 2^-24 units below
+// 2^53 under the precondition (column sums below 2^29), so the double sums are
+// exact and equal to the integer ones.  Integer sums built from the 16-bit
+// patterns (the significand shifted by the exponent, 64-bit adds) were the
+// slower path: 79 against 35 us on 2048 x 28672 bf16; for fp16 the double
+// path needs only a conversion and an add per value.
 // Across the block the sums are 64-bit integers; each row range writes its
 // column sums to a slot of its own in the workspace (no atomics, nothing to
 // clear first), and the finalisation adds a column's slots in 64-bit integers
@@ -25,8 +24,6 @@
 #include "awq_device.h"
 #include "awq_internal.h"
 
-#include <type_traits>
-
 namespace awqk {
 
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
@@ -36,34 +33,19 @@ constexpr int kStatsCols = 512;      // columns per block (64 lanes x 8)
 constexpr int kStatsUnroll = 16;     // rows per wave per loop trip (loads in flight)
 
 
-// floor(|x| 2^24) of one 16-bit value, as an integer.  fp16: a subnormal is
-// m 2^-24 -> m; a normal (1024 + m) 2^(e - 25) -> (1024 + m) 2^(e - 1).  bf16:
-// (128 + m) 2^(e - 134) -> (128 + m) 2^(e - 110), shifted right (the floor)
-// below 2^24 and 0 for subnormals.  Shifts are capped at 40: values that large
-// already break the statistic's range (sum below 2^29).
+// Per thread, per column, in double, exactly:
+//   fp16: sum of |x| (every fp16 value is a multiple of 2^-24 below 2^16, so
+//         each partial sum is an integer multiple of 2^-24; times 2^24 it is
+//         the integer fixed-point sum, scaled once at the end);
+//   bf16: sum of floor(|x| 2^24) (values below 2^-24 floor away).
+// Under the precondition (column sums below 2^29) every partial sum is below
+// 2^53 units of 2^-24, so the double sums are exact and equal to the integer
+// sums of floor(|x| 2^24).
 template <int DT>
-__device__ __forceinline__ uint64_t fixed24(uint32_t h) {
+__device__ __forceinline__ void accum_word(uint32_t w, double& a, double& b) {
   if constexpr (DT == DT_F16) {
-    const uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
-    return e ? (uint64_t)(1024u | m) << (e - 1) : (uint64_t)m;
-  } else {
-    const int e = (int)((h >> 7) & 0xFFu);
-    const uint32_t m = (h & 0x7Fu) | 0x80u;
-    const int sh = e - 110;
-    if (e == 0 || sh <= -8) return 0;
-    return sh >= 0 ? (uint64_t)m << (sh < 40 ? sh : 40) : (uint64_t)(m >> -sh);
-  }
-}
-
-// The per-thread accumulator: 64-bit integers for fp16, double for bf16.
-template <int DT>
-using Acc24 = typename std::conditional<DT == DT_F16, uint64_t, double>::type;
-
-template <int DT>
-__device__ __forceinline__ void accum_word(uint32_t w, Acc24<DT>& a, Acc24<DT>& b) {
-  if constexpr (DT == DT_F16) {
-    a += fixed24<DT>(w & 0xFFFFu);
-    b += fixed24<DT>(w >> 16);
+    a += (double)f16_to_f32(w & 0x7FFFu);
+    b += (double)f16_to_f32((w >> 16) & 0x7FFFu);
   } else {
     a += floor((double)fabsf(bf16_to_f32(w & 0xFFFFu)) * 16777216.0);   // exact: power-of-two scale
     b += floor((double)fabsf(bf16_to_f32(w >> 16)) * 16777216.0);
@@ -88,9 +70,9 @@ __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __r
   const int64_t col = slab * kStatsCols + lane * 8;
   const int64_t r0 = chunk * rows_per_block;
   const int64_t r1 = min(T, r0 + rows_per_block);
-  Acc24<DT> s[8];
+  double s[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) s[j] = 0;
+  for (int j = 0; j < 8; ++j) s[j] = 0.0;
 
   if (col < K) {
     const uint16_t* base = x + col;
@@ -119,7 +101,8 @@ __global__ __launch_bounds__(kStatsThreads) void k_act_accum(const uint16_t* __r
 
   __shared__ uint64_t red[4][8][64];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) red[wv][j][lane] = (uint64_t)s[j];   // an integer below 2^53
+  for (int j = 0; j < 8; ++j)    // an integer below 2^53 (the fp16 sums in units of 2^-24)
+    red[wv][j][lane] = (uint64_t)(DT == DT_F16 ? s[j] * 16777216.0 : s[j]);
   __syncthreads();
   if (wv == 0 && col < K) {
     // this row range's column sums, one slot per range (no atomics, nothing to clear)
