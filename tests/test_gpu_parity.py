@@ -229,6 +229,21 @@ def test_gemm_parity(M, N, K, dtype, ydt, with_r):
     assert err <= GEMM_TOL
 
 
+@pytest.mark.parametrize("M,N,K,dtype,ydt,with_r", [
+    (24, 3000, 4096, F16, torch.float32, True),   # 188 row blocks x 2 slices, summed; ragged rows
+    (20, 4090, 2048, BF16, BF16, False),          # 256 row blocks, one slice; ragged last tile and tokens
+    (17, 300, 4096, F16, torch.float32, True),    # 19 row blocks x 4 slices of 8 units, summed
+])
+def test_small_batch_single_tile_blocks(M, N, K, dtype, ydt, with_r):
+    """17..32 tokens on layers of at most one 16-row tile per compute unit
+    (one tile per block), with and without the cross-slice sum, on ragged
+    rows and tokens, against the oracle."""
+    y, ref = _run_product(M, N, K, dtype, ydt, with_r, seed=M * 1000 + N + K)
+    err = rel_max_err(y, ref, ydt)
+    print(f"small batch M={M} N={N} K={K} {dtype} -> {ydt}: rel max err {err:.3e}")
+    assert err <= GEMM_TOL
+
+
 @pytest.mark.parametrize("M,N,K,dtype,ydt,with_r,group", [
     (2048, 8092, 256, BF16, torch.float32, True, 128),   # 256-wide tiles only, ragged last tile
     (2000, 25000, 256, F16, BF16, False, 128),           # 768 wide + 32 half-width tiles, ragged m and n
