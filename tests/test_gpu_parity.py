@@ -208,6 +208,8 @@ def test_skinny_one_hot_exact_passes(M, N, K, ks):
     (6200, 28672, BF16, torch.float32, True),  # 7 K slices, 4 staged pieces per thread
     (12000, 4096, F16, F16, False),
     (300, 30720, F16, F16, True),             # K beyond the row-block kernel, few rows per block
+    (10240, 8192, F16, F16, True),            # 70B q|k|v fused: 2 K slices, one staged piece, rows in pairs
+    (8192, 28672, BF16, torch.float32, False),  # 70B down-projection: 7 K slices, four rows in flight
 ])
 def test_gemv_batch1_per_cu_parity(N, K, dtype, ydt, with_r):
     """Batch-1 shapes served by the one-block-per-compute-unit kernel (many
